@@ -1,0 +1,118 @@
+/*
+ * oracle.h -- plain fp64 CPU oracle for Flint's decode-attention hot path.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the bench's
+ * cpu_baseline leg may load this library.  It shares no code, header, table
+ * or constant with the HIP library; neither includes the other.
+ *
+ * Every function computes the plain definition in double precision from the
+ * same bf16-rounded inputs the GPU sees.  Sources (page titles and sections):
+ *   [vLLM-day0]  "Day-0 Support for Flint on vLLM" (newruntime.com),
+ *                section "What happened": 49 layers, 35 sliding-window layers
+ *                over 513 tokens, 14 full-context layers, 28 KiB of KV per
+ *                token, fused normalisation / rotary / cache operations.
+ *   [arch]       "Day-0 Support for Flint on vLLM" (hnkhoi.com), section
+ *                "Model architecture": RoPE on the sliding layers, no
+ *                positional encoding on the full layers, learned attention
+ *                sinks, GQA with 32 query and 4 KV heads, per-head Q/K RMSNorm.
+ *   [models-json] "Recursive Flint" model JSON (studiotvai.com), fields
+ *                "architecture" (GQA 4 KV x 128) and "kvCacheGiBPerRequest".
+ * Where the pages leave a step open the reading taken is stated next to it.
+ *
+ * Cache layout (the oracle's own statement of it): for each layer, K and V are
+ * arrays of bf16 bit patterns indexed [page][kv_head][row 0..15][dim 0..127];
+ * logical token p of request b lives in physical page block_tables[b][p/16],
+ * row p%16.
+ */
+#ifndef FLINT_ORACLE_H
+#define FLINT_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int hq;         /* query heads (32)                                   */
+  int hkv;        /* KV heads (4); q head h reads KV head h/(hq/hkv)     */
+  int d;          /* head dim (128)                                     */
+  int bs;         /* tokens per page (16)                               */
+  int window;     /* 0: keys 0..t;  W>0: keys max(0,t-W+1)..t           */
+  int use_rope;   /* 1 on sliding layers, 0 on full layers              */
+  double theta;   /* RoPE base (10000)                                  */
+  double eps;     /* RMSNorm epsilon (1e-6)                              */
+  double scale;   /* softmax scale (1/sqrt(d))                           */
+} orc_layer;
+
+/* O1: fp32 -> bf16 by round-to-nearest-even, chosen between the two
+ * neighbouring bf16 values by comparing exact distances (NaN stays NaN). */
+uint16_t orc_bf16_rne(float x);
+double orc_bf16_value(uint16_t b);
+
+/* O2: per-head RMSNorm: y = x / sqrt(mean(x^2) + eps) * w, n values. */
+void orc_rmsnorm(const float* x, const float* w, int n, double eps, double* y);
+
+/* O3: rotate-half RoPE in place on one head of d values at position pos:
+ * pairs (i, i+d/2) turn by pos * theta^(-2i/d). */
+void orc_rope(double* x, int d, double pos, double theta);
+
+/* O8: physical slot (page*bs + row) of logical token pos of request b. */
+int64_t orc_slot(const int32_t* block_tables, int bt_stride, int bs, int b, int pos);
+
+/* O4: per token t: q_out[t] = rope?(rmsnorm(q_in[t], qw)) for every q head;
+ * K row at slot_mapping[t] = bf16(rope?(rmsnorm(k_in[t], kw))), V row = bf16(v_in[t]).
+ * slot < 0 skips the cache write for that token.  q_out may be NULL.
+ * Returns 0, or -1 on a slot outside [0, num_blocks*bs). */
+int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
+               const float* v_in, const float* qw, const float* kw,
+               const int32_t* positions, const int32_t* slot_mapping,
+               double* q_out, uint16_t* k_cache, uint16_t* v_cache, int num_blocks);
+
+/* O5: one query of request b (absolute position t = seq_lens[b]-1) for every
+ * q head, keys lo..t read through the page table; the sink of head h is an
+ * extra logit in the softmax denominator that carries no value.
+ * q: [B][hq][d] doubles; out: [B][hq][d].  Work is spread over nthreads
+ * (<=0: all cores).  Returns 0, or -1 on a page id outside [0, num_blocks). */
+int orc_attn_decode(const orc_layer* L, int B, const double* q,
+                    const uint16_t* k_cache, const uint16_t* v_cache, int num_blocks,
+                    const int32_t* block_tables, int bt_stride, const int32_t* seq_lens,
+                    const float* sinks, double* out, int nthreads);
+
+/* O6: partial over keys [j0, j1) of request b for q head h: normalised
+ * o_tilde[d] and lse = m + ln(sum exp(s_j - m)); an empty range gives
+ * lse = -inf and o_tilde = 0. */
+void orc_attn_partial(const orc_layer* L, const double* q_h, int h,
+                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const int32_t* block_tables, int bt_stride, int b,
+                      int j0, int j1, double* o_tilde, double* lse);
+
+/* O6: fold S partials and the sink logit of one head into its output. */
+void orc_merge(int S, int d, const double* o_tildes, const double* lses,
+               double sink, double* out);
+
+/* O7: causal prefill.  Request b owns query rows cu_q_lens[b] ..
+ * cu_q_lens[b+1]-1; row i of it sits at position seq_lens[b] - q_len_b + i.
+ * q: [total_q][hq][d]; out: [total_q][hq][d].  If rows != NULL only those
+ * global rows are computed (others untouched).  Returns 0 or -1. */
+int orc_attn_prefill(const orc_layer* L, int B, const double* q, const int32_t* cu_q_lens,
+                     const uint16_t* k_cache, const uint16_t* v_cache, int num_blocks,
+                     const int32_t* block_tables, int bt_stride, const int32_t* seq_lens,
+                     const float* sinks, double* out, const int32_t* rows, int nrows,
+                     int nthreads);
+
+/* Bytes of KV per token kept by `full_layers` full-context layers. */
+int64_t orc_full_kv_bytes_per_token(int full_layers, int hkv, int d, int elem_bytes);
+
+/* KV bytes one request holds at context ctx: full layers keep every token,
+ * sliding layers keep min(ctx, window) tokens. */
+int64_t orc_kv_bytes_per_request(int64_t ctx, int full_layers, int sliding_layers,
+                                 int window, int hkv, int d, int elem_bytes);
+
+/* Number of threads the parallel oracle calls use for nthreads <= 0. */
+int orc_default_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,495 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something it does not compute itself:
+values the pages print, closed forms, invariants, an independent library
+routine (torch's bf16 conversion, numpy complex rotation) or brute force in
+50-digit arithmetic on tiny inputs.  The comment on each test names the
+plausible oracle mistake it would catch.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    oracle.build(force=False)
+
+
+# ---------------------------------------------------------------------------
+# O1 bf16
+# ---------------------------------------------------------------------------
+
+def test_bf16_widen_matches_bit_view():
+    # all 65536 patterns: the definition-based value equals reading the bits as
+    # the top half of an fp32 (catches a wrong bias / subnormal scale)
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_value(bits)
+    with np.errstate(invalid="ignore"):
+        ref = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def _torch_bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def test_bf16_rne_matches_torch():
+    # independent library rounding: catches truncation instead of RNE, a wrong
+    # tie rule, overflow and subnormal handling
+    r = synth.rng(0, 99, 1)
+    u = r.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[np.isfinite(x)]
+    specials = np.array([0.0, -0.0, 1.0, -1.0, 1.00390625, 1.01171875, 1.0078125,
+                         3.3895314e38, 3.3961e38, 3.4028235e38, -3.4028235e38, 1e-40, -1e-45,
+                         1.1754944e-38, 9.18e-41, np.inf, -np.inf], dtype=np.float32)
+    halfway = (((np.arange(4096, dtype=np.uint32) << 16) | 0x8000)).view(np.float32)
+    halfway = halfway[np.isfinite(halfway)]
+    for arr in (x, specials, halfway):
+        assert np.array_equal(oracle.bf16_rne(arr), _torch_bf16_bits(arr))
+
+
+def test_bf16_nan_stays_nan():
+    b = oracle.bf16_rne([np.float32("nan")])[0]
+    assert (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
+
+
+# ---------------------------------------------------------------------------
+# O2 RMSNorm
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_rmsnorm_rms_closed_form(eps):
+    # with w = 1 the output RMS is sqrt(ms/(ms+eps)): catches sum-vs-mean and
+    # eps outside the square root
+    x = synth.normal(1, (7,), 128) * 3.0
+    y = oracle.rmsnorm(x, np.ones(128, np.float32), eps)
+    ms = np.mean(x.astype(np.float64) ** 2)
+    assert math.isclose(np.sqrt(np.mean(y ** 2)), math.sqrt(ms / (ms + eps)), rel_tol=1e-13)
+
+
+def test_rmsnorm_scale_invariance_and_weight():
+    # eps = 0: RMSNorm(c x) = RMSNorm(x); weight multiplies elementwise
+    x = synth.normal(2, (1,), 128)
+    w = synth.norm_weight(2, (2,), 128, ones=False)
+    y1 = oracle.rmsnorm(x, w, 0.0)
+    y2 = oracle.rmsnorm(x * np.float32(4.0), w, 0.0)
+    y0 = oracle.rmsnorm(x, np.ones(128, np.float32), 0.0)
+    assert np.allclose(y1, y2, rtol=1e-14, atol=0)
+    assert np.allclose(y1, y0 * w.astype(np.float64), rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# O3 RoPE
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pos", [0, 1, 511, 99999, 262143])
+def test_rope_is_complex_rotation(pos):
+    # independent formulation: z_i = x_i + i x_{i+64} times exp(i pos theta^(-2i/128));
+    # catches a wrong sign, the interleaved pairing and a wrong frequency exponent
+    x = synth.normal(3, (pos,), 128).astype(np.float64)
+    y = oracle.rope(x, pos)
+    i = np.arange(64)
+    freq = np.exp(-(2.0 * i / 128.0) * np.log(10000.0))
+    z = (x[:64] + 1j * x[64:]) * np.exp(1j * (pos * freq))
+    assert np.allclose(y[:64], z.real, rtol=0, atol=1e-9)
+    assert np.allclose(y[64:], z.imag, rtol=0, atol=1e-9)
+
+
+def test_rope_relative_position():
+    # <rope(q, a), rope(k, b)> depends only on a - b
+    q = synth.normal(4, (1,), 128).astype(np.float64)
+    k = synth.normal(4, (2,), 128).astype(np.float64)
+    d0 = np.dot(oracle.rope(q, 700), oracle.rope(k, 650))
+    d1 = np.dot(oracle.rope(q, 50), oracle.rope(k, 0))
+    d2 = np.dot(oracle.rope(q, 100050), oracle.rope(k, 100000))
+    assert math.isclose(d0, d1, rel_tol=1e-11) and math.isclose(d0, d2, rel_tol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# attention: helpers to build a small paged problem
+# ---------------------------------------------------------------------------
+
+def _paged(L, dense_k_bits, dense_v_bits, seed, perm=True):
+    """Place dense [n, hkv, d] bf16 rows of one request into a shuffled paged
+    cache; returns (kc, vc, block_tables)."""
+    n = dense_k_bits.shape[0]
+    pages = -(-n // L.bs)
+    extra = 3
+    order = synth.permutation(seed, (77,), pages + extra) if perm else np.arange(pages + extra)
+    bt = np.full((1, pages + 2), -1, np.int32)
+    bt[0, :pages] = order[:pages]
+    kc = np.full((pages + extra, L.hkv, L.bs, L.d), 0x7FC0, np.uint16)  # NaN where unused
+    vc = kc.copy()
+    for p in range(n):
+        pg, r = bt[0, p // L.bs], p % L.bs
+        kc[pg, :, r, :] = dense_k_bits[p]
+        vc[pg, :, r, :] = dense_v_bits[p]
+    return kc, vc, bt
+
+
+def _brute(L, q, kbits, vbits, t, sinks, lo=None):
+    """50-digit evaluation of the definition on dense (unpaged) rows, without
+    max subtraction: out_h = sum_j e^{s_j} V_j / (e^{sink_h} + sum_j e^{s_j})."""
+    mpmath.mp.dps = 50
+    kf = synth.bf16_bits_to_f32(kbits).astype(np.float64)
+    vf = synth.bf16_bits_to_f32(vbits).astype(np.float64)
+    if lo is None:
+        lo = max(0, t - L.window + 1) if L.window > 0 else 0
+    grp = L.hq // L.hkv
+    out = np.empty((L.hq, L.d))
+    sc = mpmath.mpf(1) / mpmath.sqrt(L.d)
+    for h in range(L.hq):
+        g = h // grp
+        es = []
+        for j in range(lo, t + 1):
+            s = mpmath.fsum(mpmath.mpf(float(q[h, i])) * mpmath.mpf(float(kf[j, g, i]))
+                            for i in range(L.d))
+            es.append(mpmath.exp(sc * s))
+        z = mpmath.exp(mpmath.mpf(float(sinks[h]))) + mpmath.fsum(es)
+        for i in range(L.d):
+            out[h, i] = float(mpmath.fsum(e * mpmath.mpf(float(vf[lo + jj, g, i]))
+                                          for jj, e in enumerate(es)) / z)
+    return out
+
+
+def _small_layer(window=0):
+    return oracle.layer(window=window, hq=4, hkv=2, d=8, bs=4)
+
+
+@pytest.mark.parametrize("n,window", [(1, 0), (3, 0), (7, 0), (9, 5), (6, 3)])
+def test_attention_brute_force_small_shape(n, window):
+    # catches a wrong GQA head mapping, a transposed K/V index, a wrong scale,
+    # a dropped sink term and window off-by-one, on a shape other than Flint's
+    L = _small_layer(window)
+    kb = synth.normal_bf16_bits(5, (n, 1), (n, L.hkv, L.d))
+    vb = synth.normal_bf16_bits(5, (n, 2), (n, L.hkv, L.d))
+    q = synth.normal(5, (n, 3), (L.hq, L.d)).astype(np.float64)
+    sinks = synth.normal(5, (n, 4), L.hq)
+    kc, vc, bt = _paged(L, kb, vb, seed=n)
+    out = oracle.attn_decode(L, q[None], kc, vc, bt, np.array([n], np.int32), sinks)[0]
+    ref = _brute(L, q, kb, vb, n - 1, sinks)
+    assert np.max(np.abs(out - ref)) < 1e-15
+
+
+@pytest.mark.parametrize("n,window", [(5, 0), (8, 0), (8, 513)])
+def test_attention_brute_force_flint_shape(n, window):
+    L = oracle.layer(window=window, use_rope=1 if window else 0)
+    kb = synth.normal_bf16_bits(6, (n, 1), (n, 4, 128))
+    vb = synth.normal_bf16_bits(6, (n, 2), (n, 4, 128))
+    q = synth.normal(6, (n, 3), (32, 128)).astype(np.float64)
+    sinks = synth.normal(6, (n, 4), 32)
+    kc, vc, bt = _paged(L, kb, vb, seed=n)
+    out = oracle.attn_decode(L, q[None], kc, vc, bt, np.array([n], np.int32), sinks)[0]
+    ref = _brute(L, q, kb, vb, n - 1, sinks)
+    assert np.max(np.abs(out - ref)) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def _flint_case(n, seed, window=0, same_keys=False, q_zero=False, sink=None):
+    L = oracle.layer(window=window)
+    kb = synth.normal_bf16_bits(seed, (1,), (n, 4, 128))
+    if same_keys:
+        kb[:] = kb[0]
+    vb = synth.normal_bf16_bits(seed, (2,), (n, 4, 128))
+    q = synth.normal(seed, (3,), (32, 128)).astype(np.float64)
+    if q_zero:
+        q[:] = 0.0
+    sinks = synth.normal(seed, (4,), 32)
+    if sink is not None:
+        sinks[:] = sink
+    kc, vc, bt = _paged(L, kb, vb, seed)
+    out = oracle.attn_decode(L, q[None], kc, vc, bt, np.array([n], np.int32), sinks)[0]
+    kf = synth.bf16_bits_to_f32(kb).astype(np.float64)
+    vf = synth.bf16_bits_to_f32(vb).astype(np.float64)
+    return L, q, kf, vf, sinks.astype(np.float64), out
+
+
+def test_identical_keys_give_sink_weighted_mean():
+    # all scores equal s: out = (1 - w) mean_j V_j with w = e^sink/(e^sink + n e^s)
+    n = 37
+    L, q, kf, vf, sinks, out = _flint_case(n, 11, same_keys=True)
+    for h in range(32):
+        g = h // 8
+        s = np.dot(q[h], kf[0, g]) / math.sqrt(128)
+        w = math.exp(sinks[h]) / (math.exp(sinks[h]) + n * math.exp(s))
+        assert np.allclose(out[h], (1 - w) * vf[:, g].mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_sink_minus_inf_is_plain_softmax():
+    # library softmax (scipy) as the independent routine
+    from scipy.special import softmax
+    n = 50
+    L, q, kf, vf, sinks, out = _flint_case(n, 12, sink=-np.inf)
+    for h in range(32):
+        g = h // 8
+        p = softmax(kf[:, g] @ q[h] / math.sqrt(128))
+        assert np.allclose(out[h], p @ vf[:, g], rtol=0, atol=1e-13)
+
+
+def test_zero_query_gives_value_sum_over_n_plus_exp_sink():
+    n = 21
+    L, q, kf, vf, sinks, out = _flint_case(n, 13, q_zero=True)
+    for h in range(32):
+        assert np.allclose(out[h], vf[:, h // 8].sum(0) / (n + math.exp(sinks[h])), atol=1e-13)
+
+
+def test_single_key_is_sigmoid_gate():
+    # n = 1: out = V_0 * sigmoid(s_0 - sink)
+    L, q, kf, vf, sinks, out = _flint_case(1, 14)
+    for h in range(32):
+        s = np.dot(q[h], kf[0, h // 8]) / math.sqrt(128)
+        assert np.allclose(out[h], vf[0, h // 8] / (1 + math.exp(sinks[h] - s)), atol=1e-14)
+
+
+def test_gqa_equal_heads_equal_outputs():
+    L = oracle.layer()
+    n = 40
+    kb = synth.normal_bf16_bits(15, (1,), (n, 4, 128))
+    vb = synth.normal_bf16_bits(15, (2,), (n, 4, 128))
+    q = synth.normal(15, (3,), (32, 128)).astype(np.float64)
+    q[8:16] = q[8]
+    sinks = synth.normal(15, (4,), 32)
+    sinks[8:16] = sinks[8]
+    kc, vc, bt = _paged(L, kb, vb, 15)
+    out = oracle.attn_decode(L, q[None], kc, vc, bt, np.array([n], np.int32), sinks)[0]
+    for h in range(9, 16):
+        assert np.array_equal(out[h], out[8])
+    assert not np.allclose(out[0], out[8])
+
+
+# ---------------------------------------------------------------------------
+# window (P3)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 17, 512, 513])
+def test_sliding_equals_full_below_window(n):
+    # t = n - 1 < 513: the window covers every key
+    Lf, Ls = oracle.layer(window=0), oracle.layer(window=513)
+    kb = synth.normal_bf16_bits(16, (n, 1), (n, 4, 128))
+    vb = synth.normal_bf16_bits(16, (n, 2), (n, 4, 128))
+    q = synth.normal(16, (n, 3), (1, 32, 128)).astype(np.float64)
+    sinks = synth.normal(16, (n, 4), 32)
+    kc, vc, bt = _paged(Lf, kb, vb, 16)
+    sl = np.array([n], np.int32)
+    assert np.array_equal(oracle.attn_decode(Lf, q, kc, vc, bt, sl, sinks),
+                          oracle.attn_decode(Ls, q, kc, vc, bt, sl, sinks))
+
+
+@pytest.mark.parametrize("n", [514, 530, 1000])
+def test_sliding_sees_exactly_last_513_keys(n):
+    # t = n-1 >= 513: sliding equals full attention over keys t-512..t only
+    Lf, Ls = oracle.layer(window=0), oracle.layer(window=513)
+    kb = synth.normal_bf16_bits(17, (n, 1), (n, 4, 128))
+    vb = synth.normal_bf16_bits(17, (n, 2), (n, 4, 128))
+    q = synth.normal(17, (n, 3), (1, 32, 128)).astype(np.float64)
+    sinks = synth.normal(17, (n, 4), 32)
+    kc, vc, bt = _paged(Ls, kb, vb, 17)
+    out_s = oracle.attn_decode(Ls, q, kc, vc, bt, np.array([n], np.int32), sinks)
+    kc2, vc2, bt2 = _paged(Lf, kb[n - 513:], vb[n - 513:], 18)
+    out_f = oracle.attn_decode(Lf, q, kc2, vc2, bt2, np.array([513], np.int32), sinks)
+    assert np.allclose(out_s, out_f, rtol=0, atol=1e-15)
+    kc3, vc3, bt3 = _paged(Lf, kb[n - 512:], vb[n - 512:], 19)
+    out_short = oracle.attn_decode(Lf, q, kc3, vc3, bt3, np.array([512], np.int32), sinks)
+    assert not np.allclose(out_s, out_short, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# split / merge (P5) and paging (P6)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64])
+def test_split_merge_equals_direct(splits):
+    n = 300
+    L = oracle.layer()
+    kb = synth.normal_bf16_bits(20, (1,), (n, 4, 128))
+    vb = synth.normal_bf16_bits(20, (2,), (n, 4, 128))
+    q = synth.normal(20, (3,), (32, 128)).astype(np.float64)
+    sinks = synth.normal(20, (4,), 32)
+    kc, vc, bt = _paged(L, kb, vb, 20)
+    ref = oracle.attn_decode(L, q[None], kc, vc, bt, np.array([n], np.int32), sinks)[0]
+    edges = np.linspace(0, n, splits + 1).round().astype(int)
+    edges = np.concatenate([[0, 0], edges])  # plus an empty range at the front
+    for h in (0, 13, 31):
+        parts = [oracle.attn_partial(L, q[h], h, kc, vc, bt, 0, edges[i], edges[i + 1])
+                 for i in range(len(edges) - 1)]
+        got = oracle.merge(np.stack([p[0] for p in parts]), np.array([p[1] for p in parts]),
+                           sinks[h])
+        assert np.allclose(got, ref[h], rtol=0, atol=1e-12)
+
+
+def test_page_permutation_is_bit_identical():
+    n = 200
+    L = oracle.layer()
+    kb = synth.normal_bf16_bits(21, (1,), (n, 4, 128))
+    vb = synth.normal_bf16_bits(21, (2,), (n, 4, 128))
+    q = synth.normal(21, (3,), (1, 32, 128)).astype(np.float64)
+    sinks = synth.normal(21, (4,), 32)
+    a = _paged(L, kb, vb, 21, perm=False)
+    b = _paged(L, kb, vb, 22, perm=True)
+    sl = np.array([n], np.int32)
+    assert np.array_equal(oracle.attn_decode(L, q, *a, sl, sinks),
+                          oracle.attn_decode(L, q, *b, sl, sinks))
+
+
+def test_ring_aliasing_outside_window_is_bit_identical():
+    # a 33-page ring for a sliding layer gives the same output as a full table
+    n = 2000
+    Ls = oracle.layer(window=513)
+    kb = synth.normal_bf16_bits(23, (1,), (n, 4, 128))
+    vb = synth.normal_bf16_bits(23, (2,), (n, 4, 128))
+    q = synth.normal(23, (3,), (1, 32, 128)).astype(np.float64)
+    sinks = synth.normal(23, (4,), 32)
+    kc, vc, bt = _paged(Ls, kb, vb, 23)
+    logical = -(-n // 16)
+    rbt, nb = synth.ring_block_table(23, (5,), 1, logical, 33, logical + 1)
+    rk = np.zeros((nb, 4, 16, 128), np.uint16)
+    rv = rk.copy()
+    for p in range(n):  # later tokens overwrite ring pages, as appends would
+        pg = rbt[0, p // 16]
+        rk[pg, :, p % 16] = kb[p]
+        rv[pg, :, p % 16] = vb[p]
+    sl = np.array([n], np.int32)
+    assert np.array_equal(oracle.attn_decode(Ls, q, kc, vc, bt, sl, sinks),
+                          oracle.attn_decode(Ls, q, rk, rv, rbt, sl, sinks))
+
+
+def test_window_spans_33_pages():
+    # keys t-512..t always touch 33 pages of 16 once t >= 512
+    for t in range(512, 512 + 64):
+        assert (t // 16) - ((t - 512) // 16) + 1 == 33
+
+
+# ---------------------------------------------------------------------------
+# append (O4) and page walk (O8)
+# ---------------------------------------------------------------------------
+
+def test_append_places_rows_and_rounds_v_like_torch():
+    L = oracle.layer(window=513, use_rope=1)
+    T = 40
+    nb = 8
+    bt = synth.permutation(30, (1,), nb)[None, :]
+    pos = np.arange(100, 100 + T, dtype=np.int32)
+    slots = np.array([oracle.slot(bt, 0, p % (nb * 16)) for p in range(T)], np.int32)
+    slots[5] = -1  # skipped token
+    q = synth.normal(30, (2,), (T, 32, 128))
+    k = synth.normal(30, (3,), (T, 4, 128))
+    v = synth.normal(30, (4,), (T, 4, 128))
+    ones = np.ones(128, np.float32)
+    kc = np.full((nb, 4, 16, 128), 0xBEEF, np.uint16)
+    vc = kc.copy()
+    qo = oracle.append(L, q, k, v, ones, ones, pos, slots, kc, vc)
+    written = np.zeros((nb, 16), bool)
+    for t in range(T):
+        if slots[t] < 0:
+            continue
+        pg, r = divmod(int(slots[t]), 16)
+        written[pg, r] = True
+        assert np.array_equal(vc[pg, :, r], _torch_bf16_bits(v[t]))
+        for g in range(4):
+            kk = oracle.rope(oracle.rmsnorm(k[t, g], ones), pos[t])
+            # the oracle rounds the fp64 value once; torch rounds its fp32 image
+            ref = _torch_bf16_bits(kk.astype(np.float32)).astype(int)
+            assert np.max(np.abs(kc[pg, g, r].astype(int) - ref)) <= 1
+    untouched = ~written
+    assert np.all(kc.transpose(0, 2, 1, 3)[untouched] == 0xBEEF)
+    assert np.all(vc.transpose(0, 2, 1, 3)[untouched] == 0xBEEF)
+    # q out: norm then rope; norms are preserved by the rotation
+    for t in (0, 17):
+        for h in (0, 31):
+            qn = oracle.rmsnorm(q[t, h], ones)
+            assert math.isclose(np.linalg.norm(qo[t, h]), np.linalg.norm(qn), rel_tol=1e-13)
+
+
+def test_append_rejects_slot_out_of_range():
+    L = oracle.layer()
+    kc = np.zeros((2, 4, 16, 128), np.uint16)
+    vc = kc.copy()
+    x = np.zeros((1, 4, 128), np.float32)
+    with pytest.raises(ValueError):
+        oracle.append(L, np.zeros((1, 32, 128), np.float32), x, x, np.ones(128), np.ones(128),
+                      [0], [32], kc, vc)
+
+
+def test_page_walk_reconstructs_sequence():
+    # every logical token lands in a distinct slot, and reading pages in table
+    # order returns the tokens in order
+    n = 16 * 37 + 5
+    bt, nb = synth.shuffled_block_table(31, (1,), 1, [-(-n // 16)], 40)
+    slots = [oracle.slot(bt, 0, p) for p in range(n)]
+    assert len(set(slots)) == n and min(slots) >= 0 and max(slots) < nb * 16
+    flat = np.full(nb * 16, -1)
+    flat[slots] = np.arange(n)
+    seq = np.concatenate([flat[pg * 16:(pg + 1) * 16] for pg in bt[0, :-(-n // 16)]])
+    assert np.array_equal(seq[:n], np.arange(n))
+
+
+# ---------------------------------------------------------------------------
+# prefill (O7)
+# ---------------------------------------------------------------------------
+
+def test_prefill_rows_equal_decode_at_same_position():
+    L = oracle.layer(window=513)
+    n = 700
+    kb = synth.normal_bf16_bits(40, (1,), (n, 4, 128))
+    vb = synth.normal_bf16_bits(40, (2,), (n, 4, 128))
+    q = synth.normal(40, (3,), (n, 32, 128)).astype(np.float64)
+    sinks = synth.normal(40, (4,), 32)
+    kc, vc, bt = _paged(L, kb, vb, 40)
+    start = 100  # chunk of rows 100..699 with 100 keys already cached
+    out = oracle.attn_prefill(L, q[start:], np.array([0, n - start], np.int32), kc, vc, bt,
+                              np.array([n], np.int32), sinks)
+    for i in (0, 1, 412, 413, 599):
+        t = start + i
+        dec = oracle.attn_decode(L, q[t][None], kc, vc, bt, np.array([t + 1], np.int32), sinks)
+        assert np.array_equal(out[i], dec[0])
+
+
+def test_prefill_brute_force_small():
+    L = _small_layer(window=3)
+    n = 9
+    kb = synth.normal_bf16_bits(41, (1,), (n, L.hkv, L.d))
+    vb = synth.normal_bf16_bits(41, (2,), (n, L.hkv, L.d))
+    q = synth.normal(41, (3,), (n, L.hq, L.d)).astype(np.float64)
+    sinks = synth.normal(41, (4,), L.hq)
+    kc, vc, bt = _paged(L, kb, vb, 41)
+    out = oracle.attn_prefill(L, q, np.array([0, n], np.int32), kc, vc, bt,
+                              np.array([n], np.int32), sinks)
+    for i in range(n):
+        assert np.max(np.abs(out[i] - _brute(L, q[i], kb, vb, i, sinks))) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# footprint (P8): the pages' own numbers
+# ---------------------------------------------------------------------------
+
+def test_full_layer_kv_is_28_kib_per_token():
+    shape = json.load(open(os.path.join(GOLDEN, "flint_attention_shape.json")))
+    assert oracle.full_kv_bytes_per_token(shape["full_layers"], shape["kv_heads"],
+                                          shape["head_dim"], 2) == shape["kv_bytes_per_token"]
+    assert shape["sliding_layers"] + shape["full_layers"] == shape["layers"]
+
+
+def test_kv_calculator_table():
+    tab = json.load(open(os.path.join(GOLDEN, "kv_cache_gib_per_request.json")))
+    for row in tab["rows"]:
+        for fmt, eb in (("bf16", 2), ("fp8", 1)):
+            gib = oracle.kv_bytes_per_request(row["context"], elem_bytes=eb) / 2**30
+            assert round(gib, 3) == pytest.approx(row[fmt], abs=1e-9), (row, fmt, gib)
