@@ -1,0 +1,318 @@
+"""Decode-attention bench for Flint's 49-layer stack on one MI355X.
+
+Workload: one decode step at batch 1 and a 100,000-token context over all 49
+attention layers -- 14 full-context NoPE layers reading 100,000 keys each and
+35 RoPE sliding layers reading the last 513 keys -- from a bf16 paged KV cache
+(16-token pages; every full layer's 6,250 pages in a seeded random physical
+order; each sliding layer on a 33-page ring).  A step runs, per layer in
+order, the fused norm/RoPE/append of the new token and then split-K decode
+attention with the sink merge; the 49 layers are captured into one HIP graph.
+
+Prints one JSON line.  `value` is microseconds per step (lower is better).
+All inputs are seeded synthetic tensors (~N(0,1)); KV pages are drawn on the
+host and are resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "decode-attn µs/step & HBM GB/s (% of peak), bs1 100K ctx, 49 layers"
+CTX = 100_000
+LAYERS = 49
+FULL_LAYERS = [l for l in range(LAYERS) if l % 7 in (3, 6)]   # 14 full, 35 sliding
+WINDOW = 513
+RING = 33
+HQ, HKV, D, PAGE = 32, 4, 128, 16
+HBM_PEAK_GBPS = 8000.0
+BF16_DENSE_TFLOPS = 2500.0
+SEED = 0
+KV_BYTES_PER_TOKEN_LAYER = 2 * HKV * D * 2   # K and V rows of one token, one layer
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_inputs(dev):
+    """Seeded inputs for every layer, resident in HBM (the 2.9 GB of KV pages
+    are drawn on the GPU by torch's generator; small tensors on the host)."""
+    import torch
+    pages = -(-CTX // PAGE)
+    t = CTX - 1
+    layers = []
+    for l in range(LAYERS):
+        full = l in FULL_LAYERS
+        if full:
+            bt, nb = synth.shuffled_block_table(SEED, (2, l, synth.PERM), 1, [pages], pages)
+        else:
+            bt, nb = synth.ring_block_table(SEED, (2, l, synth.PERM), 1, pages, RING, pages)
+        kd = synth.normal_bf16_bits_torch(SEED, (2, l, synth.KC), (nb, HKV, PAGE, D), dev)
+        vd = synth.normal_bf16_bits_torch(SEED, (2, l, synth.VC), (nb, HKV, D, PAGE), dev)
+        q = synth.normal(SEED, (2, l, synth.Q), (1, HQ, D))
+        k = synth.normal(SEED, (2, l, synth.K), (1, HKV, D))
+        v = synth.normal(SEED, (2, l, synth.V), (1, HKV, D))
+        sinks = synth.normal(SEED, (2, l, synth.SINK), HQ)
+        slot = int(bt[0, t // PAGE]) * PAGE + t % PAGE
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(
+            a.view(np.int16) if a.dtype == np.uint16 else a)).to(dev)
+        layers.append(dict(
+            full=full, host=dict(bt=bt, q=q, k=k, v=v, sinks=sinks, slot=slot),
+            bt=up(bt), kc=kd, vc=vd, q_in=up(q), k_in=up(k), v_in=up(v),
+            sinks=up(sinks), slots=up(np.array([slot], np.int32)),
+            q_out=torch.empty((1, HQ, D), dtype=torch.float32, device=dev),
+            out=torch.empty((1, HQ, D), dtype=torch.float32, device=dev)))
+        if l % 7 == 6:
+            log(f"bench: inputs for layers 0..{l} resident")
+    return layers
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the decode path here is single-GPU (--gpus {args.gpus} "
+              "is not supported; run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import full_gqa_decode_amd as fl
+    fl.lib()
+    dev = torch.device("cuda:0")
+    eps = float(np.float32(1e-6))
+    FULL = fl.layer(window=0, use_rope=0, rms_eps=eps)
+    SLIDE = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps)
+    ones = torch.ones(D, dtype=torch.float32, device=dev)
+    pos = torch.tensor([CTX - 1], dtype=torch.int32, device=dev)
+    seq_lens = torch.tensor([CTX], dtype=torch.int32, device=dev)
+
+    t0 = time.time()
+    layers = build_inputs(dev)
+    if not args.no_cpu_baseline:   # the oracle reads the same drawn pages
+        for L in layers:
+            L["kc0"] = L["kc"].cpu().numpy().view(np.uint16)
+            L["vc0"] = L["vc"].cpu().numpy().view(np.uint16)
+    log(f"bench: inputs ready in {time.time() - t0:.1f}s")
+    ws_bytes = max(fl.flint_attn_decode_workspace_size(FULL, 1, CTX),
+                   fl.flint_attn_decode_workspace_size(SLIDE, 1, CTX), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def layer_step(L):
+        Ld = FULL if L["full"] else SLIDE
+        fl.flint_qk_norm_rope_append(Ld, L["q_in"], L["k_in"], L["v_in"], ones, ones, pos,
+                                     L["slots"], L["q_out"], L["kc"], L["vc"])
+        fl.flint_attn_decode(Ld, L["q_out"], L["kc"], L["vc"], L["bt"], seq_lens, CTX,
+                             L["sinks"], L["out"], workspace=ws)
+
+    def step():
+        for L in layers:
+            layer_step(L)
+
+    # eager once (also the reference the graph must reproduce)
+    step()
+    torch.cuda.synchronize()
+    eager = [L["out"].clone() for L in layers]
+
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            step()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    for L, e in zip(layers, eager):
+        assert torch.equal(L["out"], e), "graph replay differs from eager"
+
+    # timed region: K whole steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for i in range(args.steps):
+            g.replay()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(args.steps)]
+    us_step = ev[0].elapsed_time(ev[-1]) * 1e3 / args.steps
+    log(f"bench: {args.steps} steps, {us_step:.1f} us/step (median {statistics.median(per):.1f}, "
+        f"wall {wall * 1e6 / args.steps:.1f} us/step)")
+
+    # dominant kernel: full-layer decode, timed over back-to-back replays of the
+    # 14 full layers on the stream they run on
+    gf = torch.cuda.CUDAGraph()
+    full_layers = [L for L in layers if L["full"]]
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(gf, stream=stream):
+            for L in full_layers:
+                fl.flint_attn_decode(FULL, L["q_out"], L["kc"], L["vc"], L["bt"], seq_lens, CTX,
+                                     L["sinks"], L["out"], workspace=ws)
+    reps = 20
+    for _ in range(3):
+        gf.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            gf.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us_full = e0.elapsed_time(e1) * 1e3 / (reps * len(full_layers))
+    kv_full = CTX * KV_BYTES_PER_TOKEN_LAYER
+    extra_full = HQ * D * 4 * 2 + HQ * 4 + (-(-CTX // PAGE)) * 4   # q, out, sinks, page table
+    achieved = (kv_full + extra_full) / (us_full * 1e-6) / 1e9
+    pps, nsplit = fl.flint_attn_decode_plan(FULL, 1, CTX)
+
+    kv_step = sum(CTX * KV_BYTES_PER_TOKEN_LAYER if L["full"] else WINDOW * KV_BYTES_PER_TOKEN_LAYER
+                  for L in layers)
+    gbps_step = kv_step / (us_step * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_step, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Flint decode attention, all 49 layers (14 full-context NoPE over "
+                               "100,000 keys + 35 RoPE sliding over 513 keys), batch 1, one "
+                               "decode step incl. norm/RoPE/append of the new token, bf16 paged "
+                               "KV (16-token pages, shuffled), HIP graph",
+                   "global_batch": 1, "seq_len": CTX, "layers": LAYERS,
+                   "full_layers": len(FULL_LAYERS), "window": WINDOW, "parallelism": "none"},
+        "hbm_gbps": round(gbps_step, 1),
+        "hbm_frac_of_peak": round(gbps_step / HBM_PEAK_GBPS, 4),
+        "kv_bytes_per_step": kv_step,
+        "us_per_step_median": round(statistics.median(per), 2),
+        "us_per_step_p10": round(float(np.percentile(per, 10)), 2),
+        "us_per_step_p90": round(float(np.percentile(per, 90)), 2),
+        "roofline": {"kernel": "full-layer decode (split-K + merge), 100,000 keys",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "us_per_launch": round(us_full, 2),
+                     "bytes_per_launch": kv_full + extra_full,
+                     "pages_per_split": pps, "splits": nsplit},
+        "context": "pages' end-to-end figure (model forward + LM head + sampling, 1x GB200, "
+                   "vLLM): 2.06 ms/token ~ 485 tok/s at bs1, 100K ctx; not this metric",
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(fl, dev, stream)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity_max_abs_err"] = cpu_baseline(layers, eps)
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(fl, dev, stream):
+    """Causal prefill of a 32,768-token prompt on one full layer (MFMA-bound):
+    append all tokens (bf16 q), then time the attention kernel alone."""
+    import torch
+    T = 32768
+    eps = float(np.float32(1e-6))
+    L = fl.layer(window=0, use_rope=0, rms_eps=eps)
+    pages = T // PAGE
+    bt, nb = synth.shuffled_block_table(SEED, (4, 0, synth.PERM), 1, [pages], pages)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q = up(synth.normal(SEED, (4, 0, synth.Q), (T, HQ, D)))
+    k = up(synth.normal(SEED, (4, 0, synth.K), (T, HKV, D)))
+    v = up(synth.normal(SEED, (4, 0, synth.V), (T, HKV, D)))
+    sinks = up(synth.normal(SEED, (4, 0, synth.SINK), HQ))
+    slots = up((bt[0, np.arange(T) // PAGE].astype(np.int64) * PAGE + np.arange(T) % PAGE)
+               .astype(np.int32))
+    pos = up(np.arange(T, dtype=np.int32))
+    ones = torch.ones(D, dtype=torch.float32, device=dev)
+    kc = torch.empty((nb, HKV, PAGE, D), dtype=torch.int16, device=dev)
+    vc = torch.empty((nb, HKV, D, PAGE), dtype=torch.int16, device=dev)
+    qb = torch.empty((T, HQ, D), dtype=torch.int16, device=dev)
+    fl.flint_qk_norm_rope_append(L, q, k, v, ones, ones, pos, slots, qb, kc, vc)
+    out = torch.empty((T, HQ, D), dtype=torch.float32, device=dev)
+    cu = up(np.array([0, T], np.int32))
+    sl = up(np.array([T], np.int32))
+    btd = up(bt)
+    run = lambda: fl.flint_attn_prefill(L, qb, cu, T, kc, vc, btd, sl, T, sinks, out)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pairs = T * (T + 1) // 2
+    flops = 4.0 * D * pairs * HQ
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"bench: prefill 32768 full layer {ms:.2f} ms, {tflops:.1f} TFLOP/s")
+    return {"workload": "causal prefill, 32,768-token prompt, one full layer (32 q / 4 KV heads)",
+            "ms": round(ms, 3), "flops": flops, "tflops": round(tflops, 1),
+            "bound": "mfma", "peak_tflops": BF16_DENSE_TFLOPS,
+            "mfma_frac": round(tflops / BF16_DENSE_TFLOPS, 4),
+            "finite": bool(torch.isfinite(out).all().item())}
+
+
+def cpu_baseline(layers, eps):
+    """The fp64 oracle on the host cores, over the same 49-layer step (its own
+    append of the new token, then attention), timed; its outputs also give the
+    step's parity check."""
+    import oracle
+    oracle.build(force=False)
+    t = CTX - 1
+    nthreads = oracle.default_threads()
+    Lf = oracle.layer(window=0, use_rope=0, eps=eps)
+    Ls = oracle.layer(window=WINDOW, use_rope=1, eps=eps)
+    ones = np.ones(D, np.float32)
+    worst = 0.0
+    t0 = time.perf_counter()
+    for L in layers:   # host copies of the drawn caches (pristine: taken before any append)
+        L["host"]["kc"] = L["kc0"]
+        L["host"]["vc"] = L["vc0"]
+    for L in layers:
+        h = L["host"]
+        Lo = Lf if L["full"] else Ls
+        kc, vc = h["kc"], h["vc"]   # the new token is appended in place
+        qh = oracle.append(Lo, h["q"], h["k"], h["v"], ones, ones, np.array([t], np.int32),
+                           np.array([h["slot"]], np.int32), kc, vc)
+        ref = oracle.attn_decode(Lo, qh, kc, vc, h["bt"], np.array([CTX], np.int32), h["sinks"],
+                                 nthreads=nthreads)
+        L["ref"] = ref
+    secs = time.perf_counter() - t0
+    for L in layers:
+        worst = max(worst, float(np.max(np.abs(L["out"].cpu().numpy().astype(np.float64)
+                                               - L["ref"]))))
+    log(f"bench: oracle step {secs:.2f} s on {nthreads} threads; max|gpu-oracle| {worst:.2e}")
+    return ({"value": round(secs * 1e6, 1), "unit": "us/step", "cores": nthreads,
+             "kind": "oracle",
+             "sample": "the whole 49-layer step (append of the new token + attention for all "
+                       "32 heads of every layer), fp64, once"}, worst)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,236 @@
+"""Python binding of libflint, the MI355X decode-attention library for Flint.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libflint.so.  PyTorch supplies device memory (tensor data
+pointers) and the stream (the current HIP stream).  If the library has not
+been built this module raises on first use; there is no fallback.
+
+Functions carry the C names of include/flint.h:
+    flint_qk_norm_rope_append, flint_attn_decode, flint_attn_prefill,
+plus the size / plan queries.  bf16 tensors (K/V caches, prefill q) may be
+torch.bfloat16, torch.int16 or torch.uint16: only their bits are used.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libflint.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "flint.h")
+
+FLINT_OK = 0
+STATUS_NAMES = {0: "FLINT_OK", 1: "FLINT_ERR_INVALID_ARGUMENT", 2: "FLINT_ERR_UNSUPPORTED",
+                3: "FLINT_ERR_WORKSPACE_TOO_SMALL", 4: "FLINT_ERR_HIP"}
+
+
+class FlintError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class FlintAttnLayer(C.Structure):
+    _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("block_size", C.c_int32), ("window", C.c_int32),
+                ("use_rope", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
+                ("softmax_scale", C.c_float)]
+
+
+def layer(window: int = 0, use_rope: int = 0, num_q_heads: int = 32, num_kv_heads: int = 4,
+          head_dim: int = 128, block_size: int = 16, rope_theta: float = 10000.0,
+          rms_eps: float = 1e-6, softmax_scale: float | None = None) -> FlintAttnLayer:
+    scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
+    return FlintAttnLayer(num_q_heads, num_kv_heads, head_dim, block_size, window, use_rope,
+                          rope_theta, rms_eps, scale)
+
+
+def full_layer(**kw) -> FlintAttnLayer:
+    """One of Flint's 14 full-context layers: no positional encoding."""
+    return layer(window=0, use_rope=0, **kw)
+
+
+def sliding_layer(**kw) -> FlintAttnLayer:
+    """One of Flint's 35 sliding layers: 513-key window with RoPE."""
+    return layer(window=513, use_rope=1, **kw)
+
+
+_lib = None
+_P = C.c_void_p
+_I = C.c_int32
+_SZ = C.c_size_t
+_LP = C.POINTER(FlintAttnLayer)
+
+# (name, restype, argtypes) of every symbol include/flint.h declares
+SIGNATURES = [
+    ("flint_qk_norm_rope_append", C.c_int,
+     [_LP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P]),
+    ("flint_attn_decode_workspace_size", _SZ, [_LP, _I, _I]),
+    ("flint_attn_decode", C.c_int, [_LP, _I, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+    ("flint_attn_decode_workspace_size_ex", _SZ, [_LP, _I, _I, _I]),
+    ("flint_attn_decode_ex", C.c_int,
+     [_LP, _I, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _I, _P]),
+    ("flint_attn_decode_plan", C.c_int, [_LP, _I, _I, _I, C.POINTER(_I), C.POINTER(_I)]),
+    ("flint_attn_prefill_workspace_size", _SZ, [_LP, _I, _I, _I]),
+    ("flint_attn_prefill", C.c_int,
+     [_LP, _I, _P, _P, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+    ("flint_status_string", C.c_char_p, [C.c_int]),
+    ("flint_last_error", C.c_char_p, []),
+    ("flint_abi_version", _I, []),
+]
+
+
+def lib() -> C.CDLL:
+    """Load libflint.so (built by `python -m full_gqa_decode_amd.build`)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FileNotFoundError(
+                f"{LIB_PATH} is missing: build it with `python -m full_gqa_decode_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != FLINT_OK:
+        raise FlintError(status, lib().flint_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtypes, name, cuda=True):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _f32():
+    return (_torch().float32,)
+
+
+def _i32():
+    return (_torch().int32,)
+
+
+def _b16():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def flint_qk_norm_rope_append(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_norm_w,
+                              positions, slot_mapping, q_out, k_cache, v_cache, stream=None):
+    """Fused per-head RMSNorm + RoPE + paged append of num_tokens tokens.
+    q_out is float32 (decode) or a bf16-bits tensor (prefill); it may be q_in."""
+    torch = _torch()
+    T = k_in.shape[0]
+    num_blocks = k_cache.shape[0]
+    q_f32 = q_out if q_out is not None and q_out.dtype == torch.float32 else None
+    q_b16 = q_out if q_out is not None and q_out.dtype != torch.float32 else None
+    _check(lib().flint_qk_norm_rope_append(
+        C.byref(L), T, _ptr(q_in, _f32(), "q_in"), _ptr(k_in, _f32(), "k_in"),
+        _ptr(v_in, _f32(), "v_in"), _ptr(q_norm_w, _f32(), "q_norm_w"),
+        _ptr(k_norm_w, _f32(), "k_norm_w"), _ptr(positions, _i32(), "positions"),
+        _ptr(slot_mapping, _i32(), "slot_mapping"), _ptr(q_f32, _f32(), "q_out"),
+        _ptr(q_b16, _b16(), "q_out"), _ptr(k_cache, _b16(), "k_cache"),
+        _ptr(v_cache, _b16(), "v_cache"), num_blocks, _stream(stream)))
+
+
+def flint_attn_decode_workspace_size(L: FlintAttnLayer, num_seqs: int, max_seq_len: int,
+                                     pages_per_split: int = 0) -> int:
+    return int(lib().flint_attn_decode_workspace_size_ex(C.byref(L), num_seqs, max_seq_len,
+                                                          pages_per_split))
+
+
+def flint_attn_decode_plan(L: FlintAttnLayer, num_seqs: int, max_seq_len: int,
+                           pages_per_split: int = 0):
+    """(pages_per_split, num_splits) the library will use."""
+    pps, ns = _I(), _I()
+    _check(lib().flint_attn_decode_plan(C.byref(L), num_seqs, max_seq_len, pages_per_split,
+                                        C.byref(pps), C.byref(ns)))
+    return pps.value, ns.value
+
+
+def flint_attn_decode(L: FlintAttnLayer, q, k_cache, v_cache, block_tables, seq_lens,
+                      max_seq_len: int, sinks, out, workspace=None, pages_per_split: int = 0,
+                      stream=None):
+    """Decode attention for q.shape[0] requests; writes out [B, Hq, 128] fp32.
+    `workspace` (uint8 tensor) is allocated here when not given; pass one to
+    keep the call free of allocations (e.g. under HIP-graph capture)."""
+    torch = _torch()
+    B = q.shape[0]
+    need = flint_attn_decode_workspace_size(L, B, max_seq_len, pages_per_split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().flint_attn_decode_ex(
+        C.byref(L), B, _ptr(q, _f32(), "q"), _ptr(k_cache, _b16(), "k_cache"),
+        _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
+        _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),
+        _ptr(out, _f32(), "out"),
+        None if workspace is None else workspace.data_ptr(), ws_bytes, pages_per_split,
+        _stream(stream)))
+    return out
+
+
+def flint_attn_prefill_workspace_size(L: FlintAttnLayer, num_seqs: int, max_q_len: int,
+                                      max_seq_len: int) -> int:
+    return int(lib().flint_attn_prefill_workspace_size(C.byref(L), num_seqs, max_q_len,
+                                                        max_seq_len))
+
+
+def flint_attn_prefill(L: FlintAttnLayer, q, cu_q_lens, max_q_len: int, k_cache, v_cache,
+                       block_tables, seq_lens, max_seq_len: int, sinks, out, workspace=None,
+                       stream=None):
+    """Causal prefill for the rows in cu_q_lens; q bf16 bits [total_q, Hq, 128],
+    out fp32 [total_q, Hq, 128]."""
+    torch = _torch()
+    B = cu_q_lens.shape[0] - 1
+    need = flint_attn_prefill_workspace_size(L, B, max_q_len, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().flint_attn_prefill(
+        C.byref(L), B, _ptr(q, _b16(), "q"), _ptr(cu_q_lens, _i32(), "cu_q_lens"), max_q_len,
+        _ptr(k_cache, _b16(), "k_cache"), _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
+        _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),
+        _ptr(out, _f32(), "out"), None if workspace is None else workspace.data_ptr(), ws_bytes,
+        _stream(stream)))
+    return out
+
+
+def abi_version() -> int:
+    return int(lib().flint_abi_version())

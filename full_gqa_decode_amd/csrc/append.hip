@@ -1,0 +1,140 @@
+// append.hip -- K1: fused per-head Q/K RMSNorm, RoPE and paged KV append.
+//
+// "Day-0 Support for Flint on vLLM" (newruntime.com), "What happened": the
+// optimised path fuses normalisation, rotary-position and cache operations.
+// "Day-0 Support for Flint on vLLM" (hnkhoi.com), "Model architecture":
+// per-head Q/K RMSNorm; RoPE on the 35 sliding layers, none on the 14 full
+// layers.  Order: norm, then rotation, then the bf16 cache write.
+//
+// One wave64 handles one head of one token: lane l holds dims l and l+64,
+// which is exactly a rotate-half RoPE pair, so the rotation needs no lane
+// exchange and the only cross-lane step is the sum of squares.  A workgroup of
+// four waves covers four of the token's (num_q_heads + 2*num_kv_heads) heads.
+// The arithmetic is fp64 (full rate on gfx950, and this kernel is tiny): the
+// fp32 q output is the correctly rounded normalised/rotated value, and the
+// bf16 K is rounded once from the fp64 value (round-to-odd to fp32, then
+// round-to-nearest-even to bf16), so it matches an exact computation except
+// on ties closer than ~1e-15 relative.
+// Launch-latency bound at decode (one token per request); bandwidth bound for
+// long prefill chunks (~4.5 KB read and written per token for 32/4 heads).
+#include "device.h"
+#include "launch.h"
+
+namespace flint {
+
+namespace {
+
+// fp64 -> bf16 bits with one rounding: round to odd at fp32 precision (24
+// bits, enough guard bits for bf16's 8), then round to nearest even.
+__device__ __forceinline__ uint16_t bf16_bits_rne_f64(double x) {
+  if (x != x) return 0x7fc0u;
+  float f = (float)x;
+  const double back = (double)f;
+  if (back != x) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs(back) > fabs(x)) u -= 1u;  // the nearest fp32 toward zero
+    f = __uint_as_float(u | 1u);
+  }
+  return bf16_bits_rne(f);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// cos/sin of pos * theta^(-2i/128), in fp64 with a two-part 2*pi reduction,
+// accurate to ~1e-16 for every position up to the 262,144-token context.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, float theta, double* c, double* s) {
+  const double inv_freq = exp2(-(2.0 * i / kHeadDim) * log2((double)theta));
+  const double ang = (double)pos * inv_freq;
+  const double two_pi_hi = 6.283185307179586;           // 2*pi rounded to fp64
+  const double two_pi_lo = 2.4492935982947064e-16;      // 2*pi - two_pi_hi
+  const double k = rint(ang * 0.15915494309189535);     // ang / (2*pi)
+  double r = fma(-k, two_pi_hi, ang);
+  r = fma(-k, two_pi_lo, r);
+  sincos(r, s, c);
+}
+
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int hq = a.num_q_heads, hkv = a.num_kv_heads;
+  const int tasks = hq + 2 * hkv;
+  const int groups = (tasks + 3) >> 2;
+  const int t = blockIdx.x / groups;
+  const int task = (blockIdx.x % groups) * 4 + (threadIdx.x >> 6);
+  if (t >= a.num_tokens || task >= tasks) return;
+
+  const int pos = a.positions[t];
+  const int slot = a.slots[t];
+  const bool bad = pos < 0 || (int64_t)slot >= (int64_t)a.num_blocks * kPage;
+  const bool write_cache = slot >= 0 && !bad;
+
+  if (task >= hq + hkv) {  // V: round to bf16 and store dim-major
+    if (!write_cache) return;
+    const int g = task - hq - hkv;
+    const float* x = a.v_in + ((int64_t)t * hkv + g) * kHeadDim;
+    const float v0 = x[lane], v1 = x[lane + 64];
+    const int64_t page = slot / kPage, row = slot % kPage;
+    uint16_t* dst = a.v_cache + (page * hkv + g) * (int64_t)(kHeadDim * kPage) + row;
+    dst[lane * kPage] = bf16_bits_rne(v0);
+    dst[(lane + 64) * kPage] = bf16_bits_rne(v1);
+    return;
+  }
+
+  const bool is_q = task < hq;
+  if (!is_q && !write_cache) return;
+  const float* x = is_q ? a.q_in + ((int64_t)t * hq + task) * kHeadDim
+                        : a.k_in + ((int64_t)t * hkv + (task - hq)) * kHeadDim;
+  const float* w = is_q ? a.q_w : a.k_w;
+  const double x0 = x[lane], x1 = x[lane + 64];
+
+  // RMSNorm over the head's 128 values.
+  const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
+  const double r = 1.0 / sqrt(ss / kHeadDim + (double)a.rms_eps);
+  double y0 = x0 * r * (double)w[lane];
+  double y1 = x1 * r * (double)w[lane + 64];
+
+  // Rotate-half RoPE: pair (lane, lane+64) turns by pos * theta^(-2*lane/128).
+  if (a.use_rope) {
+    double c, s;
+    rope_cos_sin(pos < 0 ? 0 : pos, lane, a.rope_theta, &c, &s);
+    const double r0 = y0 * c - y1 * s;
+    const double r1 = y1 * c + y0 * s;
+    y0 = r0;
+    y1 = r1;
+  }
+
+  if (is_q) {
+    if (bad) y0 = y1 = __builtin_nan("");
+    const int64_t o = ((int64_t)t * hq + task) * kHeadDim;
+    if (a.q_out_f32) {
+      a.q_out_f32[o + lane] = (float)y0;
+      a.q_out_f32[o + lane + 64] = (float)y1;
+    } else {
+      a.q_out_bf16[o + lane] = bf16_bits_rne_f64(y0);
+      a.q_out_bf16[o + lane + 64] = bf16_bits_rne_f64(y1);
+    }
+    return;
+  }
+
+  const int g = task - hq;
+  const int64_t page = slot / kPage, row = slot % kPage;
+  uint16_t* dst = a.k_cache + ((page * hkv + g) * kPage + row) * kHeadDim;
+  dst[lane] = bf16_bits_rne_f64(y0);
+  dst[lane + 64] = bf16_bits_rne_f64(y1);
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const int tasks = a.num_q_heads + 2 * a.num_kv_heads;
+  const int groups = (tasks + 3) / 4;
+  const int64_t blocks = (int64_t)a.num_tokens * groups;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace flint

@@ -1,0 +1,77 @@
+// launch.h -- internal launchers behind the C ABI (host side).  Arguments are
+// already validated by api.hip when these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flint {
+
+struct AppendArgs {
+  const float* q_in;
+  const float* k_in;
+  const float* v_in;
+  const float* q_w;
+  const float* k_w;
+  const int32_t* positions;
+  const int32_t* slots;
+  float* q_out_f32;
+  uint16_t* q_out_bf16;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t use_rope;
+  float rope_theta;
+  float rms_eps;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const float* q;            // [B][Hq][128] fp32
+  const uint16_t* k_cache;   // [pages][Hkv][16][128]
+  const uint16_t* v_cache;   // [pages][Hkv][128][16]
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const float* sinks;        // [Hq]
+  float* out;                // [B][Hq][128]
+  float* part_o;             // [B][S][Hq][128] (multi-split only)
+  float* part_lse;           // [B][S][Hq], log2 units (multi-split only)
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t bt_stride;
+  int32_t window;            // 0 = full
+  int32_t max_seq_len;
+  int32_t pages_per_split;
+  int32_t num_splits;        // splits in the grid (per request)
+  float qscale;              // softmax_scale * log2(e)
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+struct PrefillArgs {
+  const uint16_t* q;         // [total_q][Hq][128] bf16
+  const int32_t* cu_q_lens;  // [B+1]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const float* sinks;
+  float* out;                // [total_q][Hq][128] fp32
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t bt_stride;
+  int32_t window;
+  int32_t max_q_len;
+  int32_t max_seq_len;
+  float qscale;              // softmax_scale * log2(e)
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+// Waves per decode workgroup (the split plan depends on it).
+constexpr int kDecodeWaves = 8;
+
+}  // namespace flint

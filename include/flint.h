@@ -1,0 +1,191 @@
+/*
+ * flint.h -- C ABI of the MI355X (gfx950) decode-attention library for the
+ * Flint 40B-A2.5B MoE.
+ *
+ * What is computed (sources by page title and section):
+ *   "Day-0 Support for Flint on vLLM" (newruntime.com), "What happened":
+ *       49 layers; 35 attend over a 513-token sliding window, 14 attend to the
+ *       full context and alone keep KV for the whole sequence (28 KiB per
+ *       token); fused normalisation, rotary-position and cache operations and
+ *       a low-latency small-batch decode path.
+ *   "Day-0 Support for Flint on vLLM" (hnkhoi.com), "Model architecture":
+ *       the sliding layers use RoPE, the full layers use no positional
+ *       encoding; learned attention sinks; GQA with 32 query and 4 KV heads;
+ *       per-head Q/K RMSNorm.
+ *   "Recursive Flint" model JSON (studiotvai.com), "architecture": 4 KV
+ *       heads of dim 128; "maxContext": 262,144 tokens.
+ * Readings taken where the pages are silent: the sink of query head h is one
+ * scalar logit that joins the softmax denominator, is not multiplied by the
+ * softmax scale and carries no value; the window holds keys t-512..t of a
+ * query at position t; RoPE is rotate-half over all 128 dims with absolute
+ * 0-based positions; q head h reads KV head h / (num_q_heads/num_kv_heads).
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless stated otherwise, owned by the
+ *     caller.  The library never allocates or frees memory and keeps no state
+ *     between calls; scratch space comes from the caller's workspace.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued on it; no call synchronises or reads device memory
+ *     back, so every call can be captured into a HIP graph.
+ *   - bf16 values are passed as their uint16 bit patterns.
+ *   - Arguments the host can see are checked before anything is launched and
+ *     a status is returned; flint_last_error() then describes the problem.
+ *     Device-resident indices (positions, slots, page ids, seq_lens) are
+ *     bounds-checked inside the kernels: nothing outside the caller's buffers
+ *     is ever read or written, and the affected outputs are set to NaN.
+ *   - Supported shape: head_dim 128, block_size 16, num_q_heads =
+ *     8 * num_kv_heads with 1 <= num_kv_heads <= 8, window 0 or >= 1.
+ *
+ * Paged KV cache layout (one K array and one V array per layer)
+ *   A page holds 16 consecutive tokens of one request.  Logical token p of
+ *   request b lives in physical page block_tables[b * bt_stride + p / 16],
+ *   row p % 16.  Per page and KV head the data is one contiguous 4 KiB tile:
+ *     K: k_cache[((page * num_kv_heads + g) * 16 + row) * 128 + dim]
+ *        (token-major: each token's 128-dim row is 256 contiguous bytes)
+ *     V: v_cache[((page * num_kv_heads + g) * 128 + dim) * 16 + row]
+ *        (dim-major: the 16 tokens of one dim are 32 contiguous bytes)
+ *   K rows feed the q.K contraction over dims; V is stored dim-major because
+ *   the P.V contraction runs over tokens, so both operands of the matrix
+ *   cores load straight from HBM with full coalescing.
+ */
+#ifndef FLINT_H
+#define FLINT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLINT_ABI_VERSION 1
+
+typedef enum {
+  FLINT_OK = 0,
+  FLINT_ERR_INVALID_ARGUMENT = 1,   /* a host-visible argument is wrong       */
+  FLINT_ERR_UNSUPPORTED = 2,        /* a shape this library does not support  */
+  FLINT_ERR_WORKSPACE_TOO_SMALL = 3,/* workspace_bytes below the size query   */
+  FLINT_ERR_HIP = 4                 /* the HIP runtime refused a launch       */
+} flint_status;
+
+/* One attention layer.  The pages fix num_q_heads 32, num_kv_heads 4,
+ * head_dim 128; window 513 with use_rope 1 for the 35 sliding layers and
+ * window 0 with use_rope 0 for the 14 full layers. */
+typedef struct {
+  int32_t num_q_heads;   /* 8 * num_kv_heads                                */
+  int32_t num_kv_heads;  /* 1..8 (Flint: 4)                                  */
+  int32_t head_dim;      /* 128                                              */
+  int32_t block_size;    /* tokens per page: 16                              */
+  int32_t window;        /* 0: keys 0..t;  W >= 1: keys max(0, t-W+1)..t     */
+  int32_t use_rope;      /* 1: rotate q and k (sliding layers); 0: NoPE      */
+  float rope_theta;      /* RoPE base (10000)                                */
+  float rms_eps;         /* RMSNorm epsilon (1e-6)                           */
+  float softmax_scale;   /* multiplies q.k (1/sqrt(128))                     */
+} flint_attn_layer;
+
+/*
+ * Fused per-head Q/K RMSNorm, optional RoPE and paged KV append for
+ * num_tokens tokens ("What happened": fused normalisation, rotary-position
+ * and cache operations; "Model architecture": per-head Q/K RMSNorm, RoPE on
+ * the sliding layers only).
+ *   q_in  [T][num_q_heads][128] fp32, k_in, v_in [T][num_kv_heads][128] fp32
+ *   q_norm_w, k_norm_w [128] fp32 (one weight vector shared by all heads)
+ *   positions [T] int32: absolute 0-based position of each token (RoPE angle)
+ *   slot_mapping [T] int32: page * 16 + row to write; < 0 skips the token
+ *   q_out_f32 [T][num_q_heads][128] (decode) or q_out_bf16 (prefill): exactly
+ *     one is non-NULL; q_out_f32 may alias q_in.
+ *   k_cache, v_cache: [num_blocks] pages in the layout above.
+ * Per token and head: y = x / sqrt(mean(x^2) + eps) * w, computed in fp32;
+ * then RoPE(y, position) when use_rope; K and V are rounded to bf16
+ * (round-to-nearest-even) and written at the slot.  V is not normalised.
+ * A slot >= num_blocks*16 or a negative position is not written and the
+ * token's q_out row is set to NaN.
+ */
+flint_status flint_qk_norm_rope_append(const flint_attn_layer* L, int32_t num_tokens,
+                                       const float* q_in, const float* k_in, const float* v_in,
+                                       const float* q_norm_w, const float* k_norm_w,
+                                       const int32_t* positions, const int32_t* slot_mapping,
+                                       float* q_out_f32, uint16_t* q_out_bf16,
+                                       uint16_t* k_cache, uint16_t* v_cache, int32_t num_blocks,
+                                       void* stream);
+
+/*
+ * Decode attention: one new query per request over its paged bf16 KV.
+ * Request b's query sits at position t = seq_lens[b] - 1 (seq_lens counts the
+ * new token, which must already be appended) and attends to keys lo..t,
+ * lo = 0 (window 0) or max(0, t - window + 1).  For query head h of KV group
+ * g = h / 8:
+ *   s_j   = softmax_scale * <q[b][h], K_j>
+ *   out   = sum_j e^{s_j} V_j / (e^{sinks[h]} + sum_j e^{s_j})
+ *   q      [B][num_q_heads][128] fp32 (normalised, rotated by the append)
+ *   block_tables [B][bt_stride] int32 page ids; seq_lens [B] int32 on device
+ *   max_seq_len  host-side upper bound of seq_lens (<= bt_stride * 16)
+ *   sinks  [num_q_heads] fp32 logits (-inf allowed: plain softmax)
+ *   out    [B][num_q_heads][128] fp32; must not alias q
+ * Work is split over key ranges (split-K) and merged with log-sum-exp
+ * weights; the sink joins in the merge.  A request whose seq_len is outside
+ * [1, max_seq_len] or whose pages include an id outside [0, num_blocks) gets
+ * NaN outputs.  workspace: >= flint_attn_decode_workspace_size(...) bytes,
+ * 256-byte aligned, contents need not be initialised.
+ */
+size_t flint_attn_decode_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
+                                        int32_t max_seq_len);
+flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, const float* q,
+                               const uint16_t* k_cache, const uint16_t* v_cache,
+                               int32_t num_blocks, const int32_t* block_tables,
+                               int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                               const float* sinks, float* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Same as flint_attn_decode with the split size fixed by the caller:
+ * pages_per_split > 0 pages of 16 keys per split (0 = the library's choice).
+ * The workspace query must be made with the same pages_per_split. */
+size_t flint_attn_decode_workspace_size_ex(const flint_attn_layer* L, int32_t num_seqs,
+                                           int32_t max_seq_len, int32_t pages_per_split);
+flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, const float* q,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  int32_t num_blocks, const int32_t* block_tables,
+                                  int32_t bt_stride, const int32_t* seq_lens,
+                                  int32_t max_seq_len, const float* sinks, float* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t pages_per_split, void* stream);
+
+/* The split plan flint_attn_decode_ex would use (host only, no HIP call):
+ * writes the pages per split and the number of splits per request. */
+flint_status flint_attn_decode_plan(const flint_attn_layer* L, int32_t num_seqs,
+                                    int32_t max_seq_len, int32_t pages_per_split,
+                                    int32_t* out_pages_per_split, int32_t* out_num_splits);
+
+/*
+ * Causal (optionally windowed) prefill attention over the paged cache, on
+ * the matrix cores.  Request b owns query rows cu_q_lens[b] ..
+ * cu_q_lens[b+1]-1 (cu_q_lens [B+1] int32 on device, cu_q_lens[0] = 0); row
+ * i of it sits at position seq_lens[b] - q_len_b + i and attends to keys
+ * lo..that position, whose K/V must already be appended.
+ *   q   [total_q][num_q_heads][128] bf16 (normalised, rotated)
+ *   max_q_len  host-side bound of every q_len; max_seq_len as for decode
+ *   out [total_q][num_q_heads][128] fp32
+ * Same per-row result as decode; the sink joins every row's denominator.
+ * Rows of a request with q_len > seq_len or seq_len > max_seq_len, or whose
+ * pages include an id outside [0, num_blocks), are set to NaN.
+ */
+size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
+                                         int32_t max_q_len, int32_t max_seq_len);
+flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* q,
+                                const int32_t* cu_q_lens, int32_t max_q_len,
+                                const uint16_t* k_cache, const uint16_t* v_cache,
+                                int32_t num_blocks, const int32_t* block_tables,
+                                int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                                const float* sinks, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Status text, thread-local detail of the last non-OK status on this thread,
+ * and the ABI version (FLINT_ABI_VERSION). */
+const char* flint_status_string(flint_status s);
+const char* flint_last_error(void);
+int32_t flint_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

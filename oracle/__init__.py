@@ -59,6 +59,7 @@ def lib():
         L.orc_bf16_rne.argtypes = [C.c_float]
         L.orc_bf16_value.restype = C.c_double
         L.orc_bf16_value.argtypes = [C.c_uint16]
+        L.orc_bf16_rne_array.argtypes = [P, P, C.c_int64]
         L.orc_rmsnorm.argtypes = [P, P, C.c_int, C.c_double, P]
         L.orc_rope.argtypes = [P, C.c_int, C.c_double, C.c_double]
         L.orc_slot.restype = C.c_int64
@@ -94,6 +95,14 @@ def bf16_rne(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float32).ravel()
     f = lib().orc_bf16_rne
     return np.array([f(float(v)) for v in x], dtype=np.uint16)
+
+
+def bf16_rne_f64(x) -> np.ndarray:
+    """Round fp64 values to bf16 bits (once, no fp32 step); keeps the shape."""
+    x = _c(x, np.float64)
+    y = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_bf16_rne_array(_p(x), _p(y), x.size)
+    return y
 
 
 def bf16_value(bits) -> np.ndarray:
@@ -218,15 +227,24 @@ def default_threads() -> int:
 
 
 # --- helpers for tests: the oracle's own view of a paged cache ----------------
-def cache_shape(num_blocks, hkv=4, bs=16, d=128):
+def k_cache_shape(num_blocks, hkv=4, bs=16, d=128):
+    """K pages: [page][kv_head][row][dim]."""
     return (num_blocks, hkv, bs, d)
 
 
-def depage(cache, block_tables, b, n_tokens, bs=16):
-    """Gather tokens 0..n_tokens-1 of request b from a [pages, hkv, bs, d]
-    cache into [n_tokens, hkv, d] (uses the oracle's own slot function)."""
-    out = np.empty((n_tokens, cache.shape[1], cache.shape[3]), dtype=cache.dtype)
+def v_cache_shape(num_blocks, hkv=4, bs=16, d=128):
+    """V pages: [page][kv_head][dim][row] (dim-major)."""
+    return (num_blocks, hkv, d, bs)
+
+
+def depage(k_cache, v_cache, block_tables, b, n_tokens, bs=16):
+    """Gather tokens 0..n_tokens-1 of request b into dense [n_tokens, hkv, d]
+    K and V arrays (uses the oracle's own slot function)."""
+    hkv, d = k_cache.shape[1], k_cache.shape[3]
+    k = np.empty((n_tokens, hkv, d), dtype=k_cache.dtype)
+    v = np.empty((n_tokens, hkv, d), dtype=v_cache.dtype)
     for p in range(n_tokens):
         s = slot(block_tables, b, p, bs)
-        out[p] = cache[s // bs, :, s % bs, :]
-    return out
+        k[p] = k_cache[s // bs, :, s % bs, :]
+        v[p] = v_cache[s // bs, :, :, s % bs]
+    return k, v

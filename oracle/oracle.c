@@ -64,6 +64,10 @@ uint16_t orc_bf16_rne(float x) {
   return bf16_rne_double((double)x);
 }
 
+void orc_bf16_rne_array(const double* x, uint16_t* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = bf16_rne_double(x[i]);
+}
+
 static double g_bf16[65536];
 __attribute__((constructor)) static void init_table(void) {
   for (uint32_t b = 0; b < 65536u; ++b) g_bf16[b] = orc_bf16_value((uint16_t)b);
@@ -100,8 +104,13 @@ int64_t orc_slot(const int32_t* bt, int bt_stride, int bs, int b, int pos) {
   return (int64_t)page * bs + pos % bs;
 }
 
-static inline int64_t row_index(const orc_layer* L, int64_t page, int g, int row) {
+/* K element (page, g, row, dim) sits at k_index + dim; V element at
+ * v_index + dim * bs (V pages are stored dim-major). */
+static inline int64_t k_index(const orc_layer* L, int64_t page, int g, int row) {
   return ((page * L->hkv + g) * L->bs + row) * L->d;
+}
+static inline int64_t v_index(const orc_layer* L, int64_t page, int g, int row) {
+  return (page * L->hkv + g) * (int64_t)L->d * L->bs + row;
 }
 
 /* O4: norm -> rope -> cache write, in that order (reading of the vLLM day-0
@@ -130,12 +139,12 @@ int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
     for (int g = 0; g < L->hkv; ++g) {
       orc_rmsnorm(k_in + ((int64_t)t * L->hkv + g) * d, kw, d, L->eps, tmp);
       if (L->use_rope) orc_rope(tmp, d, pos, L->theta);
-      uint16_t* krow = kc + row_index(L, page, g, row);
-      uint16_t* vrow = vc + row_index(L, page, g, row);
+      uint16_t* krow = kc + k_index(L, page, g, row);
+      uint16_t* vrow = vc + v_index(L, page, g, row);
       const float* v = v_in + ((int64_t)t * L->hkv + g) * d;
       for (int i = 0; i < d; ++i) {
         krow[i] = bf16_rne_double(tmp[i]);
-        vrow[i] = orc_bf16_rne(v[i]);
+        vrow[(int64_t)i * L->bs] = orc_bf16_rne(v[i]);
       }
     }
   }
@@ -162,8 +171,8 @@ static int attend_row(const orc_layer* L, const double* qh, int h, const uint16_
   for (int j = lo; j <= t; ++j) {
     int32_t page = bt[(int64_t)b * bt_stride + j / L->bs];
     if (page < 0 || page >= num_blocks) { free(s); free(rows); return -1; }
-    int64_t r = row_index(L, page, g, j % L->bs);
-    rows[j - lo] = r;
+    int64_t r = k_index(L, page, g, j % L->bs);
+    rows[j - lo] = v_index(L, page, g, j % L->bs);
     double dot = 0.0;
     for (int i = 0; i < d; ++i) dot += qh[i] * bf(kc[r + i]);
     s[j - lo] = L->scale * dot;
@@ -174,7 +183,7 @@ static int attend_row(const orc_layer* L, const double* qh, int h, const uint16_
   for (int j = 0; j < n; ++j) {
     double e = exp(s[j] - m);
     z += e;
-    for (int i = 0; i < d; ++i) out[i] += e * bf(vc[rows[j] + i]);
+    for (int i = 0; i < d; ++i) out[i] += e * bf(vc[rows[j] + (int64_t)i * L->bs]);
   }
   for (int i = 0; i < d; ++i) out[i] /= z;
   free(s);
@@ -221,7 +230,7 @@ void orc_attn_partial(const orc_layer* L, const double* qh, int h, const uint16_
   double* s = (double*)malloc(sizeof(double) * (size_t)n);
   double m = -INFINITY;
   for (int j = j0; j < j1; ++j) {
-    int64_t r = row_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
+    int64_t r = k_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
     double dot = 0.0;
     for (int i = 0; i < d; ++i) dot += qh[i] * bf(kc[r + i]);
     s[j - j0] = L->scale * dot;
@@ -229,10 +238,10 @@ void orc_attn_partial(const orc_layer* L, const double* qh, int h, const uint16_
   }
   double l = 0.0;
   for (int j = j0; j < j1; ++j) {
-    int64_t r = row_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
+    int64_t r = v_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
     double e = exp(s[j - j0] - m);
     l += e;
-    for (int i = 0; i < d; ++i) ot[i] += e * bf(vc[r + i]);
+    for (int i = 0; i < d; ++i) ot[i] += e * bf(vc[r + (int64_t)i * L->bs]);
   }
   for (int i = 0; i < d; ++i) ot[i] /= l;
   *lse = m + log(l);

@@ -19,10 +19,11 @@
  *                "architecture" (GQA 4 KV x 128) and "kvCacheGiBPerRequest".
  * Where the pages leave a step open the reading taken is stated next to it.
  *
- * Cache layout (the oracle's own statement of it): for each layer, K and V are
- * arrays of bf16 bit patterns indexed [page][kv_head][row 0..15][dim 0..127];
- * logical token p of request b lives in physical page block_tables[b][p/16],
- * row p%16.
+ * Cache layout (the oracle's own statement of the library's format): for each
+ * layer K is an array of bf16 bit patterns indexed
+ * [page][kv_head][row 0..15][dim 0..127] and V one indexed
+ * [page][kv_head][dim 0..127][row 0..15]; logical token p of request b lives
+ * in physical page block_tables[b][p/16], row p%16.
  */
 #ifndef FLINT_ORACLE_H
 #define FLINT_ORACLE_H
@@ -49,6 +50,8 @@ typedef struct {
  * neighbouring bf16 values by comparing exact distances (NaN stays NaN). */
 uint16_t orc_bf16_rne(float x);
 double orc_bf16_value(uint16_t b);
+/* O1 applied to n reals (rounds each fp64 value once, no fp32 step). */
+void orc_bf16_rne_array(const double* x, uint16_t* y, int64_t n);
 
 /* O2: per-head RMSNorm: y = x / sqrt(mean(x^2) + eps) * w, n values. */
 void orc_rmsnorm(const float* x, const float* w, int n, double eps, double* y);

@@ -14,7 +14,9 @@ GQA with 32 query and 4 KV heads of dim 128, bf16 KV, learned sinks):
   * sink logits            ~ N(0,1) fp32, one per query head
   * norm weights           1.0 (workloads) or ~ 1 + 0.1 N(0,1) (tests)
   * bf16 cache contents    N(0,1) fp32 draws truncated to their top 16 bits
-                           (a way to draw bf16 values; not the method's rounding)
+                           (a way to draw bf16 values; not the method's rounding);
+                           multi-GB caches use torch's generator on the GPU
+                           (normal_bf16_bits_torch) instead of PCG64
   * page tables            a seeded permutation of the physical pages
   * ragged lengths         uniform integers in [lo, hi], inclusive
 """
@@ -39,6 +41,23 @@ def normal_bf16_bits(seed: int, stream: tuple, shape) -> np.ndarray:
     """uint16 bf16 bit patterns: N(0,1) fp32 draws truncated to their top 16 bits."""
     x = normal(seed, stream, shape)
     return (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def torch_seed(seed: int, stream: tuple) -> int:
+    """63-bit seed for a torch.Generator, derived from (seed, *stream)."""
+    st = np.random.SeedSequence([int(seed), *map(int, stream)]).generate_state(1, np.uint64)[0]
+    return int(st) & ((1 << 63) - 1)
+
+
+def normal_bf16_bits_torch(seed: int, stream: tuple, shape, device="cpu"):
+    """Like normal_bf16_bits but drawn by torch's generator on `device` (for
+    multi-GB caches: fast on the GPU).  Returns an int16 tensor of bf16 bit
+    patterns: N(0,1) fp32 draws truncated to their top 16 bits."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(seed, stream))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
+    return (x.view(torch.int32) >> 16).to(torch.int16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

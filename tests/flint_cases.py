@@ -1,0 +1,184 @@
+"""Shared builders for the GPU parity tests: seeded inputs (synth), the
+oracle's expected values, and uploads for the HIP path.  Nothing here feeds a
+GPU result back into the oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import synth
+
+TOL = 4e-3          # max |GPU - oracle| on fp32 attention outputs (bf16 KV)
+SENTINEL = 0x7FC1   # NaN bit pattern in every cache slot nobody wrote
+
+
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+def up(a):
+    """numpy -> cuda tensor (uint16 arrays travel as int16 bits)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(dev())
+
+
+def down16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def layers(window):
+    import full_gqa_decode_amd as fl
+    rope = 1 if window else 0
+    # the library receives eps as fp32; the oracle uses that same value
+    eps = float(np.float32(1e-6))
+    return (oracle.layer(window=window, use_rope=rope, eps=eps),
+            fl.layer(window=window, use_rope=rope, rms_eps=eps))
+
+
+class DecodeCase:
+    """B requests of context lengths `ctxs` with a shuffled (or ring) paged
+    cache.  Raw q/k/v ~ N(0,1); every token a request still needs is appended
+    (both sides); the new token of request b is at position ctxs[b]-1."""
+
+    def __init__(self, seed, ctxs, window=0, ring=False, weights_one=True, extra_pages=3):
+        self.seed, self.ctxs, self.window = seed, list(ctxs), window
+        self.L, self.FL = layers(window)
+        B = len(ctxs)
+        self.B = B
+        tag = (hash((tuple(ctxs), window, ring)) & 0xFFFF,)
+        maxctx = max(ctxs)
+        logical = -(-maxctx // 16)
+        self.bt_stride = logical + 1
+        if ring:
+            self.bt, nb = synth.ring_block_table(seed, tag + (synth.PERM,), B, logical, 33,
+                                                 self.bt_stride)
+        else:
+            self.bt, nb = synth.shuffled_block_table(seed, tag + (synth.PERM,), B,
+                                                     [-(-c // 16) for c in ctxs], self.bt_stride)
+        self.num_blocks = nb + extra_pages
+        self.qw = synth.norm_weight(seed, tag + (synth.QW,), 128, weights_one)
+        self.kw = synth.norm_weight(seed, tag + (synth.KW,), 128, weights_one)
+        self.sinks = synth.normal(seed, tag + (synth.SINK,), 32)
+        # tokens to append: all of them, or (ring) only the pages the window can see
+        toks, q_rows = [], []
+        for b, c in enumerate(ctxs):
+            first = 0
+            if ring:
+                first = max(0, ((c - 1) // 16 - 32) * 16)
+            toks.append((b, first, c))
+        self.toks = toks
+        T = sum(c - f for _, f, c in toks)
+        self.T = T
+        self.q_in = np.zeros((T, 32, 128), np.float32)
+        self.k_in = np.empty((T, 4, 128), np.float32)
+        self.v_in = np.empty((T, 4, 128), np.float32)
+        self.pos = np.empty(T, np.int32)
+        self.slots = np.empty(T, np.int32)
+        self.last_row = np.empty(B, np.int64)
+        o = 0
+        for b, f, c in toks:
+            n = c - f
+            self.k_in[o:o + n] = synth.normal(seed, tag + (synth.K, b), (n, 4, 128))
+            self.v_in[o:o + n] = synth.normal(seed, tag + (synth.V, b), (n, 4, 128))
+            self.q_in[o + n - 1] = synth.normal(seed, tag + (synth.Q, b), (32, 128))
+            self.pos[o:o + n] = np.arange(f, c)
+            for p in range(f, c):
+                self.slots[o + p - f] = oracle.slot(self.bt, b, p)
+            self.last_row[b] = o + n - 1
+            o += n
+        self.seq_lens = np.array(ctxs, np.int32)
+
+    def oracle_cache(self):
+        """O4 for every token's K/V; q only for each request's new token.
+        Returns (q_hat of the new tokens [B,32,128] fp64, K cache, V cache)."""
+        kc = np.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, np.uint16)
+        vc = np.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, np.uint16)
+        oracle.append(self.L, self.q_in[:1], self.k_in, self.v_in, self.qw, self.kw, self.pos,
+                      self.slots, kc, vc, want_q=False)
+        r = self.last_row
+        q = oracle.append(self.L, self.q_in[r], self.k_in[r], self.v_in[r], self.qw, self.kw,
+                          self.pos[r], np.full(len(r), -1, np.int32), kc, vc)
+        return q, kc, vc
+
+    def expected(self):
+        q, kc, vc = self.oracle_cache()
+        out = oracle.attn_decode(self.L, q, kc, vc, self.bt, self.seq_lens, self.sinks)
+        return out, q, kc, vc
+
+    def run_gpu(self, pages_per_split=0, workspace=None):
+        """append every token, then decode; returns (out, q_out, kc, vc) tensors."""
+        import torch
+        import full_gqa_decode_amd as fl
+        kd = torch.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
+                        device=dev())
+        vd = torch.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
+                        device=dev())
+        qd = up(self.q_in)
+        fl.flint_qk_norm_rope_append(self.FL, qd, up(self.k_in), up(self.v_in), up(self.qw),
+                                     up(self.kw), up(self.pos), up(self.slots), qd, kd, vd)
+        qdec = qd[torch.from_numpy(self.last_row).to(dev())].contiguous()
+        out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        fl.flint_attn_decode(self.FL, qdec, kd, vd, up(self.bt), up(self.seq_lens),
+                             max(self.ctxs), up(self.sinks), out, workspace=workspace,
+                             pages_per_split=pages_per_split)
+        torch.cuda.synchronize()
+        return out, qd, kd, vd
+
+
+class CacheDecodeCase:
+    """Decode only: the bf16 cache and the fp32 q are drawn directly (no
+    append), so K2/K3 are tested on their own."""
+
+    def __init__(self, seed, ctxs, window=0, ring=False, q_scale=1.0):
+        self.L, self.FL = layers(window)
+        self.ctxs = list(ctxs)
+        B = len(ctxs)
+        self.B = B
+        tag = (hash((tuple(ctxs), window, ring, 7)) & 0xFFFF,)
+        logical = -(-max(ctxs) // 16)
+        self.bt_stride = logical + 2
+        if ring:
+            self.bt, nb = synth.ring_block_table(seed, tag + (synth.PERM,), B, logical, 33,
+                                                 self.bt_stride)
+        else:
+            self.bt, nb = synth.shuffled_block_table(seed, tag + (synth.PERM,), B,
+                                                     [-(-c // 16) for c in ctxs], self.bt_stride)
+        self.num_blocks = nb
+        self.kc = synth.normal_bf16_bits(seed, tag + (synth.KC,), oracle.k_cache_shape(nb))
+        self.vc = synth.normal_bf16_bits(seed, tag + (synth.VC,), oracle.v_cache_shape(nb))
+        self.q = synth.normal(seed, tag + (synth.Q,), (B, 32, 128)) * np.float32(q_scale)
+        self.sinks = synth.normal(seed, tag + (synth.SINK,), 32)
+        self.seq_lens = np.array(ctxs, np.int32)
+
+    def expected(self):
+        return oracle.attn_decode(self.L, self.q.astype(np.float64), self.kc, self.vc, self.bt,
+                                  self.seq_lens, self.sinks)
+
+    def run_gpu(self, pages_per_split=0, sinks=None, seq_lens=None, bt=None, max_seq_len=None):
+        import torch
+        import full_gqa_decode_amd as fl
+        out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        fl.flint_attn_decode(self.FL, up(self.q), up(self.kc), up(self.vc),
+                             up(self.bt if bt is None else bt),
+                             up(self.seq_lens if seq_lens is None else seq_lens),
+                             max(self.ctxs) if max_seq_len is None else max_seq_len,
+                             up(self.sinks if sinks is None else sinks), out,
+                             pages_per_split=pages_per_split)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+
+def max_err(got, ref):
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
+
+
+def bf16_ulp_diff(a, b):
+    """|a - b| in bf16 ulps for two uint16 arrays of finite values."""
+    def key(x):
+        x = x.astype(np.int64)
+        return np.where(x & 0x8000, 0x8000 - (x & 0x7FFF), 0x8000 + x)
+    return np.abs(key(a) - key(b))

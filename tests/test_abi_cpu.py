@@ -1,0 +1,150 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad host-visible arguments before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import full_gqa_decode_amd as fl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(flint_\w+)\s*\(", src))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fl.lib()
+    declared = _declared_symbols()
+    assert {"flint_qk_norm_rope_append", "flint_attn_decode", "flint_attn_prefill"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert declared == {s[0] for s in fl.SIGNATURES}
+
+
+def test_abi_version_and_status_strings():
+    lib = fl.lib()
+    assert lib.flint_abi_version() == 1
+    for s, name in fl.STATUS_NAMES.items():
+        assert lib.flint_status_string(s).decode() == name
+
+
+# fake device pointers: validation must fail before they are ever used
+P = 0x100000
+Q = 0x200000
+WS = 0x300000
+
+
+def _decode(L, **kw):
+    a = dict(num_seqs=1, q=P, k=Q, v=Q + 0x1000, nb=4, bt=P + 0x10000, bt_stride=4, sl=P + 0x20000,
+             max_seq_len=64, sinks=P + 0x30000, out=P + 0x40000, ws=WS, ws_bytes=1 << 20, pps=0)
+    a.update(kw)
+    return fl.lib().flint_attn_decode_ex(C.byref(L), a["num_seqs"], a["q"], a["k"], a["v"], a["nb"],
+                                          a["bt"], a["bt_stride"], a["sl"], a["max_seq_len"],
+                                          a["sinks"], a["out"], a["ws"], a["ws_bytes"], a["pps"],
+                                          None)
+
+
+INVALID, UNSUPPORTED, WS_SMALL = 1, 2, 3
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(sinks=None), INVALID),
+    (dict(nb=0), INVALID),
+    (dict(bt_stride=0), INVALID),
+    (dict(max_seq_len=0), INVALID),
+    (dict(max_seq_len=65), INVALID),       # > bt_stride * 16
+    (dict(num_seqs=-1), INVALID),
+    (dict(pps=-1), INVALID),
+    (dict(q=P + 4), INVALID),              # misaligned
+    (dict(out=P), INVALID),                # aliases q
+    (dict(ws=WS + 8, ws_bytes=1 << 20, max_seq_len=64, pps=1), INVALID),  # workspace alignment
+])
+def test_decode_rejects_bad_arguments(kw, status):
+    L = fl.full_layer()
+    assert _decode(L, **kw) == status
+    assert fl.lib().flint_last_error().decode() != ""
+
+
+def test_decode_workspace_too_small():
+    L = fl.full_layer()
+    need = fl.flint_attn_decode_workspace_size(L, 1, 64, pages_per_split=1)
+    assert need > 0
+    assert _decode(L, ws_bytes=need - 1, pps=1) == WS_SMALL
+    assert _decode(L, ws=None, pps=1) == WS_SMALL
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, UNSUPPORTED),
+    ("block_size", 32, UNSUPPORTED),
+    ("num_kv_heads", 0, UNSUPPORTED),
+    ("num_q_heads", 16, UNSUPPORTED),
+    ("window", -1, INVALID),
+    ("use_rope", 2, INVALID),
+    ("softmax_scale", float("inf"), INVALID),
+])
+def test_layer_validation(field, value, status):
+    L = fl.full_layer()
+    setattr(L, field, value)
+    assert _decode(L) == status
+
+
+def test_zero_requests_is_a_no_op():
+    assert _decode(fl.full_layer(), num_seqs=0, q=None, out=None) == 0
+
+
+def test_append_rejects_bad_arguments():
+    lib = fl.lib()
+    L = fl.sliding_layer()
+    args = [C.byref(L), 1, P, P + 0x10000, P + 0x20000, P + 0x30000, P + 0x40000, P + 0x50000,
+            P + 0x60000, P + 0x70000, None, Q, Q + 0x10000, 4, None]
+    bad = list(args)
+    bad[10] = P + 0x80000  # both q outputs set
+    assert lib.flint_qk_norm_rope_append(*bad) == INVALID
+    bad = list(args)
+    bad[9] = None  # no q output
+    assert lib.flint_qk_norm_rope_append(*bad) == INVALID
+    bad = list(args)
+    bad[13] = 0  # no pages
+    assert lib.flint_qk_norm_rope_append(*bad) == INVALID
+    bad = list(args)
+    bad[11] = Q + 2  # misaligned cache
+    assert lib.flint_qk_norm_rope_append(*bad) == INVALID
+    bad = list(args)
+    bad[1] = -1
+    assert lib.flint_qk_norm_rope_append(*bad) == INVALID
+    bad = list(args)
+    bad[1] = 0  # nothing to do
+    assert lib.flint_qk_norm_rope_append(*bad) == 0
+
+
+def test_prefill_rejects_bad_arguments():
+    lib = fl.lib()
+    L = fl.full_layer()
+    base = [C.byref(L), 1, P, P + 0x10000, 32, Q, Q + 0x10000, 4, P + 0x20000, 4, P + 0x30000, 64,
+            P + 0x40000, P + 0x50000, None, 0, None]
+    for idx, val in ((4, 65), (11, 65), (11, 0), (2, None), (13, None), (7, 0), (2, P + 2)):
+        bad = list(base)
+        bad[idx] = val
+        assert lib.flint_attn_prefill(*bad) == INVALID, (idx, val)
+
+
+def test_decode_plan_covers_every_page():
+    L = fl.full_layer()
+    for B, ctx, pps in ((1, 100000, 0), (1, 4096, 0), (64, 131072, 0), (3, 17, 0), (1, 100000, 7)):
+        p, s = fl.flint_attn_decode_plan(L, B, ctx, pps)
+        pages = -(-ctx // 16)
+        assert p >= 1 and s >= 1 and (s - 1) * p < pages <= s * p
+    Ls = fl.sliding_layer()
+    p, s = fl.flint_attn_decode_plan(Ls, 1, 100000, 0)
+    assert s * p >= 33 and (s - 1) * p < 33

@@ -1,0 +1,132 @@
+"""GPU parity of the MFMA prefill path (K1 append with bf16 q -> K4) against
+the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from flint_cases import SENTINEL, TOL, dev, layers, max_err, up
+
+pytestmark = pytest.mark.gpu
+
+
+class PrefillCase:
+    """Requests with (seq_len, q_len): every token is appended; the last q_len
+    rows of each request are the chunk's queries."""
+
+    def __init__(self, seed, reqs, window=0):
+        self.L, self.FL = layers(window)
+        self.reqs = reqs
+        B = len(reqs)
+        tag = (hash((tuple(reqs), window, 11)) & 0xFFFF,)
+        self.bt_stride = max(-(-s // 16) for s, _ in reqs) + 1
+        self.bt, nb = synth.shuffled_block_table(seed, tag + (synth.PERM,), B,
+                                                 [-(-s // 16) for s, _ in reqs], self.bt_stride)
+        self.num_blocks = nb + 2
+        self.sinks = synth.normal(seed, tag + (synth.SINK,), 32)
+        self.qw = synth.norm_weight(seed, tag + (synth.QW,), 128, False)
+        self.kw = synth.norm_weight(seed, tag + (synth.KW,), 128, False)
+        T = sum(s for s, _ in reqs)
+        self.k_in = np.empty((T, 4, 128), np.float32)
+        self.v_in = np.empty((T, 4, 128), np.float32)
+        self.q_in = np.empty((T, 32, 128), np.float32)
+        self.pos = np.empty(T, np.int32)
+        self.slots = np.empty(T, np.int32)
+        chunk_rows, cu = [], [0]
+        o = 0
+        for b, (s, ql) in enumerate(reqs):
+            self.k_in[o:o + s] = synth.normal(seed, tag + (synth.K, b), (s, 4, 128))
+            self.v_in[o:o + s] = synth.normal(seed, tag + (synth.V, b), (s, 4, 128))
+            self.q_in[o:o + s] = synth.normal(seed, tag + (synth.Q, b), (s, 32, 128))
+            self.pos[o:o + s] = np.arange(s)
+            self.slots[o:o + s] = [oracle.slot(self.bt, b, p) for p in range(s)]
+            chunk_rows += list(range(o + s - ql, o + s))
+            cu.append(cu[-1] + ql)
+            o += s
+        self.chunk_rows = np.array(chunk_rows, np.int64)
+        self.cu = np.array(cu, np.int32)
+        self.seq_lens = np.array([s for s, _ in reqs], np.int32)
+        self.max_q = max(ql for _, ql in reqs)
+
+    def expected(self, rows=None):
+        """Oracle: append K/V for every token, q for the chunk rows, round q to
+        bf16 (the prefill q format), then O7 on `rows` of the chunk."""
+        kc = np.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, np.uint16)
+        vc = np.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, np.uint16)
+        oracle.append(self.L, self.q_in[:1], self.k_in, self.v_in, self.qw, self.kw, self.pos,
+                      self.slots, kc, vc, want_q=False)
+        need = self.chunk_rows if rows is None else self.chunk_rows[rows]
+        skip = np.full(len(need), -1, np.int32)
+        qh = oracle.append(self.L, self.q_in[need], self.k_in[need], self.v_in[need], self.qw,
+                           self.kw, self.pos[need], skip, kc, vc)
+        qb = oracle.bf16_rne_f64(qh)
+        qf = synth.bf16_bits_to_f32(qb).astype(np.float64)
+        full_q = np.zeros((len(self.chunk_rows), 32, 128))
+        idx = np.arange(len(self.chunk_rows)) if rows is None else np.asarray(rows)
+        full_q[idx] = qf
+        return oracle.attn_prefill(self.L, full_q, self.cu, kc, vc, self.bt, self.seq_lens,
+                                   self.sinks, rows=None if rows is None else idx)
+
+    def run_gpu(self):
+        import torch
+        import full_gqa_decode_amd as fl
+        kd = torch.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
+                        device=dev())
+        vd = torch.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
+                        device=dev())
+        qb = torch.empty(self.q_in.shape, dtype=torch.int16, device=dev())
+        fl.flint_qk_norm_rope_append(self.FL, up(self.q_in), up(self.k_in), up(self.v_in),
+                                     up(self.qw), up(self.kw), up(self.pos), up(self.slots), qb,
+                                     kd, vd)
+        qc = qb[torch.from_numpy(self.chunk_rows).to(dev())].contiguous()
+        out = torch.empty((len(self.chunk_rows), 32, 128), dtype=torch.float32, device=dev())
+        fl.flint_attn_prefill(self.FL, qc, up(self.cu), self.max_q, kd, vd, up(self.bt),
+                              up(self.seq_lens), int(self.seq_lens.max()), up(self.sinks), out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), kd, vd, qb
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_prefill_whole_prompt(window):
+    case = PrefillCase(0, [(700, 700)], window=window)
+    got, _, _, _ = case.run_gpu()
+    assert max_err(got, case.expected()) <= TOL
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_prefill_chunk_ragged_batch(window):
+    # chunks that start mid-page, a one-row chunk, a chunk shorter than a page
+    case = PrefillCase(1, [(1000, 300), (37, 1), (530, 530), (65, 9)], window=window)
+    got, _, _, _ = case.run_gpu()
+    assert max_err(got, case.expected()) <= TOL
+
+
+def test_last_prefill_row_matches_decode_at_same_position():
+    import torch
+    import full_gqa_decode_amd as fl
+    case = PrefillCase(2, [(900, 64)], window=0)
+    got, kd, vd, _ = case.run_gpu()
+    # decode of the last row with fp32 q from the same append
+    qf = torch.empty(case.q_in.shape, dtype=torch.float32, device=dev())
+    kd2 = torch.empty_like(kd)
+    vd2 = torch.empty_like(vd)
+    fl.flint_qk_norm_rope_append(case.FL, up(case.q_in), up(case.k_in), up(case.v_in),
+                                 up(case.qw), up(case.kw), up(case.pos), up(case.slots), qf, kd2,
+                                 vd2)
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev())
+    fl.flint_attn_decode(case.FL, qf[-1:].contiguous(), kd, vd, up(case.bt), up(case.seq_lens),
+                         900, up(case.sinks), out)
+    torch.cuda.synchronize()
+    assert max_err(got[-1], out.cpu().numpy()[0].astype(np.float64)) <= 2 * TOL
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_prefill_config4_32768_sampled_rows(window):
+    # causal prefill of a 32,768-token prompt; the oracle checks sampled rows
+    case = PrefillCase(0, [(32768, 32768)], window=window)
+    got, _, _, _ = case.run_gpu()
+    rows = np.unique(np.concatenate([np.arange(48), np.arange(0, 32768, 1024),
+                                     np.arange(32768 - 16, 32768)]))
+    ref = case.expected(rows=rows)
+    assert max_err(got[rows], ref[rows]) <= TOL
+    assert np.all(np.isfinite(got))

@@ -63,6 +63,18 @@ def test_bf16_rne_matches_torch():
         assert np.array_equal(oracle.bf16_rne(arr), _torch_bf16_bits(arr))
 
 
+def test_bf16_rne_f64_matches_torch_and_midpoints():
+    r = synth.rng(0, 99, 2)
+    x = r.standard_normal(50_000).astype(np.float32)
+    assert np.array_equal(oracle.bf16_rne_f64(x.astype(np.float64)), _torch_bf16_bits(x))
+    # a value just above a bf16 midpoint rounds up even though its fp32 image
+    # (the midpoint itself, a tie) would round to even = down
+    mid = 1.0 + 2.0 ** -8                      # halfway between 1.0 and 1 + 2^-7
+    assert oracle.bf16_rne_f64([mid])[0] == 0x3F80
+    assert oracle.bf16_rne_f64([mid + 2.0 ** -40])[0] == 0x3F81
+    assert oracle.bf16_rne_f64([-(mid + 2.0 ** -40)])[0] == 0xBF81
+
+
 def test_bf16_nan_stays_nan():
     b = oracle.bf16_rne([np.float32("nan")])[0]
     assert (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
@@ -134,11 +146,11 @@ def _paged(L, dense_k_bits, dense_v_bits, seed, perm=True):
     bt = np.full((1, pages + 2), -1, np.int32)
     bt[0, :pages] = order[:pages]
     kc = np.full((pages + extra, L.hkv, L.bs, L.d), 0x7FC0, np.uint16)  # NaN where unused
-    vc = kc.copy()
+    vc = np.full((pages + extra, L.hkv, L.d, L.bs), 0x7FC0, np.uint16)
     for p in range(n):
         pg, r = bt[0, p // L.bs], p % L.bs
         kc[pg, :, r, :] = dense_k_bits[p]
-        vc[pg, :, r, :] = dense_v_bits[p]
+        vc[pg, :, :, r] = dense_v_bits[p]
     return kc, vc, bt
 
 
@@ -361,11 +373,11 @@ def test_ring_aliasing_outside_window_is_bit_identical():
     logical = -(-n // 16)
     rbt, nb = synth.ring_block_table(23, (5,), 1, logical, 33, logical + 1)
     rk = np.zeros((nb, 4, 16, 128), np.uint16)
-    rv = rk.copy()
+    rv = np.zeros((nb, 4, 128, 16), np.uint16)
     for p in range(n):  # later tokens overwrite ring pages, as appends would
         pg = rbt[0, p // 16]
         rk[pg, :, p % 16] = kb[p]
-        rv[pg, :, p % 16] = vb[p]
+        rv[pg, :, :, p % 16] = vb[p]
     sl = np.array([n], np.int32)
     assert np.array_equal(oracle.attn_decode(Ls, q, kc, vc, bt, sl, sinks),
                           oracle.attn_decode(Ls, q, rk, rv, rbt, sl, sinks))
@@ -394,7 +406,7 @@ def test_append_places_rows_and_rounds_v_like_torch():
     v = synth.normal(30, (4,), (T, 4, 128))
     ones = np.ones(128, np.float32)
     kc = np.full((nb, 4, 16, 128), 0xBEEF, np.uint16)
-    vc = kc.copy()
+    vc = np.full((nb, 4, 128, 16), 0xBEEF, np.uint16)
     qo = oracle.append(L, q, k, v, ones, ones, pos, slots, kc, vc)
     written = np.zeros((nb, 16), bool)
     for t in range(T):
@@ -402,7 +414,7 @@ def test_append_places_rows_and_rounds_v_like_torch():
             continue
         pg, r = divmod(int(slots[t]), 16)
         written[pg, r] = True
-        assert np.array_equal(vc[pg, :, r], _torch_bf16_bits(v[t]))
+        assert np.array_equal(vc[pg, :, :, r], _torch_bf16_bits(v[t]))
         for g in range(4):
             kk = oracle.rope(oracle.rmsnorm(k[t, g], ones), pos[t])
             # the oracle rounds the fp64 value once; torch rounds its fp32 image
@@ -410,7 +422,7 @@ def test_append_places_rows_and_rounds_v_like_torch():
             assert np.max(np.abs(kc[pg, g, r].astype(int) - ref)) <= 1
     untouched = ~written
     assert np.all(kc.transpose(0, 2, 1, 3)[untouched] == 0xBEEF)
-    assert np.all(vc.transpose(0, 2, 1, 3)[untouched] == 0xBEEF)
+    assert np.all(vc.transpose(0, 3, 1, 2)[untouched] == 0xBEEF)
     # q out: norm then rope; norms are preserved by the rotation
     for t in (0, 17):
         for h in (0, 31):
@@ -421,7 +433,7 @@ def test_append_places_rows_and_rounds_v_like_torch():
 def test_append_rejects_slot_out_of_range():
     L = oracle.layer()
     kc = np.zeros((2, 4, 16, 128), np.uint16)
-    vc = kc.copy()
+    vc = np.zeros((2, 4, 128, 16), np.uint16)
     x = np.zeros((1, 4, 128), np.float32)
     with pytest.raises(ValueError):
         oracle.append(L, np.zeros((1, 32, 128), np.float32), x, x, np.ones(128), np.ones(128),
