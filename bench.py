@@ -112,31 +112,53 @@ def main():
     log(f"bench: inputs ready in {time.time() - t0:.1f}s")
     ws_bytes = max(fl.flint_attn_decode_workspace_size(FULL, 1, CTX),
                    fl.flint_attn_decode_workspace_size(SLIDE, 1, CTX), 256)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
 
-    def layer_step(L):
+    def layer_step_unfused(L):
         Ld = FULL if L["full"] else SLIDE
         fl.flint_qk_norm_rope_append(Ld, L["q_in"], L["k_in"], L["v_in"], ones, ones, pos,
                                      L["slots"], L["q_out"], L["kc"], L["vc"])
         fl.flint_attn_decode(Ld, L["q_out"], L["kc"], L["vc"], L["bt"], seq_lens, CTX,
                              L["sinks"], L["out"], workspace=ws)
 
+    def layer_step(L):
+        # one launch per layer (plus the split merge on full layers): the fused
+        # norm/RoPE/append of the new token and the attention
+        Ld = FULL if L["full"] else SLIDE
+        fl.flint_attn_decode_step(Ld, L["q_in"], L["k_in"], L["v_in"], ones, ones, L["slots"],
+                                  L["kc"], L["vc"], L["bt"], seq_lens, CTX, L["sinks"], L["out"],
+                                  workspace=ws)
+
     def step():
         for L in layers:
             layer_step(L)
 
-    # eager once (also the reference the graph must reproduce)
-    step()
-    torch.cuda.synchronize()
-    eager = [L["out"].clone() for L in layers]
+    def step_unfused():
+        for L in layers:
+            layer_step_unfused(L)
 
     stream = torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g, stream=stream):
-            step()
+
+    def capture(fn):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(gr, stream=stream):
+                fn()
+        return gr
+
+    # eager once per path; both paths and their graphs must agree bit for bit
+    step_unfused()
+    torch.cuda.synchronize()
+    eager = [L["out"].clone() for L in layers]
+    step()
+    torch.cuda.synchronize()
+    for L, e in zip(layers, eager):
+        assert torch.equal(L["out"], e), "fused step differs from append + decode"
+    g = capture(step)
+    g_unfused = capture(step_unfused)
     for _ in range(args.warmup):
         g.replay()
+        g_unfused.replay()
     torch.cuda.synchronize()
     for L, e in zip(layers, eager):
         assert torch.equal(L["out"], e), "graph replay differs from eager"
@@ -156,16 +178,20 @@ def main():
     us_step = ev[0].elapsed_time(ev[-1]) * 1e3 / args.steps
     log(f"bench: {args.steps} steps, {us_step:.1f} us/step (median {statistics.median(per):.1f}, "
         f"wall {wall * 1e6 / args.steps:.1f} us/step)")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(args.steps):
+            g_unfused.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us_unfused = e0.elapsed_time(e1) * 1e3 / args.steps
+    log(f"bench: unfused (append, then decode) {us_unfused:.1f} us/step")
 
     # dominant kernel: full-layer decode, timed over back-to-back replays of the
     # 14 full layers on the stream they run on
-    gf = torch.cuda.CUDAGraph()
     full_layers = [L for L in layers if L["full"]]
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(gf, stream=stream):
-            for L in full_layers:
-                fl.flint_attn_decode(FULL, L["q_out"], L["kc"], L["vc"], L["bt"], seq_lens, CTX,
-                                     L["sinks"], L["out"], workspace=ws)
+    gf = capture(lambda: [layer_step(L) for L in full_layers])
     reps = 20
     for _ in range(3):
         gf.replay()
@@ -202,8 +228,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": "Flint decode attention, all 49 layers (14 full-context NoPE over "
                                "100,000 keys + 35 RoPE sliding over 513 keys), batch 1, one "
-                               "decode step incl. norm/RoPE/append of the new token, bf16 paged "
-                               "KV (16-token pages, shuffled), HIP graph",
+                               "decode step incl. norm/RoPE/append of the new token (fused, one "
+                               "launch per layer + split merge), bf16 paged KV (16-token pages, "
+                               "shuffled), HIP graph",
                    "global_batch": 1, "seq_len": CTX, "layers": LAYERS,
                    "full_layers": len(FULL_LAYERS), "window": WINDOW, "parallelism": "none"},
         "hbm_gbps": round(gbps_step, 1),
@@ -212,7 +239,8 @@ def main():
         "us_per_step_median": round(statistics.median(per), 2),
         "us_per_step_p10": round(float(np.percentile(per, 10)), 2),
         "us_per_step_p90": round(float(np.percentile(per, 90)), 2),
-        "roofline": {"kernel": "full-layer decode (split-K + merge), 100,000 keys",
+        "us_per_step_unfused": round(us_unfused, 2),
+        "roofline": {"kernel": "full-layer fused decode step (split-K + merge), 100,000 keys",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None, "us_per_launch": round(us_full, 2),

@@ -7,6 +7,7 @@ been built this module raises on first use; there is no fallback.
 
 Functions carry the C names of include/flint.h:
     flint_qk_norm_rope_append, flint_attn_decode, flint_attn_prefill,
+    flint_attn_decode_step (append + decode fused into one launch),
 plus the size / plan queries.  bf16 tensors (K/V caches, prefill q) may be
 torch.bfloat16, torch.int16 or torch.uint16: only their bits are used.
 """
@@ -72,6 +73,8 @@ SIGNATURES = [
     ("flint_attn_decode_workspace_size_ex", _SZ, [_LP, _I, _I, _I]),
     ("flint_attn_decode_ex", C.c_int,
      [_LP, _I, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _I, _P]),
+    ("flint_attn_decode_step", C.c_int,
+     [_LP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _I, _P]),
     ("flint_attn_decode_plan", C.c_int, [_LP, _I, _I, _I, C.POINTER(_I), C.POINTER(_I)]),
     ("flint_attn_prefill_workspace_size", _SZ, [_LP, _I, _I, _I]),
     ("flint_attn_prefill", C.c_int,
@@ -186,13 +189,14 @@ def flint_attn_decode(L: FlintAttnLayer, q, k_cache, v_cache, block_tables, seq_
                       max_seq_len: int, sinks, out, workspace=None, pages_per_split: int = 0,
                       stream=None):
     """Decode attention for q.shape[0] requests; writes out [B, Hq, 128] fp32.
-    `workspace` (uint8 tensor) is allocated here when not given; pass one to
-    keep the call free of allocations (e.g. under HIP-graph capture)."""
+    `workspace` (uint8 tensor) is allocated (zero-filled) here when not given;
+    pass one (zero-filled once, e.g. torch.zeros) to keep the call free of
+    allocations, e.g. under HIP-graph capture."""
     torch = _torch()
     B = q.shape[0]
     need = flint_attn_decode_workspace_size(L, B, max_seq_len, pages_per_split)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().flint_attn_decode_ex(
         C.byref(L), B, _ptr(q, _f32(), "q"), _ptr(k_cache, _b16(), "k_cache"),
@@ -202,6 +206,31 @@ def flint_attn_decode(L: FlintAttnLayer, q, k_cache, v_cache, block_tables, seq_
         _ptr(out, _f32(), "out"),
         None if workspace is None else workspace.data_ptr(), ws_bytes, pages_per_split,
         _stream(stream)))
+    return out
+
+
+def flint_attn_decode_step(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_norm_w,
+                           slot_mapping, k_cache, v_cache, block_tables, seq_lens,
+                           max_seq_len: int, sinks, out, q_out=None, workspace=None,
+                           pages_per_split: int = 0, stream=None):
+    """One fused decode step of one layer: norm/RoPE/append of each request's
+    new token (raw q_in/k_in/v_in) and decode attention, in one launch."""
+    torch = _torch()
+    B = q_in.shape[0]
+    need = flint_attn_decode_workspace_size(L, B, max_seq_len, pages_per_split)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q_in.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().flint_attn_decode_step(
+        C.byref(L), B, _ptr(q_in, _f32(), "q_in"), _ptr(k_in, _f32(), "k_in"),
+        _ptr(v_in, _f32(), "v_in"), _ptr(q_norm_w, _f32(), "q_norm_w"),
+        _ptr(k_norm_w, _f32(), "k_norm_w"), _ptr(slot_mapping, _i32(), "slot_mapping"),
+        _ptr(q_out, _f32(), "q_out"), _ptr(k_cache, _b16(), "k_cache"),
+        _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
+        _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),
+        _ptr(out, _f32(), "out"), None if workspace is None else workspace.data_ptr(), ws_bytes,
+        pages_per_split, _stream(stream)))
     return out
 
 

@@ -40,9 +40,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // The split plan is a pure function of its arguments (no device query), so the
 // workspace size and the launch always agree.  kTargetWorkgroups sizes the
-// grid for MI355X's 256 compute units at two workgroups each.
+// grid for MI355X's 256 compute units at one long-running workgroup each.
 constexpr int kMaxContext = 1 << 24;
-constexpr int kTargetWorkgroups = 512;
+constexpr int kTargetWorkgroups = 256;
 constexpr size_t kWsAlign = 256;
 
 flint_status check_layer(const flint_attn_layer* L) {
@@ -77,16 +77,24 @@ int64_t max_key_pages(const flint_attn_layer* L, int32_t max_seq_len) {
 struct Plan {
   int32_t pages_per_split;
   int32_t num_splits;
+  int32_t multi_head;  // workgroups cover four KV heads (long ranges)
 };
 
 Plan make_plan(const flint_attn_layer* L, int32_t num_seqs, int32_t max_seq_len, int32_t pps) {
   const int64_t pages = max_key_pages(L, max_seq_len);
+  // Long ranges with num_kv_heads a multiple of 4 run workgroups that cover
+  // four KV heads each, so a page's head tiles are read together.
+  const bool mh = pages > flint::kSinglePages && L->num_kv_heads % 4 == 0;
   int64_t p = pps;
   if (p <= 0) {
-    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * L->num_kv_heads;
+    // about kTargetWorkgroups workgroups; a short range (the 513-key window)
+    // becomes small splits so its bytes spread over many CUs, a long one keeps
+    // at least two pages per wave
+    const int64_t units =
+        (int64_t)(num_seqs > 0 ? num_seqs : 1) * (mh ? L->num_kv_heads / 4 : L->num_kv_heads);
     const int64_t splits = (kTargetWorkgroups + units - 1) / units;
     p = (pages + splits - 1) / splits;
-    const int64_t min_pages = 2 * flint::kDecodeWaves;  // two pages per wave
+    const int64_t min_pages = mh ? 4 : flint::kShortMinPages;
     if (p < min_pages) p = min_pages;
   }
   if (p > pages) p = pages;
@@ -94,15 +102,30 @@ Plan make_plan(const flint_attn_layer* L, int32_t num_seqs, int32_t max_seq_len,
   Plan pl;
   pl.pages_per_split = (int32_t)p;
   pl.num_splits = (int32_t)((pages + p - 1) / p);
+  pl.multi_head = mh;
   return pl;
 }
 
-size_t decode_ws_bytes(const flint_attn_layer* L, int32_t num_seqs, const Plan& pl) {
-  if (pl.num_splits <= 1 || num_seqs <= 0) return 0;
+// Workspace of a multi-split plan: [partial outputs | partial log-sum-exps],
+// each part 256-byte aligned.
+struct WsLayout {
+  size_t part_o, part_lse, total;
+};
+
+size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+WsLayout ws_layout(const flint_attn_layer* L, int32_t num_seqs, const Plan& pl) {
+  WsLayout w{0, 0, 0};
+  if (pl.num_splits <= 1 || num_seqs <= 0) return w;
   const size_t rows = (size_t)num_seqs * pl.num_splits * L->num_q_heads;
-  size_t o = rows * 128 * sizeof(float);
-  o = (o + kWsAlign - 1) / kWsAlign * kWsAlign;
-  return o + rows * sizeof(float);
+  w.part_o = 0;
+  w.part_lse = align_up(rows * 128 * sizeof(float));
+  w.total = w.part_lse + align_up(rows * sizeof(float));
+  return w;
+}
+
+size_t decode_ws_bytes(const flint_attn_layer* L, int32_t num_seqs, const Plan& pl) {
+  return ws_layout(L, num_seqs, pl).total;
 }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -203,13 +226,17 @@ size_t flint_attn_decode_workspace_size(const flint_attn_layer* L, int32_t num_s
   return flint_attn_decode_workspace_size_ex(L, num_seqs, max_seq_len, 0);
 }
 
-flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, const float* q,
-                                  const uint16_t* k_cache, const uint16_t* v_cache,
-                                  int32_t num_blocks, const int32_t* block_tables,
-                                  int32_t bt_stride, const int32_t* seq_lens,
-                                  int32_t max_seq_len, const float* sinks, float* out,
-                                  void* workspace, size_t workspace_bytes,
-                                  int32_t pages_per_split, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the decode entry points; fills the launch arguments.
+flint_status prepare_decode(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* k_cache,
+                            const uint16_t* v_cache, int32_t num_blocks,
+                            const int32_t* block_tables, int32_t bt_stride,
+                            const int32_t* seq_lens, int32_t max_seq_len, const float* sinks,
+                            float* out, void* workspace, size_t workspace_bytes,
+                            int32_t pages_per_split, flint::DecodeArgs* a) {
   flint_status st = check_layer(L);
   if (st != FLINT_OK) return st;
   if (num_seqs < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
@@ -218,20 +245,17 @@ flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, c
   if (max_seq_len < 1 || max_seq_len > kMaxContext)
     return fail(FLINT_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [1, %d]", max_seq_len,
                 kMaxContext);
-  if (num_seqs == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !sinks || !out)
+  if (num_seqs == 0) return FLINT_OK;
+  if (!k_cache || !v_cache || !block_tables || !seq_lens || !sinks || !out)
     return fail(FLINT_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   if (num_blocks < 1) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_blocks %d < 1", num_blocks);
   if (bt_stride < 1) return fail(FLINT_ERR_INVALID_ARGUMENT, "bt_stride %d < 1", bt_stride);
   if ((int64_t)max_seq_len > (int64_t)bt_stride * 16)
     return fail(FLINT_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds bt_stride*16 = %lld",
                 max_seq_len, (long long)bt_stride * 16);
-  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+  if (!aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(sinks, 4))
-    return fail(FLINT_ERR_INVALID_ARGUMENT, "misaligned pointer (q, out, caches need 16 B)");
-  const size_t qbytes = (size_t)num_seqs * L->num_q_heads * 128 * sizeof(float);
-  if (overlap(q, qbytes, out, qbytes))
-    return fail(FLINT_ERR_INVALID_ARGUMENT, "out must not alias q");
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "misaligned pointer (out, caches need 16 B)");
   const Plan pl = make_plan(L, num_seqs, max_seq_len, pages_per_split);
   const size_t need = decode_ws_bytes(L, num_seqs, pl);
   if (need > 0) {
@@ -241,28 +265,88 @@ flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, c
     if (!aligned(workspace, kWsAlign))
       return fail(FLINT_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kWsAlign);
   }
+  *a = flint::DecodeArgs{};
+  a->k_cache = const_cast<uint16_t*>(k_cache);
+  a->v_cache = const_cast<uint16_t*>(v_cache);
+  a->block_tables = block_tables;
+  a->seq_lens = seq_lens;
+  a->sinks = sinks;
+  a->out = out;
+  const WsLayout wl = ws_layout(L, num_seqs, pl);
+  a->part_o = need ? (float*)((char*)workspace + wl.part_o) : nullptr;
+  a->part_lse = need ? (float*)((char*)workspace + wl.part_lse) : nullptr;
+  a->num_seqs = num_seqs;
+  a->num_kv_heads = L->num_kv_heads;
+  a->num_blocks = num_blocks;
+  a->bt_stride = bt_stride;
+  a->window = L->window;
+  a->max_seq_len = max_seq_len;
+  a->pages_per_split = pl.pages_per_split;
+  a->num_splits = pl.num_splits;
+  a->multi_head = pl.multi_head;
+  a->qscale = L->softmax_scale * 1.4426950408889634f;
+  a->use_rope = L->use_rope;
+  a->rope_theta = L->rope_theta;
+  a->rms_eps = L->rms_eps;
+  return FLINT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, const float* q,
+                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  int32_t num_blocks, const int32_t* block_tables,
+                                  int32_t bt_stride, const int32_t* seq_lens,
+                                  int32_t max_seq_len, const float* sinks, float* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t pages_per_split, void* stream) {
   flint::DecodeArgs a;
+  flint_status st = prepare_decode(L, num_seqs, k_cache, v_cache, num_blocks, block_tables,
+                                   bt_stride, seq_lens, max_seq_len, sinks, out, workspace,
+                                   workspace_bytes, pages_per_split, &a);
+  if (st != FLINT_OK || num_seqs == 0) return st == FLINT_OK ? ok() : st;
+  if (!q) return fail(FLINT_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(q, 16)) return fail(FLINT_ERR_INVALID_ARGUMENT, "misaligned pointer (q needs 16 B)");
+  const size_t qbytes = (size_t)num_seqs * L->num_q_heads * 128 * sizeof(float);
+  if (overlap(q, qbytes, out, qbytes))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "out must not alias q");
   a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  a.sinks = sinks;
-  a.out = out;
-  const size_t rows = (size_t)num_seqs * pl.num_splits * L->num_q_heads;
-  size_t obytes = (rows * 128 * sizeof(float) + kWsAlign - 1) / kWsAlign * kWsAlign;
-  a.part_o = need ? (float*)workspace : nullptr;
-  a.part_lse = need ? (float*)((char*)workspace + obytes) : nullptr;
-  a.num_seqs = num_seqs;
-  a.num_kv_heads = L->num_kv_heads;
-  a.num_blocks = num_blocks;
-  a.bt_stride = bt_stride;
-  a.window = L->window;
-  a.max_seq_len = max_seq_len;
-  a.pages_per_split = pl.pages_per_split;
-  a.num_splits = pl.num_splits;
-  a.qscale = L->softmax_scale * 1.4426950408889634f;
   return hip_status(flint::launch_decode(a, (hipStream_t)stream), "decode launch");
+}
+
+flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
+                                    const float* q_in, const float* k_in, const float* v_in,
+                                    const float* q_norm_w, const float* k_norm_w,
+                                    const int32_t* slot_mapping, float* q_out,
+                                    uint16_t* k_cache, uint16_t* v_cache, int32_t num_blocks,
+                                    const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* seq_lens, int32_t max_seq_len,
+                                    const float* sinks, float* out, void* workspace,
+                                    size_t workspace_bytes, int32_t pages_per_split,
+                                    void* stream) {
+  flint::DecodeArgs a;
+  flint_status st = prepare_decode(L, num_seqs, k_cache, v_cache, num_blocks, block_tables,
+                                   bt_stride, seq_lens, max_seq_len, sinks, out, workspace,
+                                   workspace_bytes, pages_per_split, &a);
+  if (st != FLINT_OK || num_seqs == 0) return st == FLINT_OK ? ok() : st;
+  if (!q_in || !k_in || !v_in || !q_norm_w || !k_norm_w || !slot_mapping)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(q_in, 4) || !aligned(k_in, 4) || !aligned(v_in, 4) || !aligned(q_norm_w, 4) ||
+      !aligned(k_norm_w, 4) || !aligned(slot_mapping, 4) || (q_out && !aligned(q_out, 4)))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  const size_t qbytes = (size_t)num_seqs * L->num_q_heads * 128 * sizeof(float);
+  if (overlap(q_in, qbytes, out, qbytes) || (q_out && overlap(q_out, qbytes, out, qbytes)))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "out must not alias q_in or q_out");
+  a.q_in = q_in;
+  a.k_in = k_in;
+  a.v_in = v_in;
+  a.q_w = q_norm_w;
+  a.k_w = k_norm_w;
+  a.slots = slot_mapping;
+  a.q_out = q_out;
+  return hip_status(flint::launch_decode(a, (hipStream_t)stream), "decode step launch");
 }
 
 flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, const float* q,

@@ -24,39 +24,6 @@ namespace flint {
 
 namespace {
 
-// fp64 -> bf16 bits with one rounding: round to odd at fp32 precision (24
-// bits, enough guard bits for bf16's 8), then round to nearest even.
-__device__ __forceinline__ uint16_t bf16_bits_rne_f64(double x) {
-  if (x != x) return 0x7fc0u;
-  float f = (float)x;
-  const double back = (double)f;
-  if (back != x) {
-    uint32_t u = __float_as_uint(f);
-    if (fabs(back) > fabs(x)) u -= 1u;  // the nearest fp32 toward zero
-    f = __uint_as_float(u | 1u);
-  }
-  return bf16_bits_rne(f);
-}
-
-__device__ __forceinline__ double wave_sum_f64(double x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// cos/sin of pos * theta^(-2i/128), in fp64 with a two-part 2*pi reduction,
-// accurate to ~1e-16 for every position up to the 262,144-token context.
-__device__ __forceinline__ void rope_cos_sin(int pos, int i, float theta, double* c, double* s) {
-  const double inv_freq = exp2(-(2.0 * i / kHeadDim) * log2((double)theta));
-  const double ang = (double)pos * inv_freq;
-  const double two_pi_hi = 6.283185307179586;           // 2*pi rounded to fp64
-  const double two_pi_lo = 2.4492935982947064e-16;      // 2*pi - two_pi_hi
-  const double k = rint(ang * 0.15915494309189535);     // ang / (2*pi)
-  double r = fma(-k, two_pi_hi, ang);
-  r = fma(-k, two_pi_lo, r);
-  sincos(r, s, c);
-}
-
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int lane = threadIdx.x & 63;
   const int hq = a.num_q_heads, hkv = a.num_kv_heads;
@@ -87,24 +54,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   if (!is_q && !write_cache) return;
   const float* x = is_q ? a.q_in + ((int64_t)t * hq + task) * kHeadDim
                         : a.k_in + ((int64_t)t * hkv + (task - hq)) * kHeadDim;
-  const float* w = is_q ? a.q_w : a.k_w;
-  const double x0 = x[lane], x1 = x[lane + 64];
-
-  // RMSNorm over the head's 128 values.
-  const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
-  const double r = 1.0 / sqrt(ss / kHeadDim + (double)a.rms_eps);
-  double y0 = x0 * r * (double)w[lane];
-  double y1 = x1 * r * (double)w[lane + 64];
-
-  // Rotate-half RoPE: pair (lane, lane+64) turns by pos * theta^(-2*lane/128).
-  if (a.use_rope) {
-    double c, s;
-    rope_cos_sin(pos < 0 ? 0 : pos, lane, a.rope_theta, &c, &s);
-    const double r0 = y0 * c - y1 * s;
-    const double r1 = y1 * c + y0 * s;
-    y0 = r0;
-    y1 = r1;
-  }
+  // RMSNorm over the head's 128 values, then the rotate-half RoPE pair
+  // (lane, lane+64) turned by pos * theta^(-2*lane/128).
+  double cs = 1.0, sn = 0.0;
+  if (a.use_rope) rope_cos_sin(pos < 0 ? 0 : pos, lane, a.rope_theta, &cs, &sn);
+  double y0, y1;
+  norm_rope_head(x[lane], x[lane + 64], is_q ? a.q_w : a.k_w, a.rms_eps, a.use_rope, cs, sn,
+                 lane, &y0, &y1);
 
   if (is_q) {
     if (bad) y0 = y1 = __builtin_nan("");

@@ -1,17 +1,18 @@
-// decode.hip -- K2 split-K flash-decode and K3 log-sum-exp merge with sinks.
+// decode.hip -- K2 split-K flash-decode (optionally fused with the append of
+// the new token) and K3 log-sum-exp merge with sinks.
 //
 // What is computed ("Day-0 Support for Flint on vLLM", hnkhoi.com, "Model
-// architecture": GQA with 32 query / 4 KV heads, learned attention sinks;
-// newruntime.com, "What happened": 35 layers over a 513-token window, 14 over
-// the full context):
+// architecture": GQA with 32 query / 4 KV heads, learned attention sinks,
+// per-head Q/K RMSNorm, RoPE on the sliding layers; newruntime.com, "What
+// happened": 35 layers over a 513-token window, 14 over the full context,
+// fused normalisation / rotary / cache operations):
 //   out_h = sum_j e^{s_j} V_j / (e^{sink_h} + sum_j e^{s_j}),
 //   s_j = scale * <q_h, K_j>, keys lo..t of the request.
 //
-// Design for gfx950.  One workgroup = kDecodeWaves wave64s on one
-// (split, KV head, request); its waves take the split's 16-token pages
-// round-robin.  The eight query heads of a KV group share every K and V row,
-// so per page the work is two small dense contractions, done on the matrix
-// cores:
+// Design for gfx950.  One workgroup = WAVES wave64s on one (split, KV head,
+// request); its waves take the split's 16-token pages round-robin.  The eight
+// query heads of a KV group share every K and V row, so per page the work is
+// two small dense contractions, done on the matrix cores:
 //   scores  S[16 tok x 16]  = K_page[16 x 128] . Qhl^T[128 x 16]
 //           (4 x v_mfma_f32_16x16x32_bf16; columns 0-7 carry bf16(q*c), columns
 //           8-15 the bf16 remainder q*c - bf16(q*c) of the same heads, so the
@@ -24,11 +25,18 @@
 // (4 tokens) of V dim-row per MFMA, with no LDS staging and no transposes.
 // The score tile lands in exactly the lanes that need it as the P operand of
 // the value MFMA, so the online softmax (DPP row_ror:8 for the hi+lo sum,
-// wavefront shuffles for the page max) never moves P between lanes.  The next
-// page's loads are issued before the current page is processed.  Waves merge
-// through LDS at the end; splits are merged by K3, which folds in the sink.
-// Bound: HBM (8 KiB of K+V per page and KV head against ~20 VALU and 12 MFMA
-// instructions per wave).
+// wavefront shuffles for the page max) never moves P between lanes.
+//
+// Latency: page ids are fetched one page ahead of the K/V loads; in a split
+// the next page's K is requested right after the score MFMAs consume this
+// page's K, and its V right after the value MFMAs.  A short key range (the
+// 513-key window) is one split per (request, KV head) whose waves issue every
+// page load up front and fold the sink in directly, so no merge launch runs.
+// Fused step: the workgroup normalises/rotates its own 8 query heads (one wave
+// per head, into LDS) and the split holding the new token writes its K/V row
+// into the cache and substitutes it in registers, so append and attention are
+// one launch.  Bound: HBM (8 KiB of K+V per page and KV head against ~20 VALU
+// and 12 MFMA instructions per wave).
 #include "device.h"
 #include "launch.h"
 
@@ -36,74 +44,320 @@ namespace flint {
 
 namespace {
 
-constexpr int kWaves = kDecodeWaves;
-constexpr int kThreads = kWaves * 64;
+constexpr int kMergeThreads = 512;
 
 struct PageRegs {
   bf16x8 k[4];  // K rows: MFMA A operand, 32 dims each
   u32x2 v[8];   // V: 4 tokens x 1 dim per 16-dim block (MFMA B operand)
 };
 
-__device__ __forceinline__ void load_page(const DecodeArgs& a, int pg, int g, int n, int gq,
-                                          PageRegs& r) {
-  const int hkv = a.num_kv_heads;
+__device__ __forceinline__ void load_k(const DecodeArgs& a, int pg, int g, int n, int gq,
+                                       PageRegs& r) {
   const uint16_t* kp =
-      a.k_cache + (((int64_t)pg * hkv + g) * kPage + n) * kHeadDim + gq * 8;
+      a.k_cache + (((int64_t)pg * a.num_kv_heads + g) * kPage + n) * kHeadDim + gq * 8;
 #pragma unroll
   for (int c = 0; c < 4; ++c) r.k[c] = *(const bf16x8*)(kp + c * 32);
+}
+
+__device__ __forceinline__ void load_v(const DecodeArgs& a, int pg, int g, int n, int gq,
+                                       PageRegs& r) {
   const uint16_t* vp =
-      a.v_cache + (((int64_t)pg * hkv + g) * kHeadDim + n) * kPage + gq * 4;
+      a.v_cache + (((int64_t)pg * a.num_kv_heads + g) * kHeadDim + n) * kPage + gq * 4;
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) r.v[nb] = *(const u32x2*)(vp + nb * 16 * kPage);
 }
 
-// Page id of logical page p of request b, or -1 when outside [0, num_blocks).
+// Page id of logical page p of request b (wave-uniform scalar load), or -1
+// when outside [0, num_blocks).
 __device__ __forceinline__ int page_id(const DecodeArgs& a, int b, int p) {
   const int pg = a.block_tables[(int64_t)b * a.bt_stride + p];
   return (pg >= 0 && pg < a.num_blocks) ? pg : -1;
 }
 
-template <bool SINGLE, bool WINDOWED>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
+// Online-softmax state of one wave: PV accumulator (rows gq*4+i are the bf16
+// parts (gq < 2) and remainders (gq >= 2) of heads, columns dims nb*16+n),
+// running max of head n&7 (log2 units) and this lane's share of the sum.
+struct WaveState {
+  f32x4 acc[8];
+  float m_run;
+  float l_part;
+};
+
+// One page: scores, mask of the ragged ends, online softmax, value MFMAs.
+// The K registers are dead after the score MFMAs and may be reloaded by the
+// caller from that point (done through the `after_scores` callback).
+template <typename AfterScores>
+__device__ __forceinline__ void consume_page(PageRegs& r, const bf16x8 (&qop)[4], int p, int lo,
+                                             int t, int n, int gq, WaveState& st,
+                                             AfterScores after_scores) {
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[c], qop[c], sc, 0, 0, 0);
+  after_scores();
+  float sv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sv[i] = sc[i] + lane_xor8(sc[i]);
+
+  // ragged ends of the key range: mask scores, zero V so unwritten slots
+  // (which may hold any bits) cannot reach the accumulator
+  const int tok0 = p * kPage;
+  if (tok0 < lo || tok0 + kPage - 1 > t) {
+    uint32_t keep[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + gq * 4 + i;
+      const bool ok = tok >= lo && tok <= t;
+      if (!ok) sv[i] = -INFINITY;
+      keep[i] = ok ? 0xffffu : 0u;
+    }
+    const uint32_t mx = keep[0] | (keep[1] << 16), my = keep[2] | (keep[3] << 16);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      r.v[nb][0] &= mx;
+      r.v[nb][1] &= my;
+    }
+  }
+
+  // online softmax in log2 units (q carries scale*log2(e))
+  float pmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
+  pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+  const float m_new = fmaxf(st.m_run, pmax);
+  if (__any(m_new > st.m_run)) {
+    const float alpha = exp2_fast(st.m_run - m_new);
+    st.l_part *= alpha;
+    float al[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (gq * 4 + i) & 7);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.acc[nb][i] *= al[i];
+  }
+  st.m_run = m_new;
+  float pv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pv[i] = exp2_fast(sv[i] - m_new);
+  st.l_part += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+
+  // P operand: row n = head n&7; n < 8 bf16(p), n >= 8 its bf16 remainder
+  const f32x2 p01 = {pv[0], pv[1]}, p23 = {pv[2], pv[3]};
+  const bf16x2 h01 = __builtin_convertvector(p01, bf16x2);
+  const bf16x2 h23 = __builtin_convertvector(p23, bf16x2);
+  const bf16x2 r01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2), bf16x2);
+  const bf16x2 r23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2), bf16x2);
+  const bf16x2 s01 = (n < 8) ? h01 : r01;
+  const bf16x2 s23 = (n < 8) ? h23 : r23;
+  const bf16x4 pop = {s01[0], s01[1], s23[0], s23[1]};
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+        pop, __builtin_bit_cast(bf16x4, r.v[nb]), st.acc[nb], 0, 0, 0);
+}
+
+// The new token's K row / V column, computed by this workgroup, replace what
+// the page loads returned for row tr of the last page.
+__device__ __forceinline__ void substitute_new_token(PageRegs& r, const uint16_t* knew,
+                                                     const uint16_t* vnew, int tr, int n,
+                                                     int gq) {
+  if (n == tr) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.k[c] = *(const bf16x8*)(knew + c * 32 + gq * 8);
+  }
+  if (gq == (tr >> 2)) {
+    const int e = tr & 3;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint32_t bits = vnew[nb * 16 + n];
+      uint32_t wv = r.v[nb][e >> 1];
+      wv = (e & 1) ? ((wv & 0xffffu) | (bits << 16)) : ((wv & 0xffff0000u) | bits);
+      r.v[nb][e >> 1] = wv;
+    }
+  }
+}
+
+// K2.  WAVES waves per workgroup.  MAXP > 1: the split has at most
+// WAVES * MAXP pages and every wave issues all its page loads up front;
+// MAXP == 1: the pipelined loop.  SINGLE: the split covers the whole key
+// range, so the sink is folded in here and the output written directly.
+// FUSED: also the norm/RoPE of q and the append of the new token.
+//
+// Start-up latency: the first loads (q, the first page ids and their K/V) are
+// issued before seq_lens[b] has arrived, for the key range of a request of
+// the host-side bound max_seq_len (the common batch-1 case); once seq_len is
+// known they are kept if it equals that bound and reissued otherwise.  Every
+// speculative page id is read inside the caller's block-table row and
+// validated before it addresses the cache.
+template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED>
+__global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_kernel(
+    DecodeArgs a) {
+  constexpr int kThreads = WAVES * 64;
+  constexpr int NR = MAXP > 1 ? MAXP : 1;  // page buffers per wave
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, gq = lane >> 4;
   const int hq = a.num_kv_heads * kGroup;
 
-  __shared__ float sm_o[kWaves][kGroup][kHeadDim];
-  __shared__ float sm_m[kWaves][kGroup];
-  __shared__ float sm_l[kWaves][kGroup];
-  __shared__ int sm_bad[kWaves];
+  __shared__ float sm_o[WAVES][kGroup][kHeadDim];
+  __shared__ float sm_m[WAVES][kGroup];
+  __shared__ float sm_l[WAVES][kGroup];
+  __shared__ int sm_bad[WAVES];
+  __shared__ float sm_q[FUSED ? kGroup : 1][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_knew[FUSED ? kHeadDim : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_vnew[FUSED ? kHeadDim : 8];
+  __shared__ int sm_fused_bad;
 
-  const int seq_len = a.seq_lens[b];
-  if (seq_len < 1 || seq_len > a.max_seq_len) {
-    if (s == 0) {  // poison this request's result
-      for (int i = tid; i < kGroup * kHeadDim; i += kThreads) {
-        const int h = g * kGroup + (i >> 7);
-        if (SINGLE) a.out[((int64_t)b * hq + h) * kHeadDim + (i & 127)] = __builtin_nanf("");
-        else if ((i & 127) == 0) a.part_lse[(int64_t)b * a.num_splits * hq + h] = __builtin_nanf("");
+  // ---- loads that do not wait for seq_len -------------------------------
+  constexpr int QPW = (kGroup + WAVES - 1) / WAVES;  // fused: q heads per wave
+  double x0[QPW], x1[QPW];    // fused: raw q of heads w, w+WAVES, ...
+  f32x4 qraw[8];              // unfused: fp32 q of column n, dims c*32+gq*8..+7
+  if (FUSED) {
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      const int hh = w + j * WAVES;
+      x0[j] = x1[j] = 0.0;
+      if (hh < kGroup) {
+        const float* x = a.q_in + ((int64_t)b * hq + g * kGroup + hh) * kHeadDim;
+        x0[j] = x[lane];
+        x1[j] = x[lane + 64];
       }
     }
-    return;
-  }
-  const int t = seq_len - 1;
-  const int lo = WINDOWED ? max(0, t - a.window + 1) : 0;
-  const int first_page = lo / kPage, last_page = t / kPage;
-  const int p_begin = first_page + s * a.pages_per_split;
-  if (p_begin > last_page) return;  // empty split; K3 never reads it
-  const int p_end = min(p_begin + a.pages_per_split, last_page + 1);
-
-  // q operand: column n holds head n&7; n < 8 the bf16 part of q*c, n >= 8 the
-  // bf16 remainder.  Lane group gq holds dims c*32 + gq*8 .. +7 of block c.
-  bf16x8 qop[4];
-  {
+  } else {
     const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim + gq * 8;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const f32x4 x0 = *(const f32x4*)(qh + c * 32);
-      const f32x4 x1 = *(const f32x4*)(qh + c * 32 + 4);
-      const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      qraw[2 * c] = *(const f32x4*)(qh + c * 32);
+      qraw[2 * c + 1] = *(const f32x4*)(qh + c * 32 + 4);
+    }
+  }
+  // page range of this split for a request whose query sits at position tt
+  auto range = [&](int tt, int& lo_, int& pb, int& pe) {
+    lo_ = WINDOWED ? max(0, tt - a.window + 1) : 0;
+    pb = lo_ / kPage + s * a.pages_per_split;
+    pe = min(pb + a.pages_per_split, tt / kPage + 1);
+  };
+  int lo, p_begin, p_end;
+  range(a.max_seq_len - 1, lo, p_begin, p_end);
+  // fused, rotating layers: this lane's RoPE angle for the speculated
+  // position, computed while the loads below are in flight
+  double cs = 1.0, sn = 0.0;
+  if (FUSED && a.use_rope) rope_cos_sin(a.max_seq_len - 1, lane, a.rope_theta, &cs, &sn);
+  PageRegs r[NR];
+  int bad = 0;
+  auto issue = [&](int k) {  // page id and loads of this wave's k-th page
+    const int p = p_begin + w + k * WAVES;
+    if (p < p_end) {
+      int pg = page_id(a, b, p);
+      bad |= pg < 0;
+      pg = max(pg, 0);
+      load_k(a, pg, g, n, gq, r[k]);
+      load_v(a, pg, g, n, gq, r[k]);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NR; ++k) issue(k);
+
+  // ---- the request's real length ------------------------------------------
+  const int seq_len = a.seq_lens[b];
+  const bool len_bad = seq_len < 1 || seq_len > a.max_seq_len;
+  const int t = seq_len - 1;
+  if (!len_bad && seq_len != a.max_seq_len) {  // shorter request: redo the guesses
+    range(t, lo, p_begin, p_end);
+    bad = 0;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) issue(k);
+  }
+  const int last_page = t / kPage;
+  if (len_bad || p_begin > last_page) {
+    // bad request: NaN output; empty split: lse -inf so the merge skips it
+    const float fill = len_bad ? __builtin_nanf("") : -INFINITY;
+    if (SINGLE) {
+      for (int i = tid; i < kGroup * kHeadDim; i += kThreads)
+        a.out[((int64_t)b * hq + g * kGroup + (i >> 7)) * kHeadDim + (i & 127)] = fill;
+    } else if (tid < kGroup) {
+      a.part_lse[((int64_t)b * a.num_splits + s) * hq + g * kGroup + tid] = fill;
+    }
+    return;
+  }
+  const bool has_new = FUSED && p_end == last_page + 1;  // this split holds token t
+
+  // ---- q operand ----------------------------------------------------------
+  // column n holds head n&7; n < 8 the bf16 part of q*c, n >= 8 the bf16
+  // remainder.  Lane group gq holds dims c*32 + gq*8 .. +7 of block c.
+  bf16x8 qop[4];
+  if (FUSED) {
+    // wave w: q heads g*8 + w, w+WAVES, ...; has_new: wave 0 also the K row,
+    // wave 1 the V row
+    if (a.use_rope && t != a.max_seq_len - 1) rope_cos_sin(t, lane, a.rope_theta, &cs, &sn);
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      const int hh = w + j * WAVES;
+      if (hh < kGroup) {
+        double y0, y1;
+        norm_rope_head(x0[j], x1[j], a.q_w, a.rms_eps, a.use_rope, cs, sn, lane, &y0, &y1);
+        sm_q[hh][lane] = (float)y0;
+        sm_q[hh][lane + 64] = (float)y1;
+        if (s == 0 && a.q_out) {
+          float* qo = a.q_out + ((int64_t)b * hq + g * kGroup + hh) * kHeadDim;
+          qo[lane] = (float)y0;
+          qo[lane + 64] = (float)y1;
+        }
+      }
+    }
+    if (has_new && w < 2) {
+      // the slot must be where the page table puts position t
+      const int pg = page_id(a, b, last_page);
+      const int slot = a.slots[b];
+      const bool ok = pg >= 0 && slot == pg * kPage + t % kPage;
+      if (w == 0) {
+        const float* xk = a.k_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+        double y0, y1;
+        norm_rope_head(xk[lane], xk[lane + 64], a.k_w, a.rms_eps, a.use_rope, cs, sn, lane,
+                       &y0, &y1);
+        const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
+        sm_knew[lane] = k0;
+        sm_knew[lane + 64] = k1;
+        if (ok) {
+          uint16_t* dst = a.k_cache + (((int64_t)pg * a.num_kv_heads + g) * kPage + t % kPage) *
+                                          kHeadDim;
+          dst[lane] = k0;
+          dst[lane + 64] = k1;
+        }
+        if (lane == 0) sm_fused_bad = !ok;
+      } else {
+        const float* xv = a.v_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+        const uint16_t v0 = bf16_bits_rne(xv[lane]), v1 = bf16_bits_rne(xv[lane + 64]);
+        sm_vnew[lane] = v0;
+        sm_vnew[lane + 64] = v1;
+        if (ok) {
+          uint16_t* dst = a.v_cache + ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage) +
+                          t % kPage;
+          dst[lane * kPage] = v0;
+          dst[(lane + 64) * kPage] = v1;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float* qh = &sm_q[n & 7][c * 32 + gq * 8];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f32x2 v = {qh[j] * a.qscale, qh[j + 1] * a.qscale};
+        const bf16x2 hi = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
+        const bf16x2 sel = (n < 8) ? hi : lo2;
+        qop[c][j] = sel[0];
+        qop[c][j + 1] = sel[1];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 q0 = qraw[2 * c], q1 = qraw[2 * c + 1];
+      const float xs[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         const f32x2 v = {xs[j] * a.qscale, xs[j + 1] * a.qscale};
@@ -116,128 +370,80 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  f32x4 acc[8];
+  // ---- pages ---------------------------------------------------------------
+  WaveState st;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
-  int bad = 0;
+  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
+  const int tr = t % kPage;
 
-  PageRegs nxt;
-  int p = p_begin + w;
-  if (p < p_end) {
-    int pg = page_id(a, b, p);
-    bad |= pg < 0;
-    load_page(a, pg < 0 ? 0 : pg, g, n, gq, nxt);
-  }
-  for (; p < p_end; p += kWaves) {
-    PageRegs cur = nxt;
-    const int pn = p + kWaves;
-    if (pn < p_end) {
-      int pg = page_id(a, b, pn);
-      bad |= pg < 0;
-      load_page(a, pg < 0 ? 0 : pg, g, n, gq, nxt);
-    }
-
-    // scores for tokens p*16 + gq*4 + i, head n&7 (hi + lo column halves)
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  if (MAXP > 1) {
+    auto nothing = [] {};
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[c], qop[c], sc, 0, 0, 0);
-    float sv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sv[i] = sc[i] + lane_xor8(sc[i]);
-
-    // ragged ends of the key range: mask scores, zero V so unwritten slots
-    // (which may hold any bits) cannot reach the accumulator
-    const int tok0 = p * kPage;
-    if (tok0 < lo || tok0 + kPage - 1 > t) {
-      uint32_t keep[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = tok0 + gq * 4 + i;
-        const bool ok = tok >= lo && tok <= t;
-        if (!ok) sv[i] = -INFINITY;
-        keep[i] = ok ? 0xffffu : 0u;
-      }
-      const uint32_t mx = keep[0] | (keep[1] << 16), my = keep[2] | (keep[3] << 16);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        cur.v[nb][0] &= mx;
-        cur.v[nb][1] &= my;
+    for (int k = 0; k < NR; ++k) {
+      const int p = p_begin + w + k * WAVES;
+      if (p < p_end) {
+        if (FUSED && p == last_page) substitute_new_token(r[k], sm_knew, sm_vnew, tr, n, gq);
+        consume_page(r[k], qop, p, lo, t, n, gq, st, nothing);
       }
     }
-
-    // online softmax in log2 units (q carries scale*log2(e))
-    float pmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
-    pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
-    const float m_new = fmaxf(m_run, pmax);
-    if (__any(m_new > m_run)) {
-      const float alpha = exp2_fast(m_run - m_new);
-      l_part *= alpha;
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, (gq * 4 + i) & 7);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nb][i] *= al[i];
+  } else {
+    // page ids run one page ahead of the loads, the loads one page ahead of the
+    // math: K of the next page is requested as soon as the score MFMAs have
+    // consumed this page's K, V of the next page after the value MFMAs
+    int p = p_begin + w;
+    if (p < p_end) {
+      int pg_ahead = (p + WAVES < p_end) ? page_id(a, b, p + WAVES) : 0;
+      for (; p < p_end; p += WAVES) {
+        const bool has_next = p + WAVES < p_end;
+        bad |= pg_ahead < 0;
+        const int pg_next = max(pg_ahead, 0);
+        if (p + 2 * WAVES < p_end) pg_ahead = page_id(a, b, p + 2 * WAVES);
+        if (FUSED && p == last_page) substitute_new_token(r[0], sm_knew, sm_vnew, tr, n, gq);
+        consume_page(r[0], qop, p, lo, t, n, gq, st, [&] {
+          if (has_next) load_k(a, pg_next, g, n, gq, r[0]);
+        });
+        if (has_next) load_v(a, pg_next, g, n, gq, r[0]);
+      }
     }
-    m_run = m_new;
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = exp2_fast(sv[i] - m_new);
-    l_part += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-
-    // P operand: row n = head n&7; n < 8 bf16(p), n >= 8 its bf16 remainder
-    const f32x2 p01 = {pv[0], pv[1]}, p23 = {pv[2], pv[3]};
-    const bf16x2 h01 = __builtin_convertvector(p01, bf16x2);
-    const bf16x2 h23 = __builtin_convertvector(p23, bf16x2);
-    const bf16x2 r01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2), bf16x2);
-    const bf16x2 r23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2), bf16x2);
-    const bf16x2 s01 = (n < 8) ? h01 : r01;
-    const bf16x2 s23 = (n < 8) ? h23 : r23;
-    const bf16x4 pop = {s01[0], s01[1], s23[0], s23[1]};
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          pop, __builtin_bit_cast(bf16x4, cur.v[nb]), acc[nb], 0, 0, 0);
   }
 
-  // per-wave state -> LDS.  l: sum over the four lane groups of head n&7.
-  // acc rows gq*4+i: gq 0,1 the bf16 parts of heads 0-7, gq 2,3 the remainders.
-  float l_h = l_part + __shfl_xor(l_part, 16);
+  // ---- per-wave state -> LDS -> this split's result -----------------------
+  // l: sum over the four lane groups of head n&7.  acc rows gq*4+i: gq 0,1 the
+  // bf16 parts of heads 0-7, gq 2,3 the remainders.
+  float l_h = st.l_part + __shfl_xor(st.l_part, 16);
   l_h += __shfl_xor(l_h, 32);
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[nb][i] += __shfl_xor(acc[nb][i], 32);
+    for (int i = 0; i < 4; ++i) st.acc[nb][i] += __shfl_xor(st.acc[nb][i], 32);
   if (gq < 2) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[w][gq * 4 + i][nb * 16 + n] = acc[nb][i];
+      for (int i = 0; i < 4; ++i) sm_o[w][gq * 4 + i][nb * 16 + n] = st.acc[nb][i];
   }
   if (lane < kGroup) {
-    sm_m[w][lane] = m_run;
+    sm_m[w][lane] = st.m_run;
     sm_l[w][lane] = l_h;
   }
   bad = __any(bad);
   if (lane == 0) sm_bad[w] = bad;
   __syncthreads();
 
-  int any_bad = 0;
+  int any_bad = (FUSED && has_new) ? sm_fused_bad : 0;
 #pragma unroll
-  for (int v = 0; v < kWaves; ++v) any_bad |= sm_bad[v];
+  for (int v = 0; v < WAVES; ++v) any_bad |= sm_bad[v];
 
   for (int i = tid; i < kGroup * kHeadDim; i += kThreads) {
     const int h = i >> 7, d = i & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm_m[v][h]);
+    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sm_m[v][h]);
     float L = 0.f, o = 0.f;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
+    for (int v = 0; v < WAVES; ++v) {
       const float e = exp2_fast(sm_m[v][h] - M);
       L += e * sm_l[v][h];
       o += e * sm_o[v][h][d];
@@ -248,9 +454,260 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       const float M2 = fmaxf(M, sink);
       const float scale_o = exp2_fast(M - M2);
       const float den = exp2_fast(sink - M2) + L * scale_o;
-      float r = o * scale_o / den;
-      if (any_bad) r = __builtin_nanf("");
-      a.out[((int64_t)b * hq + hg) * kHeadDim + d] = r;
+      float res = o * scale_o / den;
+      if (any_bad) res = __builtin_nanf("");
+      a.out[((int64_t)b * hq + hg) * kHeadDim + d] = res;
+    } else {
+      const int64_t row = ((int64_t)b * a.num_splits + s) * hq + hg;
+      a.part_o[row * kHeadDim + d] = o / L;
+      if (d == 0) a.part_lse[row] = any_bad ? __builtin_nanf("") : M + log2_fast(L);
+    }
+  }
+}
+
+// K2, multi-head form for long key ranges: one workgroup of 8 waves covers all
+// four KV heads of a split's pages -- wave w takes KV head g0 + (w & 3) and
+// every other page of the split (stream w >> 2) -- so the four 4 KiB head
+// tiles of a page (16 KiB contiguous in K and in V) are read together.  On
+// MI355X that lifts the paged stream from ~5.6 to ~6.4 TB/s against per-head
+// workgroups, whose 4 KiB tiles land at random addresses.  Same per-page math
+// (consume_page), same partial format, so the merge kernel is shared.
+constexpr int kMhHeads = 4;    // KV heads per workgroup
+constexpr int kMhStreams = 2;  // page streams per KV head
+
+template <bool SINGLE, bool WINDOWED, bool FUSED>
+__global__ __launch_bounds__(kMhHeads * kMhStreams * 64, 2) void decode_mh_kernel(DecodeArgs a) {
+  constexpr int WAVES = kMhHeads * kMhStreams;
+  constexpr int kThreads = WAVES * 64;
+  const int s = blockIdx.x, g0 = blockIdx.y * kMhHeads, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = w & (kMhHeads - 1), stream = w / kMhHeads;
+  const int g = g0 + hw;  // this wave's KV head
+  const int n = lane & 15, gq = lane >> 4;
+  const int hq = a.num_kv_heads * kGroup;
+
+  __shared__ float sm_o[WAVES][kGroup][kHeadDim];
+  __shared__ float sm_m[WAVES][kGroup];
+  __shared__ float sm_l[WAVES][kGroup];
+  __shared__ int sm_bad[WAVES];
+  __shared__ float sm_q[FUSED ? kMhHeads * kGroup : 1][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_knew[FUSED ? kMhHeads : 1][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_vnew[FUSED ? kMhHeads : 1][kHeadDim];
+  __shared__ int sm_fused_bad[kMhHeads];
+
+  // ---- loads that do not wait for seq_len -------------------------------
+  constexpr int QPW = kMhHeads * kGroup / WAVES;  // fused: q heads per wave (4)
+  double x0[QPW], x1[QPW];
+  f32x4 qraw[8];
+  if (FUSED) {
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {  // q heads g0*8 + w*QPW + j of this workgroup
+      const float* x = a.q_in + ((int64_t)b * hq + g0 * kGroup + w * QPW + j) * kHeadDim;
+      x0[j] = x[lane];
+      x1[j] = x[lane + 64];
+    }
+  } else {
+    const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim + gq * 8;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qraw[2 * c] = *(const f32x4*)(qh + c * 32);
+      qraw[2 * c + 1] = *(const f32x4*)(qh + c * 32 + 4);
+    }
+  }
+  auto range = [&](int tt, int& lo_, int& pb, int& pe) {
+    lo_ = WINDOWED ? max(0, tt - a.window + 1) : 0;
+    pb = lo_ / kPage + s * a.pages_per_split;
+    pe = min(pb + a.pages_per_split, tt / kPage + 1);
+  };
+  int lo, p_begin, p_end;
+  range(a.max_seq_len - 1, lo, p_begin, p_end);
+  double cs = 1.0, sn = 0.0;
+  if (FUSED && a.use_rope) rope_cos_sin(a.max_seq_len - 1, lane, a.rope_theta, &cs, &sn);
+  PageRegs r;
+  int bad = 0;
+  auto issue_first = [&] {
+    const int p = p_begin + stream;
+    if (p < p_end) {
+      int pg = page_id(a, b, p);
+      bad |= pg < 0;
+      pg = max(pg, 0);
+      load_k(a, pg, g, n, gq, r);
+      load_v(a, pg, g, n, gq, r);
+    }
+  };
+  issue_first();
+
+  const int seq_len = a.seq_lens[b];
+  const bool len_bad = seq_len < 1 || seq_len > a.max_seq_len;
+  const int t = seq_len - 1;
+  if (!len_bad && seq_len != a.max_seq_len) {  // shorter request: redo the guesses
+    range(t, lo, p_begin, p_end);
+    bad = 0;
+    issue_first();
+  }
+  const int last_page = t / kPage;
+  if (len_bad || p_begin > last_page) {
+    const float fill = len_bad ? __builtin_nanf("") : -INFINITY;
+    if (SINGLE) {
+      for (int i = tid; i < kMhHeads * kGroup * kHeadDim; i += kThreads)
+        a.out[((int64_t)b * hq + g0 * kGroup + (i >> 7)) * kHeadDim + (i & 127)] = fill;
+    } else if (tid < kMhHeads * kGroup) {
+      a.part_lse[((int64_t)b * a.num_splits + s) * hq + g0 * kGroup + tid] = fill;
+    }
+    return;
+  }
+  const bool has_new = FUSED && p_end == last_page + 1;
+
+  bf16x8 qop[4];
+  if (FUSED) {
+    if (a.use_rope && t != a.max_seq_len - 1) rope_cos_sin(t, lane, a.rope_theta, &cs, &sn);
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+      double y0, y1;
+      norm_rope_head(x0[j], x1[j], a.q_w, a.rms_eps, a.use_rope, cs, sn, lane, &y0, &y1);
+      const int ql = w * QPW + j;
+      sm_q[ql][lane] = (float)y0;
+      sm_q[ql][lane + 64] = (float)y1;
+      if (s == 0 && a.q_out) {
+        float* qo = a.q_out + ((int64_t)b * hq + g0 * kGroup + ql) * kHeadDim;
+        qo[lane] = (float)y0;
+        qo[lane + 64] = (float)y1;
+      }
+    }
+    if (has_new) {  // waves 0-3: K row of head g0+w; waves 4-7: V row of head g0+w-4
+      const int pg = page_id(a, b, last_page);
+      const int slot = a.slots[b];
+      const bool ok = pg >= 0 && slot == pg * kPage + t % kPage;
+      if (stream == 0) {
+        const float* xk = a.k_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+        double y0, y1;
+        norm_rope_head(xk[lane], xk[lane + 64], a.k_w, a.rms_eps, a.use_rope, cs, sn, lane,
+                       &y0, &y1);
+        const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
+        sm_knew[hw][lane] = k0;
+        sm_knew[hw][lane + 64] = k1;
+        if (ok) {
+          uint16_t* dst = a.k_cache + (((int64_t)pg * a.num_kv_heads + g) * kPage + t % kPage) *
+                                          kHeadDim;
+          dst[lane] = k0;
+          dst[lane + 64] = k1;
+        }
+        if (lane == 0) sm_fused_bad[hw] = !ok;
+      } else {
+        const float* xv = a.v_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+        const uint16_t v0 = bf16_bits_rne(xv[lane]), v1 = bf16_bits_rne(xv[lane + 64]);
+        sm_vnew[hw][lane] = v0;
+        sm_vnew[hw][lane + 64] = v1;
+        if (ok) {
+          uint16_t* dst = a.v_cache + ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage) +
+                          t % kPage;
+          dst[lane * kPage] = v0;
+          dst[(lane + 64) * kPage] = v1;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float* qh = &sm_q[hw * kGroup + (n & 7)][c * 32 + gq * 8];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f32x2 v = {qh[j] * a.qscale, qh[j + 1] * a.qscale};
+        const bf16x2 hi = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
+        const bf16x2 sel = (n < 8) ? hi : lo2;
+        qop[c][j] = sel[0];
+        qop[c][j + 1] = sel[1];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 q0 = qraw[2 * c], q1 = qraw[2 * c + 1];
+      const float xs[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f32x2 v = {xs[j] * a.qscale, xs[j + 1] * a.qscale};
+        const bf16x2 hi = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
+        const bf16x2 sel = (n < 8) ? hi : lo2;
+        qop[c][j] = sel[0];
+        qop[c][j + 1] = sel[1];
+      }
+    }
+  }
+
+  WaveState st;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) st.acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_run = -INFINITY;
+  st.l_part = 0.f;
+  const int tr = t % kPage;
+  int p = p_begin + stream;
+  if (p < p_end) {
+    int pg_ahead = (p + kMhStreams < p_end) ? page_id(a, b, p + kMhStreams) : 0;
+    for (; p < p_end; p += kMhStreams) {
+      const bool has_next = p + kMhStreams < p_end;
+      bad |= pg_ahead < 0;
+      const int pg_next = max(pg_ahead, 0);
+      if (p + 2 * kMhStreams < p_end) pg_ahead = page_id(a, b, p + 2 * kMhStreams);
+      if (FUSED && p == last_page) substitute_new_token(r, sm_knew[hw], sm_vnew[hw], tr, n, gq);
+      consume_page(r, qop, p, lo, t, n, gq, st, [&] {
+        if (has_next) load_k(a, pg_next, g, n, gq, r);
+      });
+      if (has_next) load_v(a, pg_next, g, n, gq, r);
+    }
+  }
+
+  // per-wave state -> LDS; the two streams of each KV head merge below
+  float l_h = st.l_part + __shfl_xor(st.l_part, 16);
+  l_h += __shfl_xor(l_h, 32);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.acc[nb][i] += __shfl_xor(st.acc[nb][i], 32);
+  if (gq < 2) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[w][gq * 4 + i][nb * 16 + n] = st.acc[nb][i];
+  }
+  if (lane < kGroup) {
+    sm_m[w][lane] = st.m_run;
+    sm_l[w][lane] = l_h;
+  }
+  bad = __any(bad);
+  if (lane == 0) sm_bad[w] = bad;
+  __syncthreads();
+
+  for (int i = tid; i < kMhHeads * kGroup * kHeadDim; i += kThreads) {
+    const int hh = i >> 10, h = (i >> 7) & 7, d = i & 127;  // KV head, q head, dim
+    int any_bad = (FUSED && has_new) ? sm_fused_bad[hh] : 0;
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMhStreams; ++j) {
+      const int v = hh + j * kMhHeads;
+      any_bad |= sm_bad[v];
+      M = fmaxf(M, sm_m[v][h]);
+    }
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMhStreams; ++j) {
+      const int v = hh + j * kMhHeads;
+      const float e = exp2_fast(sm_m[v][h] - M);
+      L += e * sm_l[v][h];
+      o += e * sm_o[v][h][d];
+    }
+    const int hg = (g0 + hh) * kGroup + h;
+    if (SINGLE) {
+      const float sink = a.sinks[hg] * kLog2e;
+      const float M2 = fmaxf(M, sink);
+      const float scale_o = exp2_fast(M - M2);
+      const float den = exp2_fast(sink - M2) + L * scale_o;
+      float res = o * scale_o / den;
+      if (any_bad) res = __builtin_nanf("");
+      a.out[((int64_t)b * hq + hg) * kHeadDim + d] = res;
     } else {
       const int64_t row = ((int64_t)b * a.num_splits + s) * hq + hg;
       a.part_o[row * kHeadDim + d] = o / L;
@@ -260,60 +717,154 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 }
 
 // K3: out_h = sum_s w_s o_s / (e^{sink_h} + sum_s w_s), w_s = 2^{lse_s - M},
-// in log2 units.  One workgroup per (query head, request), one lane per dim.
-template <bool WINDOWED>
-__global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+// in log2 units.  Every split of the grid left an lse (-inf when it held no
+// key, NaN for a bad request or page), so no load here waits on seq_lens.
+// One workgroup per (query head, request, quarter of the dims): 512 threads =
+// 16 split groups x 32 dims, each group summing every 16th split, the first
+// kMergeChunk of them loaded into registers before the block-wide max is
+// known -- one memory round trip for plans of up to 256 splits.
+constexpr int kMergeDims = 32;
+constexpr int kMergeGroups = kMergeThreads / kMergeDims;
+constexpr int kMergeChunk = 16;
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int d = blockIdx.z * kMergeDims + (tid % kMergeDims), grp = tid / kMergeDims;
   const int hq = a.num_kv_heads * kGroup;
-  float* dst = a.out + ((int64_t)b * hq + h) * kHeadDim + d;
-  const int seq_len = a.seq_lens[b];
-  if (seq_len < 1 || seq_len > a.max_seq_len) {
-    *dst = __builtin_nanf("");
-    return;
+  const int ns = a.num_splits;
+  __shared__ float red_m[kMergeThreads / 64];
+  __shared__ int red_nan[kMergeThreads / 64];
+  __shared__ float red_o[kMergeGroups][kMergeDims];
+  __shared__ float red_den[kMergeGroups];
+
+  const int64_t base = (int64_t)b * ns * hq + h;
+  float lv[kMergeChunk], ov[kMergeChunk];
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j) {
+    const int sp = grp + j * kMergeGroups;
+    const int64_t row = base + (int64_t)min(sp, ns - 1) * hq;
+    lv[j] = a.part_lse[row];
+    ov[j] = a.part_o[row * kHeadDim + d];
+    if (sp >= ns) lv[j] = -INFINITY;
   }
-  const int t = seq_len - 1;
-  const int lo = WINDOWED ? max(0, t - a.window + 1) : 0;
-  const int pages = t / kPage - lo / kPage + 1;
-  const int ns = (pages + a.pages_per_split - 1) / a.pages_per_split;
-  const int64_t base = (int64_t)b * a.num_splits * hq + h;
   const float sink = a.sinks[h] * kLog2e;
-  float M = sink;
-  bool nan = false;
-  for (int s = 0; s < ns; ++s) {
-    const float l = a.part_lse[base + (int64_t)s * hq];
+  float m = sink;
+  int nan = 0;
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j) {
+    nan |= lv[j] != lv[j];
+    m = fmaxf(m, lv[j]);
+  }
+  for (int sp = grp + kMergeChunk * kMergeGroups; sp < ns; sp += kMergeGroups) {
+    const float l = a.part_lse[base + (int64_t)sp * hq];
     nan |= l != l;
-    M = fmaxf(M, l);
+    m = fmaxf(m, l);
   }
-  float den = exp2_fast(sink - M), o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const int64_t row = base + (int64_t)s * hq;
-    const float wgt = exp2_fast(a.part_lse[row] - M);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  nan = __any(nan);
+  if ((tid & 63) == 0) {
+    red_m[tid >> 6] = m;
+    red_nan[tid >> 6] = nan;
+  }
+  __syncthreads();
+  float M = red_m[0];
+  nan = red_nan[0];
+#pragma unroll
+  for (int v = 1; v < kMergeThreads / 64; ++v) {
+    M = fmaxf(M, red_m[v]);
+    nan |= red_nan[v];
+  }
+
+  // an empty split (lse -inf, output never written) contributes 0
+  float o = 0.f, den = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMergeChunk; ++j) {
+    const bool live = lv[j] > -INFINITY;
+    const float wgt = live ? exp2_fast(lv[j] - M) : 0.f;
     den += wgt;
-    o += wgt * a.part_o[row * kHeadDim + d];
+    o += live ? wgt * ov[j] : 0.f;
   }
-  *dst = nan ? __builtin_nanf("") : o / den;
+#pragma unroll 8
+  for (int sp = grp + kMergeChunk * kMergeGroups; sp < ns; sp += kMergeGroups) {
+    const int64_t row = base + (int64_t)sp * hq;
+    const float l = a.part_lse[row];
+    const float x = a.part_o[row * kHeadDim + d];
+    const bool live = l > -INFINITY;
+    const float wgt = live ? exp2_fast(l - M) : 0.f;
+    den += wgt;
+    o += live ? wgt * x : 0.f;
+  }
+  red_o[grp][tid % kMergeDims] = o;
+  if (tid % kMergeDims == 0) red_den[grp] = den;
+  __syncthreads();
+  if (grp == 0) {
+    float os = 0.f, ds = exp2_fast(sink - M);
+#pragma unroll
+    for (int v = 0; v < kMergeGroups; ++v) {
+      os += red_o[v][tid];
+      ds += red_den[v];
+    }
+    a.out[((int64_t)b * hq + h) * kHeadDim + d] = nan ? __builtin_nanf("") : os / ds;
+  }
+}
+
+template <bool FUSED>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
+  const bool win = a.window > 0;
+  if (!a.multi_head && a.num_splits == 1 && a.pages_per_split <= kSinglePages) {
+    constexpr int W = kDecodeWavesSingle;
+    constexpr int P = (kSinglePages + W - 1) / W;
+    if (win)
+      hipLaunchKernelGGL((decode_split_kernel<W, P, true, true, FUSED>), grid, dim3(W * 64), 0, st,
+                         a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<W, P, true, false, FUSED>), grid, dim3(W * 64), 0,
+                         st, a);
+    return hipGetLastError();
+  }
+  if (a.multi_head) {
+    // long ranges: workgroups over all KV heads of their pages
+    const dim3 mh_grid(a.num_splits, a.num_kv_heads / kMhHeads, a.num_seqs);
+    const dim3 mh_block(kMhHeads * kMhStreams * 64);
+    if (a.num_splits == 1) {
+      if (win) hipLaunchKernelGGL((decode_mh_kernel<true, true, FUSED>), mh_grid, mh_block, 0, st, a);
+      else hipLaunchKernelGGL((decode_mh_kernel<true, false, FUSED>), mh_grid, mh_block, 0, st, a);
+      return hipGetLastError();
+    }
+    if (win) hipLaunchKernelGGL((decode_mh_kernel<false, true, FUSED>), mh_grid, mh_block, 0, st, a);
+    else hipLaunchKernelGGL((decode_mh_kernel<false, false, FUSED>), mh_grid, mh_block, 0, st, a);
+    const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
+    hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);
+    return hipGetLastError();
+  }
+  constexpr int W = kDecodeWaves;
+  if (a.num_splits == 1) {  // one long split: pipelined loop, sink folded in
+    if (win)
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED>), grid, dim3(W * 64), 0, st,
+                         a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED>), grid, dim3(W * 64), 0,
+                         st, a);
+    return hipGetLastError();
+  }
+  if (win)
+    hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED>), grid, dim3(W * 64), 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED>), grid, dim3(W * 64), 0, st,
+                       a);
+  const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
+  hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
-  const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
-  const bool win = a.window > 0;
-  if (a.num_splits == 1) {
-    if (win) hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, dim3(kThreads), 0, st, a);
-    return hipGetLastError();
-  }
-  const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs);
-  if (win) {
-    hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL((decode_merge_kernel<true>), mgrid, dim3(kHeadDim), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, dim3(kThreads), 0, st, a);
-    hipLaunchKernelGGL((decode_merge_kernel<false>), mgrid, dim3(kHeadDim), 0, st, a);
-  }
-  return hipGetLastError();
+  return a.q_in ? launch_decode_t<true>(a, st) : launch_decode_t<false>(a, st);
 }
 
 }  // namespace flint

@@ -45,4 +45,87 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
+// fp64 -> bf16 bits with one rounding: round to odd at fp32 precision (24
+// bits, enough guard bits for bf16's 8), then round to nearest even.
+__device__ __forceinline__ uint16_t bf16_bits_rne_f64(double x) {
+  if (x != x) return 0x7fc0u;
+  float f = (float)x;
+  const double back = (double)f;
+  if (back != x) {
+    uint32_t u = __float_as_uint(f);
+    if (fabs(back) > fabs(x)) u -= 1u;  // the nearest fp32 toward zero
+    f = __uint_as_float(u | 1u);
+  }
+  return bf16_bits_rne(f);
+}
+
+// Sum over the 64 lanes, result in every lane: DPP row_ror 8/4/2/1 leaves
+// each 16-lane row's total in all its lanes, then the four row totals are
+// read as scalars.  No LDS traffic (a shuffle-based version costs ~6 LDS
+// round trips on the critical path of the fused decode prologue).
+__device__ __forceinline__ double dpp_ror(double x, int k) {
+  const int lo = __builtin_bit_cast(int2, x).x, hi = __builtin_bit_cast(int2, x).y;
+  int2 r;
+  switch (k) {  // the DPP control must be a constant
+    case 8: r = int2{__builtin_amdgcn_update_dpp(0, lo, 0x128, 0xF, 0xF, false),
+                     __builtin_amdgcn_update_dpp(0, hi, 0x128, 0xF, 0xF, false)}; break;
+    case 4: r = int2{__builtin_amdgcn_update_dpp(0, lo, 0x124, 0xF, 0xF, false),
+                     __builtin_amdgcn_update_dpp(0, hi, 0x124, 0xF, 0xF, false)}; break;
+    case 2: r = int2{__builtin_amdgcn_update_dpp(0, lo, 0x122, 0xF, 0xF, false),
+                     __builtin_amdgcn_update_dpp(0, hi, 0x122, 0xF, 0xF, false)}; break;
+    default: r = int2{__builtin_amdgcn_update_dpp(0, lo, 0x121, 0xF, 0xF, false),
+                      __builtin_amdgcn_update_dpp(0, hi, 0x121, 0xF, 0xF, false)}; break;
+  }
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const int2 v = __builtin_bit_cast(int2, x);
+  return __builtin_bit_cast(double, int2{__builtin_amdgcn_readlane(v.x, lane),
+                                         __builtin_amdgcn_readlane(v.y, lane)});
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  x += dpp_ror(x, 8);
+  x += dpp_ror(x, 4);
+  x += dpp_ror(x, 2);
+  x += dpp_ror(x, 1);
+  return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+
+// cos/sin of pos * theta^(-2i/128), in fp64 with a two-part 2*pi reduction,
+// accurate to ~1e-16 for every position up to the 262,144-token context.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, float theta, double* c, double* s) {
+  const double inv_freq = exp2(-(2.0 * i / kHeadDim) * log2((double)theta));
+  const double ang = (double)pos * inv_freq;
+  const double two_pi_hi = 6.283185307179586;       // 2*pi rounded to fp64
+  const double two_pi_lo = 2.4492935982947064e-16;  // 2*pi - two_pi_hi
+  const double k = rint(ang * 0.15915494309189535);  // ang / (2*pi)
+  double r = fma(-k, two_pi_hi, ang);
+  r = fma(-k, two_pi_lo, r);
+  sincos(r, s, c);
+}
+
+// Per-head RMSNorm then (optionally) rotate-half RoPE of one 128-dim head,
+// one wave64: lane l holds dims l and l+64 (a RoPE pair) in x0, x1; on return
+// y0, y1 hold the result.  fp64 throughout; cs/sn are rope_cos_sin(pos, l).
+// Used by the stand-alone append and by the fused decode step, so both
+// produce bit-identical q, K and V.
+__device__ __forceinline__ void norm_rope_head(double x0, double x1, const float* w, float eps,
+                                               bool rope, double cs, double sn, int lane,
+                                               double* y0, double* y1) {
+  const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
+  const double r = 1.0 / sqrt(ss / kHeadDim + (double)eps);
+  double a0 = x0 * r * (double)w[lane];
+  double a1 = x1 * r * (double)w[lane + 64];
+  if (rope) {
+    const double r0 = a0 * cs - a1 * sn;
+    const double r1 = a1 * cs + a0 * sn;
+    a0 = r0;
+    a1 = r1;
+  }
+  *y0 = a0;
+  *y1 = a1;
+}
+
 }  // namespace flint

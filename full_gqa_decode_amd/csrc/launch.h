@@ -30,9 +30,9 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
 struct DecodeArgs {
-  const float* q;            // [B][Hq][128] fp32
-  const uint16_t* k_cache;   // [pages][Hkv][16][128]
-  const uint16_t* v_cache;   // [pages][Hkv][128][16]
+  const float* q;            // [B][Hq][128] fp32 (normalised; unfused path)
+  uint16_t* k_cache;         // [pages][Hkv][16][128] (written only by the fused path)
+  uint16_t* v_cache;         // [pages][Hkv][128][16]
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const float* sinks;        // [Hq]
@@ -47,7 +47,20 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t pages_per_split;
   int32_t num_splits;        // splits in the grid (per request)
+  int32_t multi_head;        // split workgroups cover four KV heads each
   float qscale;              // softmax_scale * log2(e)
+  // fused append of the new token (flint_attn_decode_step); q_in == nullptr
+  // selects the unfused path
+  const float* q_in;         // [B][Hq][128] raw
+  const float* k_in;         // [B][Hkv][128] raw
+  const float* v_in;         // [B][Hkv][128] raw
+  const float* q_w;
+  const float* k_w;
+  const int32_t* slots;      // [B]
+  float* q_out;              // optional [B][Hq][128]
+  int32_t use_rope;
+  float rope_theta;
+  float rms_eps;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
@@ -71,7 +84,17 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
-// Waves per decode workgroup (the split plan depends on it).
+// Waves per decode workgroup: kDecodeWaves when the key range is split (two
+// workgroups per CU), kDecodeWavesSingle when one workgroup covers a short
+// range by itself.  kSinglePages: ranges of at most this many pages use one
+// workgroup per (request, KV head), with every page load in flight at once
+// (kSinglePages / kDecodeWavesSingle pages of registers per wave) and no
+// merge launch.
 constexpr int kDecodeWaves = 8;
+constexpr int kDecodeWavesSingle = 8;
+constexpr int kSinglePages = 40;
+// kShortMinPages: least pages per split the plan gives a short range (the
+// 513-key window spreads over many CUs, then the merge kernel runs).
+constexpr int kShortMinPages = 2;
 
 }  // namespace flint

@@ -95,9 +95,10 @@ typedef struct {
  *   q_out_f32 [T][num_q_heads][128] (decode) or q_out_bf16 (prefill): exactly
  *     one is non-NULL; q_out_f32 may alias q_in.
  *   k_cache, v_cache: [num_blocks] pages in the layout above.
- * Per token and head: y = x / sqrt(mean(x^2) + eps) * w, computed in fp32;
- * then RoPE(y, position) when use_rope; K and V are rounded to bf16
- * (round-to-nearest-even) and written at the slot.  V is not normalised.
+ * Per token and head: y = x / sqrt(mean(x^2) + eps) * w, then RoPE(y,
+ * position) when use_rope, computed in fp64; q_out is y rounded once to fp32
+ * (or bf16), K is y rounded once to bf16 (round-to-nearest-even) and V is v
+ * rounded to bf16; K and V are written at the slot.  V is not normalised.
  * A slot >= num_blocks*16 or a negative position is not written and the
  * token's q_out row is set to NaN.
  */
@@ -125,8 +126,10 @@ flint_status flint_qk_norm_rope_append(const flint_attn_layer* L, int32_t num_to
  * Work is split over key ranges (split-K) and merged with log-sum-exp
  * weights; the sink joins in the merge.  A request whose seq_len is outside
  * [1, max_seq_len] or whose pages include an id outside [0, num_blocks) gets
- * NaN outputs.  workspace: >= flint_attn_decode_workspace_size(...) bytes,
- * 256-byte aligned, contents need not be initialised.
+ * NaN outputs.  workspace: >= flint_attn_decode_workspace_size(...) bytes
+ * (0 when one split covers the range), 256-byte aligned, owned by the caller;
+ * its contents need not be initialised.  Calls that share a workspace must
+ * not run concurrently.
  */
 size_t flint_attn_decode_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                         int32_t max_seq_len);
@@ -149,6 +152,34 @@ flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, c
                                   int32_t max_seq_len, const float* sinks, float* out,
                                   void* workspace, size_t workspace_bytes,
                                   int32_t pages_per_split, void* stream);
+
+/*
+ * One decode step of one layer in a single launch: the fused per-head
+ * RMSNorm / RoPE / append of each request's new token followed by decode
+ * attention ("What happened": fused normalisation, rotary-position and cache
+ * operations).  Same results, bit for bit, as
+ *   flint_qk_norm_rope_append(L, B, q_in, k_in, v_in, q_norm_w, k_norm_w,
+ *                             positions = seq_lens - 1, slot_mapping, q_out, ...)
+ * followed by flint_attn_decode on that q_out, without the intermediate q
+ * round trip or a second launch.
+ *   q_in [B][num_q_heads][128], k_in, v_in [B][num_kv_heads][128] fp32 raw
+ *   slot_mapping [B]: must equal the slot the page table gives position
+ *     seq_lens[b]-1 (page * 16 + row); otherwise nothing is written and that
+ *     request's output is NaN
+ *   q_out: optional [B][num_q_heads][128] fp32 normalised (rotated) q, or NULL
+ *   pages_per_split: as for flint_attn_decode_ex (0 = the library's choice);
+ *     size the workspace with flint_attn_decode_workspace_size_ex.
+ */
+flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
+                                    const float* q_in, const float* k_in, const float* v_in,
+                                    const float* q_norm_w, const float* k_norm_w,
+                                    const int32_t* slot_mapping, float* q_out,
+                                    uint16_t* k_cache, uint16_t* v_cache, int32_t num_blocks,
+                                    const int32_t* block_tables, int32_t bt_stride,
+                                    const int32_t* seq_lens, int32_t max_seq_len,
+                                    const float* sinks, float* out, void* workspace,
+                                    size_t workspace_bytes, int32_t pages_per_split,
+                                    void* stream);
 
 /* The split plan flint_attn_decode_ex would use (host only, no HIP call):
  * writes the pages per split and the number of splits per request. */

@@ -129,6 +129,37 @@ class DecodeCase:
         return out, qd, kd, vd
 
 
+    def run_gpu_fused(self, pages_per_split=0, slot_delta=None):
+        """append every token except each request's new one, then the fused
+        step (append of the new token + decode in one launch)."""
+        import torch
+        import full_gqa_decode_amd as fl
+        kd = torch.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
+                        device=dev())
+        vd = torch.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
+                        device=dev())
+        keep = np.ones(self.T, bool)
+        keep[self.last_row] = False
+        pre = np.nonzero(keep)[0]
+        if len(pre):
+            qs = torch.empty((len(pre), 32, 128), dtype=torch.float32, device=dev())
+            fl.flint_qk_norm_rope_append(self.FL, up(self.q_in[pre]), up(self.k_in[pre]),
+                                         up(self.v_in[pre]), up(self.qw), up(self.kw),
+                                         up(self.pos[pre]), up(self.slots[pre]), qs, kd, vd)
+        r = self.last_row
+        slots = self.slots[r].copy()
+        if slot_delta is not None:
+            slots = slots + np.asarray(slot_delta, np.int32)
+        out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        qo = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        fl.flint_attn_decode_step(self.FL, up(self.q_in[r]), up(self.k_in[r]), up(self.v_in[r]),
+                                  up(self.qw), up(self.kw), up(slots), kd, vd, up(self.bt),
+                                  up(self.seq_lens), max(self.ctxs), up(self.sinks), out,
+                                  q_out=qo, pages_per_split=pages_per_split)
+        torch.cuda.synchronize()
+        return out, qo, kd, vd
+
+
 class CacheDecodeCase:
     """Decode only: the bf16 cache and the fp32 q are drawn directly (no
     append), so K2/K3 are tested on their own."""

@@ -119,3 +119,47 @@ def test_ragged_64_requests_config3_scaled():
     for window in (0, 513):
         case = CacheDecodeCase(7, lens, window=window)
         assert max_err(case.run_gpu(), case.expected()) <= TOL
+
+
+@pytest.mark.parametrize("window,ring,ctxs,pps", [
+    (0, False, [4096], 0),
+    (0, False, [1, 17, 1000, 5000], 0),
+    (0, False, [3000, 16], 2),
+    (0, False, [700], 1000),
+    (513, True, [32768], 0),
+    (513, True, [1, 513, 514, 2000], 0),
+    (513, False, [2000, 33], 3),
+])
+def test_fused_step_bitwise_equals_append_then_decode(window, ring, ctxs, pps):
+    case = DecodeCase(9, ctxs, window=window, ring=ring, weights_one=False)
+    out_ref, qd, kd_ref, vd_ref = case.run_gpu(pages_per_split=pps)
+    out, qo, kd, vd = case.run_gpu_fused(pages_per_split=pps)
+    assert np.array_equal(out.cpu().numpy(), out_ref.cpu().numpy())
+    assert np.array_equal(down16(kd), down16(kd_ref))
+    assert np.array_equal(down16(vd), down16(vd_ref))
+    assert np.array_equal(qo.cpu().numpy(), qd.cpu().numpy()[case.last_row])
+    ref, _, _, _ = case.expected()
+    assert max_err(out.cpu().numpy(), ref) <= TOL
+
+
+def test_fused_step_rejects_a_slot_the_page_table_disagrees_with():
+    case = DecodeCase(10, [300, 400, 500], window=0)
+    ref, _, _, _ = case.expected()
+    out, _, kd, vd = case.run_gpu_fused(slot_delta=[0, 1, 0])
+    got = out.cpu().numpy()
+    assert np.all(np.isnan(got[1]))
+    assert max_err(got[[0, 2]], ref[[0, 2]]) <= TOL
+    # nothing was written for request 1: its new token's row is still the sentinel
+    s = int(case.slots[case.last_row[1]])
+    assert np.all(down16(kd)[s // 16, :, s % 16, :] == 0x7FC1)
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_every_request_shorter_than_the_host_bound(window):
+    # the kernels start loading for a request of length max_seq_len before
+    # seq_lens arrive; here every guess is wrong and must be redone
+    case = CacheDecodeCase(11, [3000, 17, 640, 1], window=window)
+    ref = case.expected()
+    for pps in (0, 1, 3):
+        got = case.run_gpu(pages_per_split=pps, max_seq_len=case.bt_stride * 16)
+        assert max_err(got, ref) <= TOL

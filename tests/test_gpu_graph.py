@@ -13,7 +13,7 @@ def test_graph_replays_match_eager():
     case = CacheDecodeCase(8, [5000], window=0)
     q, kc, vc = up(case.q), up(case.kc), up(case.vc)
     bt, sl, sk = up(case.bt), up(case.seq_lens), up(case.sinks)
-    ws = torch.empty(fl.flint_attn_decode_workspace_size(case.FL, 1, 5000), dtype=torch.uint8,
+    ws = torch.zeros(fl.flint_attn_decode_workspace_size(case.FL, 1, 5000), dtype=torch.uint8,
                      device=dev())
     eager = torch.empty((1, 32, 128), dtype=torch.float32, device=dev())
     fl.flint_attn_decode(case.FL, q, kc, vc, bt, sl, 5000, sk, eager, workspace=ws)
