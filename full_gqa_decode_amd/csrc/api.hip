@@ -43,6 +43,9 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // grid for MI355X's 256 compute units at one long-running workgroup each.
 constexpr int kMaxContext = 1 << 24;
 constexpr int kTargetWorkgroups = 256;
+// Longest split of a batch plan (a ragged batch of 64 requests up to 131072
+// tokens streams at ~5.6 TB/s with 192-page splits, ~4 TB/s with whole requests).
+constexpr int kMaxSplitPages = 192;
 constexpr size_t kWsAlign = 256;
 
 flint_status check_layer(const flint_attn_layer* L) {
@@ -77,32 +80,28 @@ int64_t max_key_pages(const flint_attn_layer* L, int32_t max_seq_len) {
 struct Plan {
   int32_t pages_per_split;
   int32_t num_splits;
-  int32_t multi_head;  // workgroups cover four KV heads (long ranges)
 };
 
+// About kTargetWorkgroups workgroups of (split, KV head, request): a short
+// range (the 513-key window) becomes small splits so its bytes spread over many
+// CUs; a long one at batch 1 is cut into one split per CU; a batch of long
+// requests keeps splits of at most kMaxSplitPages pages, so that its longest
+// requests are spread too.
 Plan make_plan(const flint_attn_layer* L, int32_t num_seqs, int32_t max_seq_len, int32_t pps) {
   const int64_t pages = max_key_pages(L, max_seq_len);
-  // Long ranges with num_kv_heads a multiple of 4 run workgroups that cover
-  // four KV heads each, so a page's head tiles are read together.
-  const bool mh = pages > flint::kSinglePages && L->num_kv_heads % 4 == 0;
   int64_t p = pps;
   if (p <= 0) {
-    // about kTargetWorkgroups workgroups; a short range (the 513-key window)
-    // becomes small splits so its bytes spread over many CUs, a long one keeps
-    // at least two pages per wave
-    const int64_t units =
-        (int64_t)(num_seqs > 0 ? num_seqs : 1) * (mh ? L->num_kv_heads / 4 : L->num_kv_heads);
+    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * L->num_kv_heads;
     const int64_t splits = (kTargetWorkgroups + units - 1) / units;
     p = (pages + splits - 1) / splits;
-    const int64_t min_pages = mh ? 4 : flint::kShortMinPages;
-    if (p < min_pages) p = min_pages;
+    if (p > kMaxSplitPages) p = kMaxSplitPages;
+    if (p < flint::kShortMinPages) p = flint::kShortMinPages;
   }
   if (p > pages) p = pages;
   if (p < 1) p = 1;
   Plan pl;
   pl.pages_per_split = (int32_t)p;
   pl.num_splits = (int32_t)((pages + p - 1) / p);
-  pl.multi_head = mh;
   return pl;
 }
 
@@ -283,7 +282,6 @@ flint_status prepare_decode(const flint_attn_layer* L, int32_t num_seqs, const u
   a->max_seq_len = max_seq_len;
   a->pages_per_split = pl.pages_per_split;
   a->num_splits = pl.num_splits;
-  a->multi_head = pl.multi_head;
   a->qscale = L->softmax_scale * 1.4426950408889634f;
   a->use_rope = L->use_rope;
   a->rope_theta = L->rope_theta;

@@ -47,7 +47,6 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t pages_per_split;
   int32_t num_splits;        // splits in the grid (per request)
-  int32_t multi_head;        // split workgroups cover four KV heads each
   float qscale;              // softmax_scale * log2(e)
   // fused append of the new token (flint_attn_decode_step); q_in == nullptr
   // selects the unfused path
