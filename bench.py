@@ -40,6 +40,34 @@ HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_TFLOPS = 2500.0
 SEED = 0
 KV_BYTES_PER_TOKEN_LAYER = 2 * HKV * D * 2   # K and V rows of one token, one layer
+COPY_PROBE_BYTES = 256 << 20
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_full_layer_ctx100k_hbm_counters.md")
+DECODE_SOURCES = ["decode.hip", "device.h", "launch.h", "api.hip"]
+
+
+def measured_traffic():
+    """HBM bytes per full-layer launch pair from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary, or None once the decode sources differ from
+    the ones those counters were taken on."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            vals[k] = v.strip()
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "full_gqa_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch"])
 
 
 def log(msg):
@@ -86,6 +114,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy three times (the "
+                         "known-size kernel that calibrates HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode path here is single-GPU (--gpus {args.gpus} "
@@ -93,6 +124,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        copy_probe(torch.device("cuda:0"))
+        return
     import full_gqa_decode_amd as fl
     fl.lib()
     dev = torch.device("cuda:0")
@@ -240,10 +274,12 @@ def main():
         "us_per_step_p10": round(float(np.percentile(per, 10)), 2),
         "us_per_step_p90": round(float(np.percentile(per, 90)), 2),
         "us_per_step_unfused": round(us_unfused, 2),
-        "roofline": {"kernel": "full-layer fused decode step (split-K + merge), 100,000 keys",
+        "roofline": {"kernel": "full-layer decode, 100,000 keys: the split-K kernel (fused "
+                               "norm/RoPE/append) and its LSE-merge kernel, the launch pair of "
+                               "one flint_attn_decode_step call",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "us_per_launch": round(us_full, 2),
+                     "traffic": measured_traffic(), "us_per_launch": round(us_full, 2),
                      "bytes_per_launch": kv_full + extra_full,
                      "pages_per_split": pps, "splits": nsplit},
         "context": "pages' end-to-end figure (model forward + LM head + sampling, 1x GB200, "
@@ -256,6 +292,20 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_max_abs_err"] = cpu_baseline(layers, eps)
     print(json.dumps(result), flush=True)
+
+
+def copy_probe(dev):
+    """A plain copy of COPY_PROBE_BYTES (read once, written once), three times:
+    its FETCH_SIZE and WRITE_SIZE per dispatch, against the known byte count,
+    give the scale factor of those counters."""
+    import torch
+    n = COPY_PROBE_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"bench: copy probe {COPY_PROBE_BYTES} bytes x 3 done")
 
 
 def bench_prefill(fl, dev, stream):
