@@ -1,0 +1,154 @@
+"""Parity at the full workload sizes, in the launch configuration the bench
+times: one flint_attn_decode_step call per layer (norm/RoPE/append of the new
+token fused into split-K decode, then the merge) with the default plan.
+
+Workloads: batch 1 at a 100,000-token context on a full layer (6,250 shuffled
+pages) and on a sliding layer (33-page ring); and 64 requests with context
+lengths uniform in [1024, 131072] on a full layer (8.4 GB of KV, the oracle
+checking a sample of 8 requests on all 32 heads, every request checked for its
+cache write) and on a sliding layer (every request checked).
+
+The resident cache pages are N(0,1) bf16 drawn on the GPU by a seeded torch
+generator and copied to the host for the oracle; the new tokens' q/k/v come
+from synth on the host.  Nothing computed by the GPU feeds the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from flint_cases import TOL, dev, layers, up
+
+pytestmark = pytest.mark.gpu
+
+PAGE = 16
+
+
+class BigStep:
+    def __init__(self, tag, ctxs, window, full_table):
+        import torch
+        self.ctxs = np.asarray(ctxs, np.int32)
+        B = len(ctxs)
+        self.B = B
+        self.L, self.FL = layers(window)
+        logical = -(-int(self.ctxs.max()) // PAGE)
+        self.bt_stride = logical
+        if full_table:
+            self.bt, nb = synth.shuffled_block_table(0, tag + (synth.PERM,), B,
+                                                     [-(-int(c) // PAGE) for c in ctxs], logical)
+        else:
+            self.bt, nb = synth.ring_block_table(0, tag + (synth.PERM,), B, logical, 33, logical)
+        self.nb = nb
+        self.kd = synth.normal_bf16_bits_torch(0, tag + (synth.KC,), oracle.k_cache_shape(nb), dev())
+        self.vd = synth.normal_bf16_bits_torch(0, tag + (synth.VC,), oracle.v_cache_shape(nb), dev())
+        torch.cuda.synchronize()
+        # pristine host copies for the oracle (taken before the step appends)
+        self.kc = self.kd.cpu().numpy().view(np.uint16)
+        self.vc = self.vd.cpu().numpy().view(np.uint16)
+        self.q_in = synth.normal(0, tag + (synth.Q,), (B, 32, 128))
+        self.k_in = synth.normal(0, tag + (synth.K,), (B, 4, 128))
+        self.v_in = synth.normal(0, tag + (synth.V,), (B, 4, 128))
+        self.sinks = synth.normal(0, tag + (synth.SINK,), 32)
+        self.qw = np.ones(128, np.float32)
+        self.kw = np.ones(128, np.float32)
+        t = self.ctxs - 1
+        self.pos = t.astype(np.int32)
+        self.slots = np.array([oracle.slot(self.bt, b, int(t[b])) for b in range(B)], np.int32)
+
+    def run_gpu(self):
+        import torch
+        import full_gqa_decode_amd as fl
+        out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        fl.flint_attn_decode_step(self.FL, up(self.q_in), up(self.k_in), up(self.v_in),
+                                  up(self.qw), up(self.kw), up(self.slots), self.kd, self.vd,
+                                  up(self.bt), up(self.ctxs), int(self.ctxs.max()),
+                                  up(self.sinks), out)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def oracle_step(self, sel):
+        """Append every request's new token to the host caches (in place),
+        then attention for the requests in `sel`."""
+        q = oracle.append(self.L, self.q_in, self.k_in, self.v_in, self.qw, self.kw, self.pos,
+                          self.slots, self.kc, self.vc)
+        return oracle.attn_decode(self.L, q[sel], self.kc, self.vc, self.bt[sel], self.ctxs[sel],
+                                  self.sinks)
+
+    def check_written_rows(self):
+        """The new tokens' cache rows: V bit-exact, K within one bf16 ulp of
+        the oracle's correctly rounded value (ties of the fp64 value aside)."""
+        k_gpu = self.kd.cpu().numpy().view(np.uint16) if self.nb * 4 * 16 * 128 < (1 << 28) else None
+        for b in range(self.B):
+            page, row = divmod(int(self.slots[b]), PAGE)
+            v_ref = self.vc.reshape(self.nb, 4, 128, PAGE)[page, :, :, row]
+            v_got = self.vd.view(self.nb, 4, 128, PAGE)[page, :, :, row].cpu().numpy().view(np.uint16)
+            assert np.array_equal(v_got, v_ref), f"V row of request {b}"
+            k_ref = self.kc.reshape(self.nb, 4, PAGE, 128)[page, :, row, :]
+            if k_gpu is not None:
+                k_got = k_gpu.reshape(self.nb, 4, PAGE, 128)[page, :, row, :]
+            else:
+                k_got = self.kd.view(self.nb, 4, PAGE, 128)[page, :, row, :].cpu().numpy().view(np.uint16)
+            diff = np.abs(k_got.astype(np.int32) - k_ref.astype(np.int32))
+            assert diff.max() <= 1, f"K row of request {b}"
+        return k_gpu
+
+
+def test_bs1_100k_full_layer_step():
+    import full_gqa_decode_amd as fl
+    case = BigStep((11, 1), [100_000], window=0, full_table=True)
+    assert fl.flint_attn_decode_plan(case.FL, 1, 100_000) == (98, 64)
+    got = case.run_gpu()
+    ref = case.oracle_step(np.arange(1))
+    err = float(np.abs(got - ref).max())
+    print(f"bs1 100K full layer: max err {err:.3e}", flush=True)
+    assert err <= TOL
+    k_gpu = case.check_written_rows()
+    # nothing but the new token's row changed anywhere in the 204.8 MB cache
+    assert k_gpu is not None
+    slot = int(case.slots[0])
+    kr = k_gpu.reshape(case.nb, 4, PAGE, 128).copy()
+    kh = case.kc.reshape(case.nb, 4, PAGE, 128)
+    kr[slot // PAGE, :, slot % PAGE, :] = kh[slot // PAGE, :, slot % PAGE, :]
+    assert np.array_equal(kr, kh)
+    assert np.array_equal(case.vd.cpu().numpy().view(np.uint16), case.vc)
+
+
+def test_bs1_100k_sliding_layer_step():
+    import full_gqa_decode_amd as fl
+    case = BigStep((11, 2), [100_000], window=513, full_table=False)
+    assert fl.flint_attn_decode_plan(case.FL, 1, 100_000) == (2, 17)
+    got = case.run_gpu()
+    ref = case.oracle_step(np.arange(1))
+    err = float(np.abs(got - ref).max())
+    print(f"bs1 100K sliding layer: max err {err:.3e}", flush=True)
+    assert err <= TOL
+    case.check_written_rows()
+
+
+def ragged_lengths():
+    return synth.uniform_ints(0, (11, 3), 64, 1024, 131072)
+
+
+def test_ragged_64_requests_full_layer_full_size():
+    lens = ragged_lengths()
+    case = BigStep((11, 4), lens, window=0, full_table=True)
+    got = case.run_gpu()
+    assert np.isfinite(got).all()
+    order = synth.permutation(0, (11, 5), 64)
+    sel = np.unique(np.concatenate([[int(np.argmin(lens)), int(np.argmax(lens))], order[:6]]))
+    ref = case.oracle_step(sel)
+    err = float(np.abs(got[sel] - ref).max())
+    print(f"64 ragged requests, full layer, {int(lens.sum())} keys: sampled {[int(s) for s in sel]} "
+          f"max err {err:.3e}", flush=True)
+    assert err <= TOL
+    case.check_written_rows()
+
+
+def test_ragged_64_requests_sliding_layer_full_size():
+    lens = ragged_lengths()
+    case = BigStep((11, 6), lens, window=513, full_table=False)
+    got = case.run_gpu()
+    ref = case.oracle_step(np.arange(64))
+    err = float(np.abs(got - ref).max())
+    print(f"64 ragged requests, sliding layer: max err {err:.3e}", flush=True)
+    assert err <= TOL
+    case.check_written_rows()
