@@ -8,18 +8,23 @@
 //
 // Design.  A query vector is one (row, head) pair; the eight heads of a KV
 // group share every key, so a 16-wide MFMA tile holds 2 rows x 8 heads.  A
-// wave owns kTiles such tiles (kTiles*2 consecutive rows); a workgroup of
-// four waves owns kRows rows of one KV group, and its waves walk the same
-// key pages in step so the K/V lines fetched by one wave are L1/L2 hits for
-// the others.  Per pair of 16-key pages:
-//   S^T[32 keys x 16 qv] = K . Q^T     2 x 4 v_mfma_f32_16x16x32_bf16 per tile
-//   O[16 qv x 128]      += P . V        8 x 2 v_mfma_f32_16x16x32_bf16 per tile
+// wave owns kTiles such tiles (kWaveRows consecutive rows); a workgroup of
+// kPWaves waves owns kRows rows of one KV group.  The workgroup walks the key
+// pages of its rows in pairs (32 keys): every thread fetches 16 bytes of K and
+// 16 bytes of V of the next pair while the waves compute on the current one,
+// and the pair is staged once in LDS (double-buffered, one barrier per pair)
+// for all waves -- HBM/L2 traffic per flop falls by the number of waves.
+// Per pair and tile:
+//   S^T[32 keys x 16 qv] = K . Q^T     2 x 4 v_mfma_f32_16x16x32_bf16
+//   O[16 qv x 128]      += P . V        8 x 2 v_mfma_f32_16x16x32_bf16
 // The PV contraction runs over 32 keys: MFMA k index gq*8+j takes key gq*4+j
 // of the first page for j < 4 and key gq*4+j-4 of the second page for j >= 4,
-// which is exactly where the score MFMAs left P, and exactly 2 x 8 contiguous
-// bytes of each dim-major V page row.  P is split into bf16(p) and its bf16
-// remainder (two MFMAs) so the value product is fp32-accurate.  Online
-// softmax in log2 units; the sink joins the denominator in the epilogue.
+// which is exactly where the score MFMAs left P; the LDS copy of V interleaves
+// the two pages per dim row so that this operand is one 16-byte LDS read.  P
+// is split into bf16(p) and its bf16 remainder (two MFMAs) so the value
+// product is fp32-accurate.  Online softmax in log2 units with a lazy
+// reference max (moved only when a score exceeds it by 2^8), the sink joining
+// the denominator in the epilogue.
 // Bound: the matrix cores for full layers (4*D flops per (query, key) pair).
 #include "device.h"
 #include "launch.h"
@@ -28,55 +33,91 @@ namespace flint {
 
 namespace {
 
-constexpr int kTiles = 2;               // 16-vector MFMA tiles per wave
-constexpr int kWaveRows = kTiles * 2;   // query rows per wave
-constexpr int kPWaves = 4;
-constexpr int kRows = kWaveRows * kPWaves;  // query rows per workgroup
+constexpr int kTiles = 2;                    // 16-vector MFMA tiles per wave
+constexpr int kWaveRows = kTiles * 2;        // query rows per wave
+constexpr int kPWaves = 8;                   // waves per workgroup
+constexpr int kPThreads = kPWaves * 64;
+constexpr int kRows = kWaveRows * kPWaves;   // query rows per workgroup
+// LDS copy of one page pair.  K: 32 key rows of 256 bytes, padded to 272 so
+// that the 16 rows one MFMA operand read touches fall in distinct banks.  V:
+// 128 dim rows of 64 bytes (keys 4k..4k+3 of page a, then of page b, k = 0..3),
+// padded to 80 bytes for the same reason.
+constexpr int kKStride = kHeadDim * 2 + 16;
+constexpr int kVStride = 2 * kPage * 2 + 16;
+constexpr int kKBytes = 2 * kPage * kKStride;
+constexpr int kBufBytes = kKBytes + kHeadDim * kVStride;
+static_assert(kPThreads == 2 * 256, "staging: one K and one V 16-byte chunk per thread");
 
 struct PairRegs {
   bf16x8 ka[4], kb[4];  // K of the two pages (MFMA A operand)
   u32x4 v[8];           // V: keys gq*4..+3 of page a and of page b, one dim
 };
 
-__device__ __forceinline__ void load_pair(const PrefillArgs& a, int pga, int pgb, bool has_b,
-                                          int g, int n, int gq, PairRegs& r) {
-  const int hkv = a.num_kv_heads;
-  const uint16_t* ka = a.k_cache + (((int64_t)pga * hkv + g) * kPage + n) * kHeadDim + gq * 8;
-  const uint16_t* kb = a.k_cache + (((int64_t)pgb * hkv + g) * kPage + n) * kHeadDim + gq * 8;
+// This thread's 16-byte K and V chunks of the pair (pga, pgb).
+__device__ __forceinline__ void fetch_pair(const PrefillArgs& a, int pga, int pgb, int g, int tid,
+                                           u32x4& kr, u32x4& vr) {
+  const int sel = tid >> 8, c = tid & 255;
+  const int64_t pg = sel ? pgb : pga;
+  const int64_t tile = (pg * a.num_kv_heads + g) * (kPage * kHeadDim);
+  kr = *(const u32x4*)(a.k_cache + tile + (c >> 4) * kHeadDim + (c & 15) * 8);
+  vr = *(const u32x4*)(a.v_cache + tile + (c >> 1) * kPage + (c & 1) * 8);
+}
+
+__device__ __forceinline__ void stage_pair(unsigned char* buf, int tid, const u32x4& kr,
+                                           const u32x4& vr) {
+  const int sel = tid >> 8, c = tid & 255;
+  *(u32x4*)(buf + (sel * kPage + (c >> 4)) * kKStride + (c & 15) * 16) = kr;
+  // V chunk: dim c>>1, keys h*8..h*8+7 = key groups 2h and 2h+1 of page sel
+  unsigned char* vrow = buf + kKBytes + (c >> 1) * kVStride + sel * 8;
+  const int h = c & 1;
+  *(u32x2*)(vrow + (2 * h) * 16) = u32x2{vr[0], vr[1]};
+  *(u32x2*)(vrow + (2 * h + 1) * 16) = u32x2{vr[2], vr[3]};
+}
+
+__device__ __forceinline__ void read_pair(const unsigned char* buf, int n, int gq, PairRegs& r) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    r.ka[c] = *(const bf16x8*)(ka + c * 32);
-    r.kb[c] = has_b ? *(const bf16x8*)(kb + c * 32) : bf16x8{};
+    r.ka[c] = *(const bf16x8*)(buf + n * kKStride + c * 64 + gq * 16);
+    r.kb[c] = *(const bf16x8*)(buf + (kPage + n) * kKStride + c * 64 + gq * 16);
   }
-  const uint16_t* va = a.v_cache + (((int64_t)pga * hkv + g) * kHeadDim + n) * kPage + gq * 4;
-  const uint16_t* vb = a.v_cache + (((int64_t)pgb * hkv + g) * kHeadDim + n) * kPage + gq * 4;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const u32x2 x = *(const u32x2*)(va + nb * 16 * kPage);
-    const u32x2 y = has_b ? *(const u32x2*)(vb + nb * 16 * kPage) : u32x2{0u, 0u};
-    r.v[nb] = u32x4{x[0], x[1], y[0], y[1]};
-  }
+  for (int nb = 0; nb < 8; ++nb)
+    r.v[nb] = *(const u32x4*)(buf + kKBytes + (nb * 16 + n) * kVStride + gq * 16);
 }
 
 template <bool WINDOWED>
-__global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char sm[2][kBufBytes];
   const int ntile = gridDim.x;
   const int tile = ntile - 1 - blockIdx.x;  // longest key ranges first
   const int g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, gq = lane >> 4;
   const int hkv = a.num_kv_heads, hq = hkv * kGroup;
 
   const int q0 = a.cu_q_lens[b];
   const int q_len = a.cu_q_lens[b + 1] - q0;
   const int seq_len = a.seq_lens[b];
-  const int row0 = tile * kRows + w * kWaveRows;  // first row of this wave
-  if (q_len <= 0 || row0 >= q_len) return;         // no rows here
+  const int wg_row0 = tile * kRows;
+  if (q_len <= 0 || wg_row0 >= q_len) return;  // no rows in this workgroup
   const bool req_bad = q_len > a.max_q_len || seq_len > a.max_seq_len || q_len > seq_len;
-  const int rows_here = min(kWaveRows, q_len - row0);
-  const int pos0 = seq_len - q_len + row0;           // position of the wave's first row
+  const int base = seq_len - q_len;  // position of row 0
+
+  // this wave's rows (possibly none: it still stages pages and meets barriers)
+  const int row0 = wg_row0 + w * kWaveRows;
+  const bool active = row0 < q_len;
+  const int rows_here = active ? min(kWaveRows, q_len - row0) : 1;
+  const int pos0 = base + row0;
   const int pos_last = pos0 + rows_here - 1;
+  const int lo_first = WINDOWED ? max(0, pos0 - a.window + 1) : 0;
+  const int lo_last = WINDOWED ? max(0, pos_last - a.window + 1) : 0;
+
+  // the workgroup's page range: the union of its rows' key ranges
+  const int wg_pos_last = base + min(wg_row0 + kRows, q_len) - 1;
+  const int wg_lo = WINDOWED ? max(0, base + wg_row0 - a.window + 1) : 0;
+  const int p_first = wg_lo / kPage, p_last = wg_pos_last / kPage;
+  const int npairs = req_bad ? 0 : (p_last - p_first) / 2 + 1;
 
   // Q operands: tile mt, column n -> row row0 + 2*mt + (n>>3), head g*8 + (n&7)
   bf16x8 qop[kTiles][4];
@@ -84,15 +125,12 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int mt = 0; mt < kTiles; ++mt) {
     const int r = min(row0 + 2 * mt + (n >> 3), q_len - 1);
-    qpos[mt] = seq_len - q_len + row0 + 2 * mt + (n >> 3);
+    qpos[mt] = base + row0 + 2 * mt + (n >> 3);
     const uint16_t* qp = a.q + (((int64_t)(q0 + r) * hq) + g * kGroup + (n & 7)) * kHeadDim + gq * 8;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qop[mt][c] = req_bad ? bf16x8{} : *(const bf16x8*)(qp + c * 32);
+    for (int c = 0; c < 4; ++c)
+      qop[mt][c] = (req_bad || !active) ? bf16x8{} : *(const bf16x8*)(qp + c * 32);
   }
-
-  const int lo_first = WINDOWED ? max(0, pos0 - a.window + 1) : 0;
-  const int lo_last = WINDOWED ? max(0, pos_last - a.window + 1) : 0;
-  const int p_first = lo_first / kPage, p_last = pos_last / kPage;
 
   f32x4 acc[kTiles][8];
   float m_run[kTiles], l_part[kTiles];
@@ -105,98 +143,128 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
   }
   int bad = req_bad;
 
-  for (int p = req_bad ? p_last + 1 : p_first; p <= p_last; p += 2) {
-    const bool has_b = p + 1 <= p_last;
-    int pga = a.block_tables[(int64_t)b * a.bt_stride + p];
-    int pgb = has_b ? a.block_tables[(int64_t)b * a.bt_stride + p + 1] : pga;
+  // physical pages of pair p (page b = page a past the range end); an id
+  // outside [0, num_blocks) marks the request bad and reads page 0 instead
+  auto pair_ids = [&](int p, int& pga, int& pgb) {
+    pga = a.block_tables[(int64_t)b * a.bt_stride + p];
+    pgb = p + 1 <= p_last ? a.block_tables[(int64_t)b * a.bt_stride + p + 1] : pga;
     if (pga < 0 || pga >= a.num_blocks) { bad = 1; pga = 0; }
     if (pgb < 0 || pgb >= a.num_blocks) { bad = 1; pgb = 0; }
-    PairRegs pr;
-    load_pair(a, pga, pgb, has_b, g, n, gq, pr);
+  };
 
-    // keys of this pair that some row of the wave may not see
-    const int key_lo = p * kPage, key_hi = p * kPage + 2 * kPage - 1;
-    const bool edge = key_lo < lo_last || key_hi > pos0 || !has_b;
-    if (edge) {  // zero V of keys no row of the wave may see (unwritten slots)
-      uint32_t keep[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = p * kPage + (j >= 4 ? kPage : 0) + gq * 4 + (j & 3);
-        const bool ok = key >= lo_first && key <= pos_last && (j < 4 || has_b);
-        keep[j] = ok ? 0xffffu : 0u;
-      }
-      const u32x4 mk = {keep[0] | (keep[1] << 16), keep[2] | (keep[3] << 16),
-                        keep[4] | (keep[5] << 16), keep[6] | (keep[7] << 16)};
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) pr.v[nb] &= mk;
+  u32x4 kr, vr;
+  if (npairs > 0) {
+    int pga, pgb;
+    pair_ids(p_first, pga, pgb);
+    fetch_pair(a, pga, pgb, g, tid, kr, vr);
+    stage_pair(sm[0], tid, kr, vr);
+  }
+  __syncthreads();
+
+  for (int i = 0; i < npairs; ++i) {
+    const int p = p_first + 2 * i;
+    const bool more = i + 1 < npairs;
+    if (more) {  // the next pair's loads fly during this pair's math
+      int pga, pgb;
+      pair_ids(p + 2, pga, pgb);
+      fetch_pair(a, pga, pgb, g, tid, kr, vr);
     }
-
-#pragma unroll
-    for (int mt = 0; mt < kTiles; ++mt) {
-      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr.ka[c], qop[mt][c], sa, 0, 0, 0);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr.kb[c], qop[mt][c], sb, 0, 0, 0);
-      }
-      float sv[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sv[i] = sa[i] * a.qscale;
-        sv[4 + i] = sb[i] * a.qscale;
-      }
-      if (edge) {
-        const int qp = min(qpos[mt], pos_last);  // rows past the chunk end: any finite cut
-        const int qlo = WINDOWED ? qp - a.window + 1 : 0;
+    const bool has_b = p + 1 <= p_last;
+    const int key_lo = p * kPage, key_hi = p * kPage + 2 * kPage - 1;
+    if (active && key_hi >= lo_first && key_lo <= pos_last) {
+      PairRegs pr;
+      read_pair(sm[i & 1], n, gq, pr);
+      // keys of this pair that some row of the wave may not see
+      const bool edge = key_lo < lo_last || key_hi > pos0 || !has_b;
+      if (edge) {  // zero V of keys no row of the wave may see (unwritten slots)
+        uint32_t keep[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = p * kPage + (j >= 4 ? kPage : 0) + gq * 4 + (j & 3);
-          if (key < qlo || key > qp || (j >= 4 && !has_b)) sv[j] = -INFINITY;
+          const bool ok = key >= lo_first && key <= pos_last && (j < 4 || has_b);
+          keep[j] = ok ? 0xffffu : 0u;
+        }
+        const u32x4 mk = {keep[0] | (keep[1] << 16), keep[2] | (keep[3] << 16),
+                          keep[4] | (keep[5] << 16), keep[6] | (keep[7] << 16)};
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) pr.v[nb] &= mk;
+      }
+
+#pragma unroll
+      for (int mt = 0; mt < kTiles; ++mt) {
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr.ka[c], qop[mt][c], sa, 0, 0, 0);
+          sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr.kb[c], qop[mt][c], sb, 0, 0, 0);
+        }
+        // raw scores; the softmax runs on s * qscale (log2 units)
+        float sv[8];
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          sv[i2] = sa[i2];
+          sv[4 + i2] = sb[i2];
+        }
+        if (edge) {
+          const int qp = min(qpos[mt], pos_last);  // rows past the chunk end: any finite cut
+          const int qlo = WINDOWED ? qp - a.window + 1 : 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int key = p * kPage + (j >= 4 ? kPage : 0) + gq * 4 + (j & 3);
+            if (key < qlo || key > qp || (j >= 4 && !has_b)) sv[j] = -INFINITY;
+          }
+        }
+        float pmax = sv[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) pmax = fmaxf(pmax, sv[j]);
+        pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
+        pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+        pmax *= a.qscale;
+        // lazy rescale: the reference max moves only when a score exceeds it
+        // by more than 8 (log2 units), so p < 2^8 and the accumulators are
+        // rescaled a few times per row rather than every pair
+        if (__any(pmax > m_run[mt] + 8.f)) {
+          const float m_new = fmaxf(m_run[mt], pmax);
+          const float alpha = exp2_fast(m_run[mt] - m_new);
+          l_part[mt] *= alpha;
+          float al[4];
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) al[i2] = __shfl(alpha, gq * 4 + i2);
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int i2 = 0; i2 < 4; ++i2) acc[mt][nb][i2] *= al[i2];
+          m_run[mt] = m_new;
+        }
+        // a row that has seen no key yet keeps a finite reference
+        const float m_use = m_run[mt] == -INFINITY ? 0.f : m_run[mt];
+        float pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(fmaf(sv[j], a.qscale, -m_use));
+        l_part[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const f32x2 pp = {pv[j], pv[j + 1]};
+          const bf16x2 h = __builtin_convertvector(pp, bf16x2);
+          const bf16x2 l = __builtin_convertvector(pp - __builtin_convertvector(h, f32x2), bf16x2);
+          ph[j] = h[0];
+          ph[j + 1] = h[1];
+          pl[j] = l[0];
+          pl[j + 1] = l[1];
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const bf16x8 vv = __builtin_bit_cast(bf16x8, pr.v[nb]);
+          acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, acc[mt][nb], 0, 0, 0);
+          acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, acc[mt][nb], 0, 0, 0);
         }
       }
-      float pmax = sv[0];
-#pragma unroll
-      for (int j = 1; j < 8; ++j) pmax = fmaxf(pmax, sv[j]);
-      pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
-      pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
-      // rows past the chunk end see no key at all; keep them finite
-      const float m_new = fmaxf(m_run[mt], pmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      if (__any(m_new > m_run[mt])) {
-        const float alpha = exp2_fast(m_run[mt] - m_use);
-        l_part[mt] *= alpha;
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, gq * 4 + i);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][nb][i] *= al[i];
-      }
-      m_run[mt] = m_new;
-      float pv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(sv[j] - m_use);
-      l_part[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-      bf16x8 ph, pl;
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const f32x2 pp = {pv[j], pv[j + 1]};
-        const bf16x2 h = __builtin_convertvector(pp, bf16x2);
-        const bf16x2 l = __builtin_convertvector(pp - __builtin_convertvector(h, f32x2), bf16x2);
-        ph[j] = h[0];
-        ph[j + 1] = h[1];
-        pl[j] = l[0];
-        pl[j + 1] = l[1];
-      }
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const bf16x8 vv = __builtin_bit_cast(bf16x8, pr.v[nb]);
-        acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, acc[mt][nb], 0, 0, 0);
-        acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, acc[mt][nb], 0, 0, 0);
-      }
     }
+    if (more) stage_pair(sm[(i + 1) & 1], tid, kr, vr);
+    __syncthreads();
   }
+  if (!active) return;
 
   bad = __any(bad);
   // epilogue: acc rows gq*4+i are query vectors; their m and l live in lane gq*4+i
@@ -229,8 +297,8 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
   const dim3 grid((a.max_q_len + kRows - 1) / kRows, a.num_kv_heads, a.num_seqs);
-  if (a.window > 0) hipLaunchKernelGGL((prefill_kernel<true>), grid, dim3(kPWaves * 64), 0, st, a);
-  else hipLaunchKernelGGL((prefill_kernel<false>), grid, dim3(kPWaves * 64), 0, st, a);
+  if (a.window > 0) hipLaunchKernelGGL((prefill_kernel<true>), grid, dim3(kPThreads), 0, st, a);
+  else hipLaunchKernelGGL((prefill_kernel<false>), grid, dim3(kPThreads), 0, st, a);
   return hipGetLastError();
 }
 

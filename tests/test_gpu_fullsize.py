@@ -4,7 +4,7 @@ token fused into split-K decode, then the merge) with the default plan.
 
 Workloads: batch 1 at a 100,000-token context on a full layer (6,250 shuffled
 pages) and on a sliding layer (33-page ring); and 64 requests with context
-lengths uniform in [1024, 131072] on a full layer (8.4 GB of KV, the oracle
+lengths uniform in [1024, 131072] on a full layer (about 7.9 GB of KV, the oracle
 checking a sample of 8 requests on all 32 heads, every request checked for its
 cache write) and on a sliding layer (every request checked).
 
