@@ -11,9 +11,9 @@
 // wave owns kTiles such tiles (kWaveRows consecutive rows); a workgroup of
 // kPWaves waves owns kRows rows of one KV group.  The workgroup walks the key
 // pages of its rows in pairs (32 keys): every thread fetches 16 bytes of K and
-// 16 bytes of V of the next pair while the waves compute on the current one,
-// and the pair is staged once in LDS (double-buffered, one barrier per pair)
-// for all waves -- HBM/L2 traffic per flop falls by the number of waves.
+// 16 bytes of V of the pair two ahead while the waves compute on the current
+// one, and each pair is staged once in LDS (double-buffered, one barrier per
+// pair) for all waves -- HBM/L2 traffic per flop falls by the number of waves.
 // Per pair and tile:
 //   S^T[32 keys x 16 qv] = K . Q^T     2 x 4 v_mfma_f32_16x16x32_bf16
 //   O[16 qv x 128]      += P . V        8 x 2 v_mfma_f32_16x16x32_bf16
@@ -152,23 +152,19 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     if (pgb < 0 || pgb >= a.num_blocks) { bad = 1; pgb = 0; }
   };
 
-  u32x4 kr, vr;
-  if (npairs > 0) {
-    int pga, pgb;
-    pair_ids(p_first, pga, pgb);
-    fetch_pair(a, pga, pgb, g, tid, kr, vr);
-    stage_pair(sm[0], tid, kr, vr);
-  }
-  __syncthreads();
-
-  for (int i = 0; i < npairs; ++i) {
-    const int p = p_first + 2 * i;
-    const bool more = i + 1 < npairs;
-    if (more) {  // the next pair's loads fly during this pair's math
+  // Pairs in flight: at the top of iteration i, pair i is in LDS buffer i&1,
+  // pair i+1 in register set 1 and pair i+2 in register set 0 (loop unrolled
+  // by two so the sets are static), i.e. the global loads of a pair are
+  // issued two iterations before they are staged.
+  auto fetch = [&](int i, u32x4& kr, u32x4& vr) {
+    if (i < npairs) {
       int pga, pgb;
-      pair_ids(p + 2, pga, pgb);
+      pair_ids(p_first + 2 * i, pga, pgb);
       fetch_pair(a, pga, pgb, g, tid, kr, vr);
     }
+  };
+  auto compute = [&](int i) {
+    const int p = p_first + 2 * i;
     const bool has_b = p + 1 <= p_last;
     const int key_lo = p * kPage, key_hi = p * kPage + 2 * kPage - 1;
     if (active && key_hi >= lo_first && key_lo <= pos_last) {
@@ -261,7 +257,24 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    if (more) stage_pair(sm[(i + 1) & 1], tid, kr, vr);
+  };
+  u32x4 kr0, vr0, kr1, vr1;
+  if (npairs > 0) {
+    fetch(0, kr0, vr0);
+    stage_pair(sm[0], tid, kr0, vr0);
+  }
+  fetch(1, kr1, vr1);
+  fetch(2, kr0, vr0);
+  __syncthreads();
+  for (int i = 0; i < npairs; i += 2) {
+    compute(i);
+    if (i + 1 < npairs) stage_pair(sm[1], tid, kr1, vr1);
+    fetch(i + 3, kr1, vr1);
+    __syncthreads();
+    if (i + 1 >= npairs) break;
+    compute(i + 1);
+    if (i + 2 < npairs) stage_pair(sm[0], tid, kr0, vr0);
+    fetch(i + 4, kr0, vr0);
     __syncthreads();
   }
   if (!active) return;
