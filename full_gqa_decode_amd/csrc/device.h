@@ -36,6 +36,47 @@ __device__ __forceinline__ float lane_xor8(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }
 
+// Value of lane l ^ 16 / l ^ 32 paired with lane l's, without LDS: with both
+// operands x, v_permlane16_swap returns rows (0,0,2,2) and (1,1,3,3) of x and
+// v_permlane32_swap halves (0,0) and (1,1), so the two results of one swap
+// are {x[l], x[l^16]} (resp. {x[l], x[l^32]}) in some order on every lane.
+// (The two results are copied to scalars before the bit casts: a bit cast of
+// an element of the builtin's vector result reads element 0.)
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  a = __builtin_bit_cast(float, r0);
+  b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  float a, b;
+  swap16(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a, b;
+  swap32(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  float a, b;
+  swap16(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a, b;
+  swap32(x, a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);

@@ -132,6 +132,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       qop[mt][c] = (req_bad || !active) ? bf16x8{} : *(const bf16x8*)(qp + c * 32);
   }
 
+  // wait for the Q operands here, once: inside the loop the compiler cannot
+  // tell them apart from the page loads in flight and would wait for all of
+  // those before every pair's first MFMA
+#pragma unroll
+  for (int mt = 0; mt < kTiles; ++mt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qop[mt][c]));
+
   f32x4 acc[kTiles][8];
   float m_run[kTiles], l_part[kTiles];
 #pragma unroll
@@ -143,26 +151,35 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
   int bad = req_bad;
 
-  // physical pages of pair p (page b = page a past the range end); an id
-  // outside [0, num_blocks) marks the request bad and reads page 0 instead
-  auto pair_ids = [&](int p, int& pga, int& pgb) {
-    pga = a.block_tables[(int64_t)b * a.bt_stride + p];
-    pgb = p + 1 <= p_last ? a.block_tables[(int64_t)b * a.bt_stride + p + 1] : pga;
+  // Physical pages of pair j.  The page-table reads are vector loads, which
+  // complete in issue order with the page loads, so each id is requested two
+  // iterations before its pair's page loads need it: waiting for it then
+  // never waits for a page load that is not already needed.  Loads are
+  // unconditional (index clamped to the range) so no wait lands on a branch
+  // join.  An id outside [0, num_blocks) marks the request bad and reads
+  // page 0 instead; past the range end page b repeats page a.
+  const int* bt_row = a.block_tables + (int64_t)b * a.bt_stride;
+  auto load_ids = [&](int j, int& ia, int& ib) {
+    const int p = min(p_first + 2 * j, p_last);
+    ia = bt_row[p];
+    ib = bt_row[min(p + 1, p_last)];
+  };
+  auto check_ids = [&](int j, int ia, int ib, int& pga, int& pgb) {
+    const int p = p_first + 2 * j;
+    pga = __builtin_amdgcn_readfirstlane(ia);
+    pgb = p + 1 <= p_last ? __builtin_amdgcn_readfirstlane(ib) : pga;
     if (pga < 0 || pga >= a.num_blocks) { bad = 1; pga = 0; }
     if (pgb < 0 || pgb >= a.num_blocks) { bad = 1; pgb = 0; }
   };
-
-  // Pairs in flight: at the top of iteration i, pair i is in LDS buffer i&1,
-  // pair i+1 in register set 1 and pair i+2 in register set 0 (loop unrolled
-  // by two so the sets are static), i.e. the global loads of a pair are
-  // issued two iterations before they are staged.
-  auto fetch = [&](int i, u32x4& kr, u32x4& vr) {
-    if (i < npairs) {
+  // page loads of pair j (ids ia, ib), if it exists
+  auto fetch = [&](int j, int ia, int ib, u32x4& kr, u32x4& vr) {
+    if (j < npairs) {
       int pga, pgb;
-      pair_ids(p_first + 2 * i, pga, pgb);
+      check_ids(j, ia, ib, pga, pgb);
       fetch_pair(a, pga, pgb, g, tid, kr, vr);
     }
   };
+
   auto compute = [&](int i) {
     const int p = p_first + 2 * i;
     const bool has_b = p + 1 <= p_last;
@@ -186,6 +203,10 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         for (int nb = 0; nb < 8; ++nb) pr.v[nb] &= mk;
       }
 
+      // scores of every tile first, one branch for masking and one for the
+      // (rare) rescale, then the value products: large basic blocks, so the
+      // softmax arithmetic of one tile can overlap the other tile's MFMAs
+      float sv[kTiles][8];
 #pragma unroll
       for (int mt = 0; mt < kTiles; ++mt) {
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -194,33 +215,42 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
           sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr.ka[c], qop[mt][c], sa, 0, 0, 0);
           sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr.kb[c], qop[mt][c], sb, 0, 0, 0);
         }
-        // raw scores; the softmax runs on s * qscale (log2 units)
-        float sv[8];
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) {
-          sv[i2] = sa[i2];
-          sv[4 + i2] = sb[i2];
+          sv[mt][i2] = sa[i2];
+          sv[mt][4 + i2] = sb[i2];
         }
-        if (edge) {
+      }
+      if (edge) {
+#pragma unroll
+        for (int mt = 0; mt < kTiles; ++mt) {
           const int qp = min(qpos[mt], pos_last);  // rows past the chunk end: any finite cut
           const int qlo = WINDOWED ? qp - a.window + 1 : 0;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int key = p * kPage + (j >= 4 ? kPage : 0) + gq * 4 + (j & 3);
-            if (key < qlo || key > qp || (j >= 4 && !has_b)) sv[j] = -INFINITY;
+            if (key < qlo || key > qp || (j >= 4 && !has_b)) sv[mt][j] = -INFINITY;
           }
         }
-        float pmax = sv[0];
+      }
+      // raw scores; the softmax runs on s * qscale (log2 units)
+      float pmax[kTiles];
+      bool grow = false;
 #pragma unroll
-        for (int j = 1; j < 8; ++j) pmax = fmaxf(pmax, sv[j]);
-        pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
-        pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
-        pmax *= a.qscale;
-        // lazy rescale: the reference max moves only when a score exceeds it
-        // by more than 8 (log2 units), so p < 2^8 and the accumulators are
-        // rescaled a few times per row rather than every pair
-        if (__any(pmax > m_run[mt] + 8.f)) {
-          const float m_new = fmaxf(m_run[mt], pmax);
+      for (int mt = 0; mt < kTiles; ++mt) {
+        float x = sv[mt][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) x = fmaxf(x, sv[mt][j]);
+        pmax[mt] = max_xor32(max_xor16(x)) * a.qscale;
+        grow |= pmax[mt] > m_run[mt] + 8.f;
+      }
+      // lazy rescale: the reference max moves only when a score exceeds it
+      // by more than 8 (log2 units), so p < 2^8 and the accumulators are
+      // rescaled a few times per row rather than every pair
+      if (__any(grow)) {
+#pragma unroll
+        for (int mt = 0; mt < kTiles; ++mt) {
+          const float m_new = fmaxf(m_run[mt], pmax[mt]);
           const float alpha = exp2_fast(m_run[mt] - m_new);
           l_part[mt] *= alpha;
           float al[4];
@@ -232,11 +262,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
             for (int i2 = 0; i2 < 4; ++i2) acc[mt][nb][i2] *= al[i2];
           m_run[mt] = m_new;
         }
+      }
+#pragma unroll
+      for (int mt = 0; mt < kTiles; ++mt) {
         // a row that has seen no key yet keeps a finite reference
         const float m_use = m_run[mt] == -INFINITY ? 0.f : m_run[mt];
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(fmaf(sv[j], a.qscale, -m_use));
+        for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(fmaf(sv[mt][j], a.qscale, -m_use));
         l_part[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
         bf16x8 ph, pl;
 #pragma unroll
@@ -258,23 +291,35 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
+  // In flight at the top of iteration i: pair i in LDS buffer i&1, the page
+  // loads of pairs i+1 and i+2 in register sets (i+1)&1 and (i+2)&1, the ids
+  // of pairs i+3 and i+4 in id sets (i+3)&1 and (i+4)&1 (loop unrolled by two
+  // so every set is static).
   u32x4 kr0, vr0, kr1, vr1;
+  int ia0, ib0, ia1, ib1, ia2, ib2;
   if (npairs > 0) {
-    fetch(0, kr0, vr0);
+    load_ids(0, ia0, ib0);
+    load_ids(1, ia1, ib1);
+    load_ids(2, ia2, ib2);
+    fetch(0, ia0, ib0, kr0, vr0);
     stage_pair(sm[0], tid, kr0, vr0);
+    fetch(1, ia1, ib1, kr1, vr1);
+    fetch(2, ia2, ib2, kr0, vr0);
+    load_ids(3, ia1, ib1);
+    load_ids(4, ia0, ib0);
   }
-  fetch(1, kr1, vr1);
-  fetch(2, kr0, vr0);
   __syncthreads();
   for (int i = 0; i < npairs; i += 2) {
     compute(i);
     if (i + 1 < npairs) stage_pair(sm[1], tid, kr1, vr1);
-    fetch(i + 3, kr1, vr1);
+    fetch(i + 3, ia1, ib1, kr1, vr1);
+    load_ids(i + 5, ia1, ib1);
     __syncthreads();
     if (i + 1 >= npairs) break;
     compute(i + 1);
     if (i + 2 < npairs) stage_pair(sm[0], tid, kr0, vr0);
-    fetch(i + 4, kr0, vr0);
+    fetch(i + 4, ia0, ib0, kr0, vr0);
+    load_ids(i + 6, ia0, ib0);
     __syncthreads();
   }
   if (!active) return;
