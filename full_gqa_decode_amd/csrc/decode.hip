@@ -124,8 +124,7 @@ __device__ __forceinline__ void consume_page(PageRegs& r, const bf16x8 (&qop)[4]
 
   // online softmax in log2 units (q carries scale*log2(e))
   float pmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
-  pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+  pmax = max_xor32(max_xor16(pmax));
   const float m_new = fmaxf(st.m_run, pmax);
   if (__any(m_new > st.m_run)) {
     const float alpha = exp2_fast(st.m_run - m_new);
@@ -415,12 +414,11 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_ker
   // ---- per-wave state -> LDS -> this split's result -----------------------
   // l: sum over the four lane groups of head n&7.  acc rows gq*4+i: gq 0,1 the
   // bf16 parts of heads 0-7, gq 2,3 the remainders.
-  float l_h = st.l_part + __shfl_xor(st.l_part, 16);
-  l_h += __shfl_xor(l_h, 32);
+  const float l_h = sum_xor32(sum_xor16(st.l_part));
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.acc[nb][i] += __shfl_xor(st.acc[nb][i], 32);
+    for (int i = 0; i < 4; ++i) st.acc[nb][i] = sum_xor32(st.acc[nb][i]);
   if (gq < 2) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
