@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from flint_cases import CacheDecodeCase, dev, up
+from flint_cases import CacheDecodeCase, DecodeCase, dev, up
 
 pytestmark = pytest.mark.gpu
 
@@ -33,4 +33,45 @@ def test_graph_replays_match_eager():
         assert np.array_equal(out.cpu().numpy(), ref)
         # eager work between replays
         fl.flint_attn_decode(case.FL, q, kc, vc, bt, sl, 5000, sk, eager, workspace=ws)
+        torch.cuda.synchronize()
+
+
+def test_fused_step_graph_replays_match_eager():
+    # the whole fused step (norm/RoPE/append of the new token + decode) of a
+    # full and a sliding layer in one graph; re-appending the same token is
+    # idempotent, so every replay must reproduce the eager outputs and cache
+    import torch
+    import full_gqa_decode_amd as fl
+    cases = [DecodeCase(3, [3000, 129], window=0), DecodeCase(3, [3000, 129], window=513, ring=True)]
+    runs = []
+    for c in cases:
+        out, qo, kd, vd = c.run_gpu_fused()
+        r = c.last_row
+        runs.append(dict(c=c, eager=out.cpu().numpy(), kc=kd.cpu().numpy(), kd=kd, vd=vd,
+                         q=up(c.q_in[r]), k=up(c.k_in[r]), v=up(c.v_in[r]), qw=up(c.qw),
+                         kw=up(c.kw), sl=up(c.slots[r]), bt=up(c.bt), lens=up(c.seq_lens),
+                         sk=up(c.sinks), out=torch.empty_like(out),
+                         ws=torch.zeros(fl.flint_attn_decode_workspace_size(c.FL, c.B, max(c.ctxs)),
+                                        dtype=torch.uint8, device=dev())))
+    def step():
+        for x in runs:
+            c = x["c"]
+            fl.flint_attn_decode_step(c.FL, x["q"], x["k"], x["v"], x["qw"], x["kw"], x["sl"],
+                                      x["kd"], x["vd"], x["bt"], x["lens"], max(c.ctxs), x["sk"],
+                                      x["out"], workspace=x["ws"])
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    for _ in range(3):
+        for x in runs:
+            x["out"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x in runs:
+            assert np.array_equal(x["out"].cpu().numpy(), x["eager"])
+            assert np.array_equal(x["kd"].cpu().numpy(), x["kc"])
+        step()  # eager work between replays
         torch.cuda.synchronize()

@@ -67,7 +67,7 @@ class PrefillCase:
         return oracle.attn_prefill(self.L, full_q, self.cu, kc, vc, self.bt, self.seq_lens,
                                    self.sinks, rows=None if rows is None else idx)
 
-    def run_gpu(self):
+    def run_gpu(self, bt=None, seq_lens=None):
         import torch
         import full_gqa_decode_amd as fl
         kd = torch.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
@@ -80,8 +80,10 @@ class PrefillCase:
                                      kd, vd)
         qc = qb[torch.from_numpy(self.chunk_rows).to(dev())].contiguous()
         out = torch.empty((len(self.chunk_rows), 32, 128), dtype=torch.float32, device=dev())
-        fl.flint_attn_prefill(self.FL, qc, up(self.cu), self.max_q, kd, vd, up(self.bt),
-                              up(self.seq_lens), int(self.seq_lens.max()), up(self.sinks), out)
+        bt = self.bt if bt is None else bt
+        sl = self.seq_lens if seq_lens is None else seq_lens
+        fl.flint_attn_prefill(self.FL, qc, up(self.cu), self.max_q, kd, vd, up(bt), up(sl),
+                              int(self.seq_lens.max()), up(self.sinks), out)
         torch.cuda.synchronize()
         return out.cpu().numpy(), kd, vd, qb
 
@@ -130,3 +132,59 @@ def test_prefill_config4_32768_sampled_rows(window):
     ref = case.expected(rows=rows)
     assert max_err(got[rows], ref[rows]) <= TOL
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_prefill_short_chunk_at_the_end_of_a_long_context(window):
+    case = PrefillCase(4, [(12000, 80)], window=window)
+    got, _, _, _ = case.run_gpu()
+    assert max_err(got, case.expected()) <= TOL
+
+
+def test_prefill_empty_chunk_in_a_batch():
+    case = PrefillCase(5, [(100, 50), (64, 0), (200, 20)], window=0)
+    got, _, _, _ = case.run_gpu()
+    assert got.shape[0] == 70
+    assert max_err(got, case.expected()) <= TOL
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_prefill_invalid_requests_give_nan_and_spare_the_rest(window):
+    # request 1: a page id past num_blocks; request 2: a chunk longer than
+    # its context.  Both come out NaN; request 0 is untouched by them.
+    case = PrefillCase(6, [(300, 100), (200, 50), (150, 150)], window=window)
+    bt = case.bt.copy()
+    bt[1, 3] = case.num_blocks + 7
+    sl = case.seq_lens.copy()
+    sl[2] = 149
+    got, _, _, _ = case.run_gpu(bt=bt, seq_lens=sl)
+    assert np.isnan(got[100:300]).all()
+    ok = PrefillCase(6, [(300, 100), (200, 50), (150, 150)], window=window).expected(
+        rows=np.arange(100))
+    assert max_err(got[:100], ok[:100]) <= TOL
+
+
+def test_prefill_graph_replays_match_eager():
+    import torch
+    import full_gqa_decode_amd as fl
+    case = PrefillCase(7, [(700, 300), (90, 90)], window=513)
+    eager, kd, vd, qb = case.run_gpu()
+    qc = qb[torch.from_numpy(case.chunk_rows).to(dev())].contiguous()
+    cu, bt, sl, sk = up(case.cu), up(case.bt), up(case.seq_lens), up(case.sinks)
+    out = torch.empty((len(case.chunk_rows), 32, 128), dtype=torch.float32, device=dev())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fl.flint_attn_prefill(case.FL, qc, cu, case.max_q, kd, vd, bt, sl,
+                                  int(case.seq_lens.max()), sk, out)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager)
+        # eager work between replays
+        fl.flint_attn_prefill(case.FL, qc, cu, case.max_q, kd, vd, bt, sl,
+                              int(case.seq_lens.max()), sk, torch.empty_like(out))
+        torch.cuda.synchronize()
