@@ -222,26 +222,39 @@ def main():
     us_unfused = e0.elapsed_time(e1) * 1e3 / args.steps
     log(f"bench: unfused (append, then decode) {us_unfused:.1f} us/step")
 
-    # dominant kernel: full-layer decode, timed over back-to-back replays of the
-    # 14 full layers on the stream they run on
+    # dominant kernel: the split-K kernel (K2) of a full layer, alone, through
+    # flint_attn_decode_partials -- 14 full layers back to back in one graph,
+    # timed on the stream it runs on; and the launch pair of the fused step
+    # (split kernel + merge) the same way
     full_layers = [L for L in layers if L["full"]]
-    gf = capture(lambda: [layer_step(L) for L in full_layers])
-    reps = 20
-    for _ in range(3):
-        gf.replay()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(reps):
-            gf.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    us_full = e0.elapsed_time(e1) * 1e3 / (reps * len(full_layers))
-    kv_full = CTX * KV_BYTES_PER_TOKEN_LAYER
-    extra_full = HQ * D * 4 * 2 + HQ * 4 + (-(-CTX // PAGE)) * 4   # q, out, sinks, page table
-    achieved = (kv_full + extra_full) / (us_full * 1e-6) / 1e9
     pps, nsplit = fl.flint_attn_decode_plan(FULL, 1, CTX)
+    part_o = torch.empty((1, nsplit, HQ, D), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((1, nsplit, HQ), dtype=torch.float32, device=dev)
+
+    def time_graph(fn, reps=20):
+        gr = capture(fn)
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            t0.record(stream)
+            for _ in range(reps):
+                gr.replay()
+            t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / (reps * len(full_layers))
+
+    us_k2 = time_graph(lambda: [fl.flint_attn_decode_partials(
+        FULL, L["q_out"], L["kc"], L["vc"], L["bt"], seq_lens, CTX, pps, part_o, part_lse)
+        for L in full_layers])
+    us_full = time_graph(lambda: [layer_step(L) for L in full_layers])
+    kv_full = CTX * KV_BYTES_PER_TOKEN_LAYER
+    table = (-(-CTX // PAGE)) * 4
+    k2_bytes = kv_full + HQ * D * 4 + table                   # K/V, q, page table
+    pair_bytes = kv_full + HQ * D * 4 * 2 + HQ * 4 + table    # + out, sinks
+    achieved = k2_bytes / (us_k2 * 1e-6) / 1e9
+    pair_achieved = pair_bytes / (us_full * 1e-6) / 1e9
 
     kv_step = sum(CTX * KV_BYTES_PER_TOKEN_LAYER if L["full"] else WINDOW * KV_BYTES_PER_TOKEN_LAYER
                   for L in layers)
@@ -274,14 +287,19 @@ def main():
         "us_per_step_p10": round(float(np.percentile(per, 10)), 2),
         "us_per_step_p90": round(float(np.percentile(per, 90)), 2),
         "us_per_step_unfused": round(us_unfused, 2),
-        "roofline": {"kernel": "full-layer decode, 100,000 keys: the split-K kernel (fused "
-                               "norm/RoPE/append) and its LSE-merge kernel, the launch pair of "
-                               "one flint_attn_decode_step call",
+        "roofline": {"kernel": "decode_split_kernel (K2, split-K flash decode) of one full "
+                               "layer over 100,000 keys, alone: 64 splits x 4 KV heads, launched "
+                               "through flint_attn_decode_partials",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(), "us_per_launch": round(us_full, 2),
-                     "bytes_per_launch": kv_full + extra_full,
-                     "pages_per_split": pps, "splits": nsplit},
+                     "traffic": measured_traffic(), "us_per_launch": round(us_k2, 2),
+                     "bytes_per_launch": k2_bytes, "pages_per_split": pps, "splits": nsplit,
+                     "pair": {"kernels": "split kernel (fused norm/RoPE/append) + LSE merge, "
+                                         "the two launches of one full-layer "
+                                         "flint_attn_decode_step",
+                              "us_per_launch": round(us_full, 2), "bytes_per_launch": pair_bytes,
+                              "achieved": round(pair_achieved, 1),
+                              "frac": round(pair_achieved / HBM_PEAK_GBPS, 4)}},
         "context": "pages' end-to-end figure (model forward + LM head + sampling, 1x GB200, "
                    "vLLM): 2.06 ms/token ~ 485 tok/s at bs1, 100K ctx; not this metric",
     }

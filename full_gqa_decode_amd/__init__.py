@@ -76,6 +76,9 @@ SIGNATURES = [
     ("flint_attn_decode_step", C.c_int,
      [_LP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _I, _P]),
     ("flint_attn_decode_plan", C.c_int, [_LP, _I, _I, _I, C.POINTER(_I), C.POINTER(_I)]),
+    ("flint_attn_decode_partials", C.c_int,
+     [_LP, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
+    ("flint_attn_merge", C.c_int, [_LP, _I, _I, _P, _P, _P, _P, _P]),
     ("flint_attn_prefill_workspace_size", _SZ, [_LP, _I, _I, _I]),
     ("flint_attn_prefill", C.c_int,
      [_LP, _I, _P, _P, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
@@ -183,6 +186,40 @@ def flint_attn_decode_plan(L: FlintAttnLayer, num_seqs: int, max_seq_len: int,
     _check(lib().flint_attn_decode_plan(C.byref(L), num_seqs, max_seq_len, pages_per_split,
                                         C.byref(pps), C.byref(ns)))
     return pps.value, ns.value
+
+
+def flint_attn_decode_partials(L: FlintAttnLayer, q, k_cache, v_cache, block_tables, seq_lens,
+                               max_seq_len: int, pages_per_split: int, part_o=None,
+                               part_lse=None, stream=None):
+    """K2 alone: every split's partial (normalised output, base-2 lse) for
+    splits of `pages_per_split` pages; returns (part_o [B,S,Hq,128],
+    part_lse [B,S,Hq]), allocated here when not given."""
+    torch = _torch()
+    B = q.shape[0]
+    _, S = flint_attn_decode_plan(L, B, max_seq_len, pages_per_split)
+    if part_o is None:
+        part_o = torch.empty((B, S, L.num_q_heads, 128), dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty((B, S, L.num_q_heads), dtype=torch.float32, device=q.device)
+    _check(lib().flint_attn_decode_partials(
+        C.byref(L), B, _ptr(q, _f32(), "q"), _ptr(k_cache, _b16(), "k_cache"),
+        _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
+        _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, pages_per_split, S,
+        _ptr(part_o, _f32(), "part_o"), _ptr(part_lse, _f32(), "part_lse"), _stream(stream)))
+    return part_o, part_lse
+
+
+def flint_attn_merge(L: FlintAttnLayer, part_o, part_lse, sinks, out=None, stream=None):
+    """K3 alone: fold the partials [B,S,Hq,...] and the sinks into out [B,Hq,128]."""
+    torch = _torch()
+    B, S = part_lse.shape[0], part_lse.shape[1]
+    if out is None:
+        out = torch.empty((B, L.num_q_heads, 128), dtype=torch.float32, device=part_o.device)
+    _check(lib().flint_attn_merge(C.byref(L), B, S, _ptr(part_o, _f32(), "part_o"),
+                                  _ptr(part_lse, _f32(), "part_lse"), _ptr(sinks, _f32(), "sinks"),
+                                  _ptr(out, _f32(), "out"), _stream(stream)))
+    return out
 
 
 def flint_attn_decode(L: FlintAttnLayer, q, k_cache, v_cache, block_tables, seq_lens,

@@ -358,6 +358,81 @@ flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, cons
                               workspace_bytes, 0, stream);
 }
 
+flint_status flint_attn_decode_partials(const flint_attn_layer* L, int32_t num_seqs,
+                                        const float* q, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, int32_t num_blocks,
+                                        const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* seq_lens, int32_t max_seq_len,
+                                        int32_t pages_per_split, int32_t num_splits,
+                                        float* part_o, float* part_lse, void* stream) {
+  flint_status st = check_layer(L);
+  if (st != FLINT_OK) return st;
+  if (pages_per_split < 1)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "pages_per_split %d < 1", pages_per_split);
+  if (num_seqs < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
+  if (max_seq_len < 1 || max_seq_len > kMaxContext)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [1, %d]", max_seq_len,
+                kMaxContext);
+  const Plan pl = make_plan(L, num_seqs, max_seq_len, pages_per_split);
+  if (num_splits != pl.num_splits)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "num_splits %d, the plan has %d", num_splits,
+                pl.num_splits);
+  if (num_seqs == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !part_o || !part_lse)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (num_blocks < 1) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_blocks %d < 1", num_blocks);
+  if (bt_stride < 1) return fail(FLINT_ERR_INVALID_ARGUMENT, "bt_stride %d < 1", bt_stride);
+  if ((int64_t)max_seq_len > (int64_t)bt_stride * 16)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "max_seq_len %d exceeds bt_stride*16 = %lld",
+                max_seq_len, (long long)bt_stride * 16);
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(part_o, 16) || !aligned(part_lse, 4) || !aligned(block_tables, 4) ||
+      !aligned(seq_lens, 4))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "misaligned pointer (q, caches, part_o need 16 B)");
+  flint::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = const_cast<uint16_t*>(k_cache);
+  a.v_cache = const_cast<uint16_t*>(v_cache);
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = L->num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.bt_stride = bt_stride;
+  a.window = L->window;
+  a.max_seq_len = max_seq_len;
+  a.pages_per_split = pl.pages_per_split;
+  a.num_splits = pl.num_splits;
+  a.partials_only = 1;
+  a.qscale = L->softmax_scale * 1.4426950408889634f;
+  return hip_status(flint::launch_decode(a, (hipStream_t)stream), "partials launch");
+}
+
+flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32_t num_splits,
+                              const float* part_o, const float* part_lse, const float* sinks,
+                              float* out, void* stream) {
+  flint_status st = check_layer(L);
+  if (st != FLINT_OK) return st;
+  if (num_seqs < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
+  if (num_splits < 1) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_splits %d < 1", num_splits);
+  if (num_seqs == 0) return ok();
+  if (!part_o || !part_lse || !sinks || !out)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (!aligned(part_o, 4) || !aligned(part_lse, 4) || !aligned(sinks, 4) || !aligned(out, 4))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "misaligned pointer");
+  flint::DecodeArgs a{};
+  a.part_o = const_cast<float*>(part_o);
+  a.part_lse = const_cast<float*>(part_lse);
+  a.sinks = sinks;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = L->num_kv_heads;
+  a.num_splits = num_splits;
+  return hip_status(flint::launch_merge(a, (hipStream_t)stream), "merge launch");
+}
+
 size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_seq_len) {
   (void)L;

@@ -563,6 +563,16 @@ template <bool FUSED>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
   const bool win = a.window > 0;
+  if (!FUSED && a.partials_only) {  // every split's partial, whatever the count
+    constexpr int W = kDecodeWaves;
+    if (win)
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false>), grid, dim3(W * 64), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false>), grid, dim3(W * 64), 0,
+                         st, a);
+    return hipGetLastError();
+  }
   if (a.num_splits == 1 && a.pages_per_split <= kSinglePages) {
     constexpr int W = kDecodeWavesSingle;
     constexpr int P = (kSinglePages + W - 1) / W;
@@ -600,6 +610,13 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
   return a.q_in ? launch_decode_t<true>(a, st) : launch_decode_t<false>(a, st);
+}
+
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {
+  if (a.num_seqs == 0) return hipSuccess;
+  const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
+  hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace flint

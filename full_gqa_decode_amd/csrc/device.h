@@ -28,8 +28,6 @@ __device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
 // Value from lane (lane ^ 8) inside each row of 16 lanes (DPP row_ror:8).
 __device__ __forceinline__ float lane_xor8(float x) {
   return __builtin_bit_cast(
@@ -75,12 +73,6 @@ __device__ __forceinline__ float sum_xor32(float x) {
   float a, b;
   swap32(x, a, b);
   return a + b;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -47,6 +47,7 @@ struct DecodeArgs {
   int32_t max_seq_len;
   int32_t pages_per_split;
   int32_t num_splits;        // splits in the grid (per request)
+  int32_t partials_only;     // write every split's partial (no merge, no sink)
   float qscale;              // softmax_scale * log2(e)
   // fused append of the new token (flint_attn_decode_step); q_in == nullptr
   // selects the unfused path
@@ -62,6 +63,8 @@ struct DecodeArgs {
   float rms_eps;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// K3 alone: out from part_o / part_lse / sinks (num_seqs, num_kv_heads, num_splits)
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 
 struct PrefillArgs {
   const uint16_t* q;         // [total_q][Hq][128] bf16

@@ -188,6 +188,47 @@ flint_status flint_attn_decode_plan(const flint_attn_layer* L, int32_t num_seqs,
                                     int32_t* out_pages_per_split, int32_t* out_num_splits);
 
 /*
+ * The two halves of flint_attn_decode on their own: the split partials (no
+ * sink), then their log-sum-exp merge with the sink.  They serve a caller
+ * that holds the keys of one request on several devices (each computes the
+ * partials of its range; the merge folds them), and they let each half be
+ * checked and timed alone.  flint_attn_decode_ex with the same
+ * pages_per_split (when the plan has more than one split) produces the same
+ * output, bit for bit, as this pair.
+ *
+ * flint_attn_decode_partials: request b's key range lo..t (t = seq_lens[b]-1,
+ * lo as for decode) is cut by logical page: split s holds the keys of pages
+ * lo/16 + s*P .. lo/16 + (s+1)*P - 1 that lie in lo..t, where P and the split
+ * count S are what flint_attn_decode_plan returns for this pages_per_split
+ * (>= 1; num_splits must equal S).  For query head h, with
+ * s_j = softmax_scale * q.k_j over the split's keys:
+ *   part_lse[(b*S + s)*Hq + h]           = log2( sum_j e^{s_j} )   (base 2)
+ *   part_o[((b*S + s)*Hq + h)*128 + d]   = sum_j e^{s_j} V_j[d] / sum_j e^{s_j}
+ * An empty split has part_lse = -inf (part_o left as it was); a request with
+ * a bad seq_len or page id has NaN part_lse in every split.
+ *   part_o [B][S][num_q_heads][128] fp32, part_lse [B][S][num_q_heads] fp32
+ */
+flint_status flint_attn_decode_partials(const flint_attn_layer* L, int32_t num_seqs,
+                                        const float* q, const uint16_t* k_cache,
+                                        const uint16_t* v_cache, int32_t num_blocks,
+                                        const int32_t* block_tables, int32_t bt_stride,
+                                        const int32_t* seq_lens, int32_t max_seq_len,
+                                        int32_t pages_per_split, int32_t num_splits,
+                                        float* part_o, float* part_lse, void* stream);
+
+/*
+ * flint_attn_merge: out[b][h] from the S partials of (b, h) and the sink
+ * ("Model architecture": learned attention sinks), M = max(sink_h, lse_s):
+ *   out = sum_s 2^{lse_s - M} o_s / (2^{sink_h*log2(e) - M} + sum_s 2^{lse_s - M})
+ * with lse_s in the base-2 form above and M in the same units.  Splits with
+ * lse = -inf are skipped (their part_o is not read as a number); a NaN lse
+ * makes that output NaN.  out [B][num_q_heads][128] fp32.
+ */
+flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32_t num_splits,
+                              const float* part_o, const float* part_lse, const float* sinks,
+                              float* out, void* stream);
+
+/*
  * Causal (optionally windowed) prefill attention over the paged cache, on
  * the matrix cores.  Request b owns query rows cu_q_lens[b] ..
  * cu_q_lens[b+1]-1 (cu_q_lens [B+1] int32 on device, cu_q_lens[0] = 0); row

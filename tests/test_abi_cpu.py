@@ -148,3 +148,45 @@ def test_decode_plan_covers_every_page():
     Ls = fl.sliding_layer()
     p, s = fl.flint_attn_decode_plan(Ls, 1, 100000, 0)
     assert s * p >= 33 and (s - 1) * p < 33
+
+
+def _partials(L, **kw):
+    a = dict(num_seqs=1, q=P, k=Q, v=Q + 0x1000, nb=4, bt=P + 0x10000, bt_stride=4,
+             sl=P + 0x20000, max_seq_len=64, pps=1, ns=4, po=P + 0x40000, pl=P + 0x50000)
+    a.update(kw)
+    return fl.lib().flint_attn_decode_partials(C.byref(L), a["num_seqs"], a["q"], a["k"], a["v"],
+                                                a["nb"], a["bt"], a["bt_stride"], a["sl"],
+                                                a["max_seq_len"], a["pps"], a["ns"], a["po"],
+                                                a["pl"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(pps=0),               # the split size must be explicit
+    dict(ns=3),                # 64 keys in 1-page splits is 4 splits
+    dict(q=None),
+    dict(po=None),
+    dict(pl=None),
+    dict(po=P + 0x40004),      # misaligned partial outputs
+    dict(max_seq_len=65),      # > bt_stride * 16
+    dict(nb=0),
+])
+def test_partials_reject_bad_arguments(kw):
+    assert _partials(fl.full_layer(), **kw) == INVALID
+    assert fl.lib().flint_last_error().decode() != ""
+
+
+def test_partials_split_count_follows_the_plan():
+    L = fl.sliding_layer()
+    # a 513-key window spans at most 33 pages: 3-page splits give 11
+    assert fl.flint_attn_decode_plan(L, 1, 100_000, 3) == (3, 11)
+    assert _partials(L, max_seq_len=64, bt_stride=4, pps=3, ns=2, num_seqs=0) == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ns=0), dict(po=None), dict(pl=None), dict(sinks=None), dict(out=None),
+])
+def test_merge_rejects_bad_arguments(kw):
+    a = dict(num_seqs=1, ns=4, po=P, pl=P + 0x10000, sinks=P + 0x20000, out=P + 0x30000)
+    a.update(kw)
+    assert fl.lib().flint_attn_merge(C.byref(fl.full_layer()), a["num_seqs"], a["ns"], a["po"],
+                                     a["pl"], a["sinks"], a["out"], None) == INVALID
