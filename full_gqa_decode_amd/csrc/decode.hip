@@ -559,6 +559,62 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   }
 }
 
+// K3 for plans of at most kSmallMergeSplits splits (a batch of requests cut
+// into a few splits each): one thread per output element, all of its
+// partials loaded in one round trip.  The wide kernel above would leave most
+// of its split groups idle and launch a workgroup per (head, request, quarter).
+constexpr int kSmallMergeSplits = 8;
+constexpr int kSmallMergeThreads = 256;
+
+__global__ __launch_bounds__(kSmallMergeThreads) void decode_merge_small_kernel(DecodeArgs a) {
+  const int hq = a.num_kv_heads * kGroup;
+  const int ns = a.num_splits;
+  const int64_t idx = (int64_t)blockIdx.x * kSmallMergeThreads + threadIdx.x;
+  if (idx >= (int64_t)a.num_seqs * hq * kHeadDim) return;
+  const int d = (int)(idx & (kHeadDim - 1));
+  const int64_t bh = idx >> 7;
+  const int h = (int)(bh % hq);
+  const int64_t b = bh / hq;
+  const int64_t base = b * ns * hq + h;
+  float lv[kSmallMergeSplits], ov[kSmallMergeSplits];
+#pragma unroll
+  for (int s = 0; s < kSmallMergeSplits; ++s) {
+    const int64_t row = base + (int64_t)min(s, ns - 1) * hq;
+    lv[s] = a.part_lse[row];
+    ov[s] = a.part_o[row * kHeadDim + d];
+    if (s >= ns) lv[s] = -INFINITY;
+  }
+  const float sink = a.sinks[h] * kLog2e;
+  float M = sink;
+  int nan = 0;
+#pragma unroll
+  for (int s = 0; s < kSmallMergeSplits; ++s) {
+    nan |= lv[s] != lv[s];
+    M = fmaxf(M, lv[s]);
+  }
+  float o = 0.f, den = exp2_fast(sink - M);
+#pragma unroll
+  for (int s = 0; s < kSmallMergeSplits; ++s) {
+    const bool live = lv[s] > -INFINITY;
+    const float w = live ? exp2_fast(lv[s] - M) : 0.f;
+    den += w;
+    o += live ? w * ov[s] : 0.f;
+  }
+  a.out[bh * kHeadDim + d] = nan ? __builtin_nanf("") : o / den;
+}
+
+hipError_t launch_merge_k(const DecodeArgs& a, hipStream_t st) {
+  if (a.num_splits <= kSmallMergeSplits) {
+    const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * kGroup * kHeadDim;
+    const dim3 grid((unsigned)((n + kSmallMergeThreads - 1) / kSmallMergeThreads));
+    hipLaunchKernelGGL(decode_merge_small_kernel, grid, dim3(kSmallMergeThreads), 0, st, a);
+  } else {
+    const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
+    hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
 template <bool FUSED>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
@@ -600,9 +656,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED>), grid, dim3(W * 64), 0, st,
                        a);
-  const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
-  hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_merge_k(a, st);
 }
 
 }  // namespace
@@ -614,9 +670,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
-  const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
-  hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);
-  return hipGetLastError();
+  return launch_merge_k(a, st);
 }
 
 }  // namespace flint
