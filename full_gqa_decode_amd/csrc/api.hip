@@ -85,16 +85,22 @@ struct Plan {
 // About kTargetWorkgroups workgroups of (split, KV head, request): a short
 // range (the 513-key window) becomes small splits so its bytes spread over many
 // CUs; a long one at batch 1 is cut into one split per CU; a batch of long
-// requests keeps splits of at most kMaxSplitPages pages, so that its longest
-// requests are spread too.
+// requests keeps splits of at most kMaxSplitPages pages (so that its longest
+// requests are spread too) in a grid of whole rounds of kTargetWorkgroups.
 Plan make_plan(const flint_attn_layer* L, int32_t num_seqs, int32_t max_seq_len, int32_t pps) {
   const int64_t pages = max_key_pages(L, max_seq_len);
   int64_t p = pps;
   if (p <= 0) {
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * L->num_kv_heads;
-    const int64_t splits = (kTargetWorkgroups + units - 1) / units;
+    int64_t splits = (kTargetWorkgroups + units - 1) / units;
     p = (pages + splits - 1) / splits;
-    if (p > kMaxSplitPages) p = kMaxSplitPages;
+    if (p > kMaxSplitPages) {
+      // a whole multiple of the base split count, so that the grid stays a
+      // whole number of rounds of kTargetWorkgroups (a few workgroups past a
+      // round would cost a whole extra round)
+      splits *= (p + kMaxSplitPages - 1) / kMaxSplitPages;
+      p = (pages + splits - 1) / splits;
+    }
     if (p < flint::kShortMinPages) p = flint::kShortMinPages;
   }
   if (p > pages) p = pages;
