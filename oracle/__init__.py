@@ -36,13 +36,26 @@ def build(force: bool = True) -> str:
 class Layer(C.Structure):
     _fields_ = [("hq", C.c_int), ("hkv", C.c_int), ("d", C.c_int), ("bs", C.c_int),
                 ("window", C.c_int), ("use_rope", C.c_int), ("theta", C.c_double),
-                ("eps", C.c_double), ("scale", C.c_double)]
+                ("eps", C.c_double), ("scale", C.c_double), ("kv_fp8", C.c_int),
+                ("k_scale", C.c_double), ("v_scale", C.c_double)]
 
 
 def layer(window: int = 0, use_rope: int = 0, hq: int = 32, hkv: int = 4, d: int = 128,
-          bs: int = 16, theta: float = 10000.0, eps: float = 1e-6, scale: float | None = None):
+          bs: int = 16, theta: float = 10000.0, eps: float = 1e-6, scale: float | None = None,
+          kv_fp8: int = 0, k_scale: float = 1.0, v_scale: float = 1.0):
+    """kv_fp8 = 1: the caches hold fp8 E4M3 codes (uint8) of K / k_scale and
+    V / v_scale; otherwise bf16 codes (uint16)."""
     return Layer(hq, hkv, d, bs, window, use_rope, theta, eps,
-                 (1.0 / np.sqrt(d)) if scale is None else scale)
+                 (1.0 / np.sqrt(d)) if scale is None else scale, kv_fp8, k_scale, v_scale)
+
+
+def cache_dtype(L: Layer):
+    return np.uint8 if L.kv_fp8 else np.uint16
+
+
+def _cache(L: Layer, a):
+    assert a.dtype == cache_dtype(L) and a.flags.c_contiguous, "cache dtype/layout"
+    return a
 
 
 _lib = None
@@ -60,6 +73,10 @@ def lib():
         L.orc_bf16_value.restype = C.c_double
         L.orc_bf16_value.argtypes = [C.c_uint16]
         L.orc_bf16_rne_array.argtypes = [P, P, C.c_int64]
+        L.orc_fp8_rne.restype = C.c_uint8
+        L.orc_fp8_rne.argtypes = [C.c_double]
+        L.orc_fp8_value.restype = C.c_double
+        L.orc_fp8_value.argtypes = [C.c_uint8]
         L.orc_rmsnorm.argtypes = [P, P, C.c_int, C.c_double, P]
         L.orc_rope.argtypes = [P, C.c_int, C.c_double, C.c_double]
         L.orc_slot.restype = C.c_int64
@@ -129,7 +146,8 @@ def rope(x, pos, theta=10000.0) -> np.ndarray:
 # --- O4 ----------------------------------------------------------------------
 def append(L: Layer, q_in, k_in, v_in, qw, kw, positions, slots, k_cache, v_cache,
            want_q=True):
-    """Apply O4 for T tokens; the caches (uint16 arrays) are updated in place.
+    """Apply O4 for T tokens; the caches (uint16 bf16 codes, or uint8 fp8 codes
+    for an fp8 layer) are updated in place.
     Returns q_out [T, hq, d] fp64 (or None)."""
     q_in = _c(q_in, np.float32)
     k_in = _c(k_in, np.float32)
@@ -137,8 +155,8 @@ def append(L: Layer, q_in, k_in, v_in, qw, kw, positions, slots, k_cache, v_cach
     T = k_in.shape[0]
     positions = _c(positions, np.int32)
     slots = _c(slots, np.int32)
-    assert k_cache.dtype == np.uint16 and k_cache.flags.c_contiguous
-    assert v_cache.dtype == np.uint16 and v_cache.flags.c_contiguous
+    _cache(L, k_cache)
+    _cache(L, v_cache)
     num_blocks = k_cache.size // (L.hkv * L.bs * L.d)
     q_out = np.empty((T, L.hq, L.d), dtype=np.float64) if want_q else None
     rc = lib().orc_append(C.byref(L), T, _p(q_in), _p(k_in), _p(v_in), _p(_c(qw, np.float32)),
@@ -158,7 +176,8 @@ def attn_decode(L: Layer, q, k_cache, v_cache, block_tables, seq_lens, sinks, nt
     sk = _c(sinks, np.float32)
     num_blocks = k_cache.size // (L.hkv * L.bs * L.d)
     out = np.empty((B, L.hq, L.d), dtype=np.float64)
-    rc = lib().orc_attn_decode(C.byref(L), B, _p(q), _p(k_cache), _p(v_cache), num_blocks,
+    rc = lib().orc_attn_decode(C.byref(L), B, _p(q), _p(_cache(L, k_cache)),
+                               _p(_cache(L, v_cache)), num_blocks,
                                _p(bt), bt.shape[1], _p(sl), _p(sk), _p(out), int(nthreads))
     if rc != 0:
         raise ValueError("oracle decode: bad page id or seq_len")
@@ -171,7 +190,8 @@ def attn_partial(L: Layer, q_h, h, k_cache, v_cache, block_tables, b, j0, j1):
     bt = _c(block_tables, np.int32)
     ot = np.empty(L.d, dtype=np.float64)
     lse = np.zeros(1, dtype=np.float64)
-    lib().orc_attn_partial(C.byref(L), _p(q_h), int(h), _p(k_cache), _p(v_cache), _p(bt),
+    lib().orc_attn_partial(C.byref(L), _p(q_h), int(h), _p(_cache(L, k_cache)),
+                           _p(_cache(L, v_cache)), _p(bt),
                            bt.shape[1], int(b), int(j0), int(j1), _p(ot), _p(lse))
     return ot, float(lse[0])
 
@@ -198,12 +218,27 @@ def attn_prefill(L: Layer, q, cu_q_lens, k_cache, v_cache, block_tables, seq_len
     num_blocks = k_cache.size // (L.hkv * L.bs * L.d)
     out = np.full(q.shape, np.nan, dtype=np.float64)
     r = None if rows is None else _c(rows, np.int32)
-    rc = lib().orc_attn_prefill(C.byref(L), B, _p(q), _p(cu), _p(k_cache), _p(v_cache),
+    rc = lib().orc_attn_prefill(C.byref(L), B, _p(q), _p(cu), _p(_cache(L, k_cache)),
+                                _p(_cache(L, v_cache)),
                                 num_blocks, _p(bt), bt.shape[1], _p(sl), _p(sk), _p(out), _p(r),
                                 0 if r is None else r.shape[0], int(nthreads))
     if rc != 0:
         raise ValueError("oracle prefill: bad row, page id or seq_len")
     return out
+
+
+# --- fp8 E4M3 ------------------------------------------------------------------
+def fp8_rne(x) -> np.ndarray:
+    """fp8 E4M3 codes of reals (nearest, ties to even, saturating at 448)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = lib().orc_fp8_rne
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def fp8_value(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.uint8)
+    f = lib().orc_fp8_value
+    return np.array([f(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
 
 
 # --- O8 / footprint -----------------------------------------------------------

@@ -75,6 +75,49 @@ __attribute__((constructor)) static void init_table(void) {
 static inline double bf(uint16_t b) { return g_bf16[b]; }
 
 /* ------------------------------------------------------------------------ */
+/* fp8 E4M3 by its definition: code c (0..126 for the finite magnitudes) is
+ * m/8 * 2^-6 for exponent field 0 and (1 + m/8) * 2^(e-7) otherwise. */
+static double fp8_mag(int c) {
+  const int e = c >> 3, m = c & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+double orc_fp8_value(uint8_t c) {
+  if ((c & 0x7F) == 0x7F) return NAN;
+  const double v = fp8_mag(c & 0x7F);
+  return (c & 0x80) ? -v : v;
+}
+
+uint8_t orc_fp8_rne(double x) {
+  const uint8_t s = signbit(x) ? 0x80 : 0;
+  if (isnan(x)) return s | 0x7F;
+  const double a = fabs(x);
+  if (a >= 448.0) return s | 0x7E; /* saturate to the largest finite value */
+  /* codes 0..0x7E grow with their value: bracket a as mag(lo) <= a < mag(hi) */
+  int lo = 0, hi = 0x7E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (fp8_mag(mid) <= a) lo = mid; else hi = mid;
+  }
+  const double dl = a - fp8_mag(lo), dh = fp8_mag(hi) - a;
+  const int c = dl < dh ? lo : (dh < dl ? hi : ((lo & 1) ? hi : lo));
+  return (uint8_t)(s | c);
+}
+
+static double g_fp8[256];
+__attribute__((constructor)) static void init_fp8_table(void) {
+  for (int c = 0; c < 256; ++c) g_fp8[c] = orc_fp8_value((uint8_t)c);
+}
+
+/* element i of the K (resp. V) cache as a real number */
+static inline double k_at(const orc_layer* L, const void* kc, int64_t i) {
+  return L->kv_fp8 ? g_fp8[((const uint8_t*)kc)[i]] * L->k_scale : bf(((const uint16_t*)kc)[i]);
+}
+static inline double v_at(const orc_layer* L, const void* vc, int64_t i) {
+  return L->kv_fp8 ? g_fp8[((const uint8_t*)vc)[i]] * L->v_scale : bf(((const uint16_t*)vc)[i]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* O2: per-head RMSNorm (hnkhoi "Model architecture": per-head Q/K RMSNorm). */
 void orc_rmsnorm(const float* x, const float* w, int n, double eps, double* y) {
   double ss = 0.0;
@@ -118,7 +161,7 @@ static inline int64_t v_index(const orc_layer* L, int64_t page, int g, int row) 
 int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
                const float* v_in, const float* qw, const float* kw,
                const int32_t* positions, const int32_t* slots,
-               double* q_out, uint16_t* kc, uint16_t* vc, int num_blocks) {
+               double* q_out, void* kc, void* vc, int num_blocks) {
   const int d = L->d;
   double* tmp = (double*)malloc(sizeof(double) * d);
   int rc = 0;
@@ -139,12 +182,16 @@ int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
     for (int g = 0; g < L->hkv; ++g) {
       orc_rmsnorm(k_in + ((int64_t)t * L->hkv + g) * d, kw, d, L->eps, tmp);
       if (L->use_rope) orc_rope(tmp, d, pos, L->theta);
-      uint16_t* krow = kc + k_index(L, page, g, row);
-      uint16_t* vrow = vc + v_index(L, page, g, row);
+      const int64_t kr = k_index(L, page, g, row), vr = v_index(L, page, g, row);
       const float* v = v_in + ((int64_t)t * L->hkv + g) * d;
       for (int i = 0; i < d; ++i) {
-        krow[i] = bf16_rne_double(tmp[i]);
-        vrow[(int64_t)i * L->bs] = orc_bf16_rne(v[i]);
+        if (L->kv_fp8) {
+          ((uint8_t*)kc)[kr + i] = orc_fp8_rne(tmp[i] / L->k_scale);
+          ((uint8_t*)vc)[vr + (int64_t)i * L->bs] = orc_fp8_rne((double)v[i] / L->v_scale);
+        } else {
+          ((uint16_t*)kc)[kr + i] = bf16_rne_double(tmp[i]);
+          ((uint16_t*)vc)[vr + (int64_t)i * L->bs] = orc_bf16_rne(v[i]);
+        }
       }
     }
   }
@@ -158,8 +205,8 @@ int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
  * scalar logit per query head that joins the softmax denominator, is not
  * multiplied by the softmax scale and carries no value.
  * Keys: lo..t with lo = 0 (full layers) or max(0, t-window+1) (sliding). */
-static int attend_row(const orc_layer* L, const double* qh, int h, const uint16_t* kc,
-                      const uint16_t* vc, int num_blocks, const int32_t* bt, int bt_stride,
+static int attend_row(const orc_layer* L, const double* qh, int h, const void* kc,
+                      const void* vc, int num_blocks, const int32_t* bt, int bt_stride,
                       int b, int t, double sink, double* out) {
   const int d = L->d, g = h / (L->hq / L->hkv);
   int lo = (L->window > 0) ? t - L->window + 1 : 0;
@@ -174,7 +221,7 @@ static int attend_row(const orc_layer* L, const double* qh, int h, const uint16_
     int64_t r = k_index(L, page, g, j % L->bs);
     rows[j - lo] = v_index(L, page, g, j % L->bs);
     double dot = 0.0;
-    for (int i = 0; i < d; ++i) dot += qh[i] * bf(kc[r + i]);
+    for (int i = 0; i < d; ++i) dot += qh[i] * k_at(L, kc, r + i);
     s[j - lo] = L->scale * dot;
     if (s[j - lo] > m) m = s[j - lo];
   }
@@ -183,7 +230,7 @@ static int attend_row(const orc_layer* L, const double* qh, int h, const uint16_
   for (int j = 0; j < n; ++j) {
     double e = exp(s[j] - m);
     z += e;
-    for (int i = 0; i < d; ++i) out[i] += e * bf(vc[rows[j] + (int64_t)i * L->bs]);
+    for (int i = 0; i < d; ++i) out[i] += e * v_at(L, vc, rows[j] + (int64_t)i * L->bs);
   }
   for (int i = 0; i < d; ++i) out[i] /= z;
   free(s);
@@ -199,8 +246,8 @@ int orc_default_threads(void) {
 #endif
 }
 
-int orc_attn_decode(const orc_layer* L, int B, const double* q, const uint16_t* kc,
-                    const uint16_t* vc, int num_blocks, const int32_t* bt, int bt_stride,
+int orc_attn_decode(const orc_layer* L, int B, const double* q, const void* kc,
+                    const void* vc, int num_blocks, const int32_t* bt, int bt_stride,
                     const int32_t* seq_lens, const float* sinks, double* out, int nthreads) {
   if (nthreads <= 0) nthreads = orc_default_threads();
   int bad = 0;
@@ -220,8 +267,8 @@ int orc_attn_decode(const orc_layer* L, int B, const double* q, const uint16_t* 
 
 /* ------------------------------------------------------------------------ */
 /* O6: partial softmax over a key range and the log-sum-exp merge. */
-void orc_attn_partial(const orc_layer* L, const double* qh, int h, const uint16_t* kc,
-                      const uint16_t* vc, const int32_t* bt, int bt_stride, int b,
+void orc_attn_partial(const orc_layer* L, const double* qh, int h, const void* kc,
+                      const void* vc, const int32_t* bt, int bt_stride, int b,
                       int j0, int j1, double* ot, double* lse) {
   const int d = L->d, g = h / (L->hq / L->hkv);
   for (int i = 0; i < d; ++i) ot[i] = 0.0;
@@ -232,7 +279,7 @@ void orc_attn_partial(const orc_layer* L, const double* qh, int h, const uint16_
   for (int j = j0; j < j1; ++j) {
     int64_t r = k_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
     double dot = 0.0;
-    for (int i = 0; i < d; ++i) dot += qh[i] * bf(kc[r + i]);
+    for (int i = 0; i < d; ++i) dot += qh[i] * k_at(L, kc, r + i);
     s[j - j0] = L->scale * dot;
     if (s[j - j0] > m) m = s[j - j0];
   }
@@ -241,7 +288,7 @@ void orc_attn_partial(const orc_layer* L, const double* qh, int h, const uint16_
     int64_t r = v_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
     double e = exp(s[j - j0] - m);
     l += e;
-    for (int i = 0; i < d; ++i) ot[i] += e * bf(vc[r + (int64_t)i * L->bs]);
+    for (int i = 0; i < d; ++i) ot[i] += e * v_at(L, vc, r + (int64_t)i * L->bs);
   }
   for (int i = 0; i < d; ++i) ot[i] /= l;
   *lse = m + log(l);
@@ -265,7 +312,7 @@ void orc_merge(int S, int d, const double* ot, const double* lse, double sink, d
 /* ------------------------------------------------------------------------ */
 /* O7: prefill = O5 for every query row at its own position. */
 int orc_attn_prefill(const orc_layer* L, int B, const double* q, const int32_t* cu,
-                     const uint16_t* kc, const uint16_t* vc, int num_blocks,
+                     const void* kc, const void* vc, int num_blocks,
                      const int32_t* bt, int bt_stride, const int32_t* seq_lens,
                      const float* sinks, double* out, const int32_t* rows, int nrows,
                      int nthreads) {

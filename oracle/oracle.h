@@ -44,6 +44,9 @@ typedef struct {
   double theta;   /* RoPE base (10000)                                  */
   double eps;     /* RMSNorm epsilon (1e-6)                              */
   double scale;   /* softmax scale (1/sqrt(d))                           */
+  int kv_fp8;     /* 0: bf16 cache elements; 1: fp8 E4M3 (x / scale)     */
+  double k_scale; /* fp8 cache: K element = code value * k_scale         */
+  double v_scale; /* fp8 cache: V element = code value * v_scale         */
 } orc_layer;
 
 /* O1: fp32 -> bf16 by round-to-nearest-even, chosen between the two
@@ -52,6 +55,14 @@ uint16_t orc_bf16_rne(float x);
 double orc_bf16_value(uint16_t b);
 /* O1 applied to n reals (rounds each fp64 value once, no fp32 step). */
 void orc_bf16_rne_array(const double* x, uint16_t* y, int64_t n);
+
+/* fp8 E4M3 (the "fp8" column of the models JSON "kvCacheGiBPerRequest";
+ * reading: the OCP E4M3 format -- 1 sign, 4 exponent bits of bias 7, 3
+ * mantissa bits, subnormals, no infinities, S.1111.111 is NaN, largest
+ * finite value 448).  Round to nearest, ties to the even code, |x| > 448
+ * saturates to +-448, NaN stays NaN. */
+uint8_t orc_fp8_rne(double x);
+double orc_fp8_value(uint8_t c);
 
 /* O2: per-head RMSNorm: y = x / sqrt(mean(x^2) + eps) * w, n values. */
 void orc_rmsnorm(const float* x, const float* w, int n, double eps, double* y);
@@ -64,13 +75,15 @@ void orc_rope(double* x, int d, double pos, double theta);
 int64_t orc_slot(const int32_t* block_tables, int bt_stride, int bs, int b, int pos);
 
 /* O4: per token t: q_out[t] = rope?(rmsnorm(q_in[t], qw)) for every q head;
- * K row at slot_mapping[t] = bf16(rope?(rmsnorm(k_in[t], kw))), V row = bf16(v_in[t]).
+ * K row at slot_mapping[t] = bf16(rope?(rmsnorm(k_in[t], kw))), V row = bf16(v_in[t])
+ * (fp8 cache: fp8(K / k_scale) and fp8(v_in[t] / v_scale), each rounded once).
+ * Caches are uint16 bf16 codes or (kv_fp8) uint8 fp8 codes in the same layout.
  * slot < 0 skips the cache write for that token.  q_out may be NULL.
  * Returns 0, or -1 on a slot outside [0, num_blocks*bs). */
 int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
                const float* v_in, const float* qw, const float* kw,
                const int32_t* positions, const int32_t* slot_mapping,
-               double* q_out, uint16_t* k_cache, uint16_t* v_cache, int num_blocks);
+               double* q_out, void* k_cache, void* v_cache, int num_blocks);
 
 /* O5: one query of request b (absolute position t = seq_lens[b]-1) for every
  * q head, keys lo..t read through the page table; the sink of head h is an
@@ -78,7 +91,7 @@ int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
  * q: [B][hq][d] doubles; out: [B][hq][d].  Work is spread over nthreads
  * (<=0: all cores).  Returns 0, or -1 on a page id outside [0, num_blocks). */
 int orc_attn_decode(const orc_layer* L, int B, const double* q,
-                    const uint16_t* k_cache, const uint16_t* v_cache, int num_blocks,
+                    const void* k_cache, const void* v_cache, int num_blocks,
                     const int32_t* block_tables, int bt_stride, const int32_t* seq_lens,
                     const float* sinks, double* out, int nthreads);
 
@@ -86,7 +99,7 @@ int orc_attn_decode(const orc_layer* L, int B, const double* q,
  * o_tilde[d] and lse = m + ln(sum exp(s_j - m)); an empty range gives
  * lse = -inf and o_tilde = 0. */
 void orc_attn_partial(const orc_layer* L, const double* q_h, int h,
-                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, int bt_stride, int b,
                       int j0, int j1, double* o_tilde, double* lse);
 
@@ -99,7 +112,7 @@ void orc_merge(int S, int d, const double* o_tildes, const double* lses,
  * q: [total_q][hq][d]; out: [total_q][hq][d].  If rows != NULL only those
  * global rows are computed (others untouched).  Returns 0 or -1. */
 int orc_attn_prefill(const orc_layer* L, int B, const double* q, const int32_t* cu_q_lens,
-                     const uint16_t* k_cache, const uint16_t* v_cache, int num_blocks,
+                     const void* k_cache, const void* v_cache, int num_blocks,
                      const int32_t* block_tables, int bt_stride, const int32_t* seq_lens,
                      const float* sinks, double* out, const int32_t* rows, int nrows,
                      int nthreads);

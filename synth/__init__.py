@@ -17,6 +17,9 @@ GQA with 32 query and 4 KV heads of dim 128, bf16 KV, learned sinks):
                            (a way to draw bf16 values; not the method's rounding);
                            multi-GB caches use torch's generator on the GPU
                            (normal_bf16_bits_torch) instead of PCG64
+  * fp8 cache contents     uniform random E4M3 codes: a random sign and a
+                           magnitude code uniform in [0, max_code] (default
+                           0x3F, |x| < 2), so no NaN code is ever drawn
   * page tables            a seeded permutation of the physical pages
   * ragged lengths         uniform integers in [lo, hi], inclusive
 """
@@ -58,6 +61,25 @@ def normal_bf16_bits_torch(seed: int, stream: tuple, shape, device="cpu"):
     g.manual_seed(torch_seed(seed, stream))
     x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
     return (x.view(torch.int32) >> 16).to(torch.int16)
+
+
+def fp8_codes(seed: int, stream: tuple, shape, max_code: int = 0x3F) -> np.ndarray:
+    """uint8 fp8 E4M3 codes: a random sign bit over a magnitude code uniform in
+    [0, max_code]; max_code < 0x7F keeps the NaN codes out."""
+    r = rng(seed, *stream)
+    mag = r.integers(0, max_code, size=shape, endpoint=True).astype(np.uint8)
+    sign = (r.integers(0, 1, size=shape, endpoint=True).astype(np.uint8) << np.uint8(7))
+    return mag | sign
+
+
+def fp8_codes_torch(seed: int, stream: tuple, shape, device="cpu", max_code: int = 0x3F):
+    """Like fp8_codes, drawn by torch's generator on `device`; uint8 tensor."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(seed, stream))
+    mag = torch.randint(0, max_code + 1, tuple(shape), generator=g, dtype=torch.uint8, device=device)
+    sign = torch.randint(0, 2, tuple(shape), generator=g, dtype=torch.uint8, device=device)
+    return mag | (sign << 7)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

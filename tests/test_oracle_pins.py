@@ -505,3 +505,130 @@ def test_kv_calculator_table():
         for fmt, eb in (("bf16", 2), ("fp8", 1)):
             gib = oracle.kv_bytes_per_request(row["context"], elem_bytes=eb) / 2**30
             assert round(gib, 3) == pytest.approx(row[fmt], abs=1e-9), (row, fmt, gib)
+
+
+# ---------------------------------------------------------------------------
+# fp8 E4M3 KV cache (OCP 8-bit floating point: E4M3, bias 7, no infinities,
+# S.1111.111 is NaN, largest finite 448)
+# ---------------------------------------------------------------------------
+
+def _torch_fp8_values(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _torch_fp8_codes(x32):
+    return torch.from_numpy(np.asarray(x32, np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+
+
+def test_fp8_value_of_every_code_matches_torch():
+    codes = np.arange(256)
+    got, ref = oracle.fp8_value(codes), _torch_fp8_values(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    # and the format's landmarks, from its definition
+    assert oracle.fp8_value(0x7E) == 448.0 and oracle.fp8_value(0x08) == 2.0**-6
+    assert oracle.fp8_value(0x01) == 2.0**-9 and oracle.fp8_value(0x38) == 1.0
+    assert oracle.fp8_value(0xC0) == -2.0
+
+
+def test_fp8_rounding_matches_torch_below_overflow():
+    # nearest with ties to even; inputs are fp32 so torch rounds the same real.
+    # Below the overflow threshold torch and the saturating reading agree.
+    mags = oracle.fp8_value(np.arange(0x7F))                 # 0 .. 448, increasing
+    mids = (mags[:-1] + mags[1:]) / 2                         # every tie, exact in fp32
+    nudged = np.concatenate([np.nextafter(mids.astype(np.float32), np.float32(0)),
+                             np.nextafter(mids.astype(np.float32), np.float32(1e9))])
+    rnd = synth.normal(40, (1,), 4000) * np.exp2(synth.rng(40, 2).random(4000) * 18 - 12)
+    x = np.concatenate([mags, mids, nudged, rnd, [2.0**-11, 2.0**-10, 3 * 2.0**-10, 1e-30]])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    x = x[np.abs(x) < 448]
+    assert np.array_equal(oracle.fp8_rne(x.astype(np.float64)), _torch_fp8_codes(x))
+
+
+def test_fp8_ties_go_to_even_code():
+    # 1 + 1/16 lies halfway between 1 (code 0x38) and 1.125 (0x39): even wins;
+    # 1 + 3/16 lies between 0x39 and 0x3A: again the even code
+    assert oracle.fp8_rne([1.0625, 1.1875, -1.0625]).tolist() == [0x38, 0x3A, 0xB8]
+    # subnormal tie: 2^-10 is halfway between 0 and 2^-9
+    assert oracle.fp8_rne([2.0**-10, 3 * 2.0**-10]).tolist() == [0x00, 0x02]
+
+
+def test_fp8_saturates_and_keeps_nan():
+    big = [448.0, 449.0, 464.0, 480.0, 1e6, 1e300, np.inf]
+    assert (oracle.fp8_rne(big) == 0x7E).all()
+    assert (oracle.fp8_rne(np.negative(big)) == 0xFE).all()
+    assert (oracle.fp8_rne([np.nan]) & 0x7F == 0x7F).all()
+
+
+def _fp8_layer(**kw):
+    return oracle.layer(kv_fp8=1, **kw)
+
+
+def test_fp8_append_places_scaled_codes():
+    # V codes are the rounding of v / v_scale (fp32 inputs: torch rounds the
+    # same real when v_scale is a power of two); K codes are within one code of
+    # torch's rounding of the fp32 image of the normed, rotated row / k_scale
+    L = _fp8_layer(window=513, use_rope=1, k_scale=0.25, v_scale=2.0)
+    T, nb = 24, 6
+    bt = synth.permutation(41, (1,), nb)[None, :]
+    pos = np.arange(7, 7 + T, dtype=np.int32)
+    slots = np.array([oracle.slot(bt, 0, p) for p in pos], np.int32)
+    slots[3] = -1
+    q = synth.normal(41, (2,), (T, 32, 128))
+    k = synth.normal(41, (3,), (T, 4, 128))
+    v = synth.normal(41, (4,), (T, 4, 128)) * 50.0
+    ones = np.ones(128, np.float32)
+    kc = np.full((nb, 4, 16, 128), 0x5A, np.uint8)
+    vc = np.full((nb, 4, 128, 16), 0x5A, np.uint8)
+    oracle.append(L, q, k, v, ones, ones, pos, slots, kc, vc)
+    written = np.zeros((nb, 16), bool)
+    for t in range(T):
+        if slots[t] < 0:
+            continue
+        pg, r = divmod(int(slots[t]), 16)
+        written[pg, r] = True
+        assert np.array_equal(vc[pg, :, :, r], _torch_fp8_codes(v[t] / np.float32(2.0)))
+        for g in range(4):
+            kk = oracle.rope(oracle.rmsnorm(k[t, g], ones), pos[t]) / 0.25
+            ref = _torch_fp8_values(_torch_fp8_codes(kk.astype(np.float32)))
+            got = oracle.fp8_value(kc[pg, g, r])
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0**-6))) - 3)
+            assert np.all(np.abs(got - ref) <= ulp)
+    assert np.all(kc.transpose(0, 2, 1, 3)[~written] == 0x5A)
+    assert np.all(vc.transpose(0, 3, 1, 2)[~written] == 0x5A)
+    # values beyond 448 * v_scale saturate instead of turning into NaN
+    v2 = np.full((1, 4, 128), 2000.0, np.float32)
+    oracle.append(L, q[:1], k[:1], v2, ones, ones, pos[:1], slots[:1], kc, vc)
+    pg, r = divmod(int(slots[0]), 16)
+    assert (vc[pg, :, :, r] == 0x7E).all()
+
+
+def test_fp8_attention_is_bf16_attention_of_the_dequantised_cache():
+    # attention over fp8 codes with scales equals attention over a bf16 cache
+    # holding code value x scale (exact in bf16 for power-of-two scales),
+    # which the brute-force pins above tie to the definition
+    for window in (0, 5):
+        L8 = _fp8_layer(window=window, hq=4, hkv=2, d=8, bs=4, k_scale=0.5, v_scale=4.0)
+        L16 = _small_layer(window)
+        n = 11
+        kcode = synth.fp8_codes(42, (1, window), (n, L8.hkv, L8.d))          # |k| < 2
+        vcode = synth.fp8_codes(42, (2, window), (n, L8.hkv, L8.d), 0x7E)    # all finite codes
+        kb = _torch_bf16_bits(oracle.fp8_value(kcode) * 0.5)
+        vb = _torch_bf16_bits(oracle.fp8_value(vcode) * 4.0)
+        q = synth.normal(42, (3, window), (L8.hq, L8.d)).astype(np.float64)
+        sinks = synth.normal(42, (4, window), L8.hq)
+        kc16, vc16, bt = _paged(L16, kb, vb, seed=9)
+        kc8 = np.zeros(kc16.shape, np.uint8)
+        vc8 = np.zeros(vc16.shape, np.uint8)
+        for p in range(n):
+            pg, r = bt[0, p // 4], p % 4
+            kc8[pg, :, r, :] = kcode[p]
+            vc8[pg, :, :, r] = vcode[p]
+        sl = np.array([n], np.int32)
+        out8 = oracle.attn_decode(L8, q[None], kc8, vc8, bt, sl, sinks)[0]
+        out16 = oracle.attn_decode(L16, q[None], kc16, vc16, bt, sl, sinks)[0]
+        assert np.array_equal(out8, out16)
+        ref = _brute(L16, q, kb, vb, n - 1, sinks)
+        assert np.max(np.abs(out8 - ref)) < 1e-13 * max(1.0, np.abs(ref).max())
