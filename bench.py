@@ -114,6 +114,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times (the "
                          "known-size kernel that calibrates HBM byte counters) and exit")
@@ -304,12 +305,82 @@ def main():
                    "vLLM): 2.06 ms/token ~ 485 tok/s at bs1, 100K ctx; not this metric",
     }
 
+    if not args.no_fp8:
+        result["fp8"] = bench_fp8(fl, dev, layers, ws, ones, seq_lens, capture, time_graph,
+                                  args.steps, stream, eps)
+
     if not args.no_prefill:
         result["prefill"] = bench_prefill(fl, dev, stream)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_max_abs_err"] = cpu_baseline(layers, eps)
     print(json.dumps(result), flush=True)
+
+
+FP8_SCALES = (1.0 / 16, 0.5)
+
+
+def bench_fp8(fl, dev, layers, ws, ones, seq_lens, capture, time_graph, steps, stream, eps):
+    """The same 49-layer step over an fp8 E4M3 KV cache (the pages' fp8
+    KV-cache format; 14 KiB per token): fused step graph and the full-layer
+    split kernel alone.  Cache codes are drawn uniformly over the E4M3 codes
+    below 2.0 (a random sign, no NaN codes); the bf16 leg's q/k/v, tables and
+    sinks are reused."""
+    import torch
+    ks, vs = FP8_SCALES
+    FULL8 = fl.layer(window=0, use_rope=0, rms_eps=eps, kv_dtype=fl.FLINT_KV_FP8_E4M3,
+                     k_scale=ks, v_scale=vs)
+    SLIDE8 = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps, kv_dtype=fl.FLINT_KV_FP8_E4M3,
+                      k_scale=ks, v_scale=vs)
+    l8 = []
+    for l, L in enumerate(layers):
+        nb = L["kc"].shape[0]
+        l8.append(dict(L, kc=synth.fp8_codes_torch(SEED, (3, l, synth.KC), (nb, HKV, PAGE, D), dev),
+                       vc=synth.fp8_codes_torch(SEED, (3, l, synth.VC), (nb, HKV, D, PAGE), dev),
+                       out=torch.empty((1, HQ, D), dtype=torch.float32, device=dev)))
+
+    def step8():
+        for L in l8:
+            fl.flint_attn_decode_step(FULL8 if L["full"] else SLIDE8, L["q_in"], L["k_in"],
+                                      L["v_in"], ones, ones, L["slots"], L["kc"], L["vc"],
+                                      L["bt"], seq_lens, CTX, L["sinks"], L["out"], workspace=ws)
+
+    step8()
+    torch.cuda.synchronize()
+    assert all(bool(torch.isfinite(L["out"]).all()) for L in l8), "fp8 step output not finite"
+    g8 = capture(step8)
+    for _ in range(5):
+        g8.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(steps):
+            g8.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us_step = e0.elapsed_time(e1) * 1e3 / steps
+    full8 = [L for L in l8 if L["full"]]
+    pps, nsplit = fl.flint_attn_decode_plan(FULL8, 1, CTX)
+    part_o = torch.empty((1, nsplit, HQ, D), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((1, nsplit, HQ), dtype=torch.float32, device=dev)
+    us_k2 = time_graph(lambda: [fl.flint_attn_decode_partials(
+        FULL8, L["q_out"], L["kc"], L["vc"], L["bt"], seq_lens, CTX, pps, part_o, part_lse)
+        for L in full8])
+    kv8 = CTX * KV_BYTES_PER_TOKEN_LAYER // 2
+    k2_bytes = kv8 + HQ * D * 4 + (-(-CTX // PAGE)) * 4
+    achieved = k2_bytes / (us_k2 * 1e-6) / 1e9
+    kv_step = sum((CTX if L["full"] else WINDOW) * KV_BYTES_PER_TOKEN_LAYER // 2 for L in l8)
+    log(f"bench: fp8 cache {us_step:.1f} us/step, full-layer split kernel {us_k2:.2f} us "
+        f"({achieved:.0f} GB/s)")
+    res = {"us_per_step": round(us_step, 2), "k_scale": ks, "v_scale": vs,
+           "kv_bytes_per_step": kv_step,
+           "hbm_gbps": round(kv_step / (us_step * 1e-6) / 1e9, 1),
+           "split_kernel": {"us_per_launch": round(us_k2, 2), "bytes_per_launch": k2_bytes,
+                            "achieved": round(achieved, 1),
+                            "frac": round(achieved / HBM_PEAK_GBPS, 4)}}
+    del l8, g8
+    return res
 
 
 def copy_probe(dev):

@@ -9,7 +9,8 @@ Functions carry the C names of include/flint.h:
     flint_qk_norm_rope_append, flint_attn_decode, flint_attn_prefill,
     flint_attn_decode_step (append + decode fused into one launch),
 plus the size / plan queries.  bf16 tensors (K/V caches, prefill q) may be
-torch.bfloat16, torch.int16 or torch.uint16: only their bits are used.
+torch.bfloat16, torch.int16 or torch.uint16, and fp8 caches torch.uint8 or
+torch.float8_e4m3fn: only their bits are used.
 """
 from __future__ import annotations
 
@@ -37,15 +38,24 @@ class FlintAttnLayer(C.Structure):
     _fields_ = [("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
                 ("head_dim", C.c_int32), ("block_size", C.c_int32), ("window", C.c_int32),
                 ("use_rope", C.c_int32), ("rope_theta", C.c_float), ("rms_eps", C.c_float),
-                ("softmax_scale", C.c_float)]
+                ("softmax_scale", C.c_float), ("kv_dtype", C.c_int32), ("k_scale", C.c_float),
+                ("v_scale", C.c_float)]
+
+
+FLINT_KV_BF16 = 0
+FLINT_KV_FP8_E4M3 = 1
 
 
 def layer(window: int = 0, use_rope: int = 0, num_q_heads: int = 32, num_kv_heads: int = 4,
           head_dim: int = 128, block_size: int = 16, rope_theta: float = 10000.0,
-          rms_eps: float = 1e-6, softmax_scale: float | None = None) -> FlintAttnLayer:
+          rms_eps: float = 1e-6, softmax_scale: float | None = None,
+          kv_dtype: int = FLINT_KV_BF16, k_scale: float = 1.0,
+          v_scale: float = 1.0) -> FlintAttnLayer:
+    """kv_dtype FLINT_KV_FP8_E4M3: the caches hold fp8 codes of K / k_scale and
+    V / v_scale (uint8 or torch.float8_e4m3fn tensors)."""
     scale = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
     return FlintAttnLayer(num_q_heads, num_kv_heads, head_dim, block_size, window, use_rope,
-                          rope_theta, rms_eps, scale)
+                          rope_theta, rms_eps, scale, kv_dtype, k_scale, v_scale)
 
 
 def full_layer(**kw) -> FlintAttnLayer:
@@ -146,6 +156,14 @@ def _b16():
     return (torch.bfloat16, torch.int16, torch.uint16)
 
 
+def _kv(L):
+    """Accepted cache tensor dtypes for the layer's KV element format."""
+    torch = _torch()
+    if L.kv_dtype == FLINT_KV_FP8_E4M3:
+        return (torch.uint8, torch.float8_e4m3fn)
+    return _b16()
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -169,8 +187,8 @@ def flint_qk_norm_rope_append(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_n
         _ptr(v_in, _f32(), "v_in"), _ptr(q_norm_w, _f32(), "q_norm_w"),
         _ptr(k_norm_w, _f32(), "k_norm_w"), _ptr(positions, _i32(), "positions"),
         _ptr(slot_mapping, _i32(), "slot_mapping"), _ptr(q_f32, _f32(), "q_out"),
-        _ptr(q_b16, _b16(), "q_out"), _ptr(k_cache, _b16(), "k_cache"),
-        _ptr(v_cache, _b16(), "v_cache"), num_blocks, _stream(stream)))
+        _ptr(q_b16, _b16(), "q_out"), _ptr(k_cache, _kv(L), "k_cache"),
+        _ptr(v_cache, _kv(L), "v_cache"), num_blocks, _stream(stream)))
 
 
 def flint_attn_decode_workspace_size(L: FlintAttnLayer, num_seqs: int, max_seq_len: int,
@@ -202,8 +220,8 @@ def flint_attn_decode_partials(L: FlintAttnLayer, q, k_cache, v_cache, block_tab
     if part_lse is None:
         part_lse = torch.empty((B, S, L.num_q_heads), dtype=torch.float32, device=q.device)
     _check(lib().flint_attn_decode_partials(
-        C.byref(L), B, _ptr(q, _f32(), "q"), _ptr(k_cache, _b16(), "k_cache"),
-        _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        C.byref(L), B, _ptr(q, _f32(), "q"), _ptr(k_cache, _kv(L), "k_cache"),
+        _ptr(v_cache, _kv(L), "v_cache"), k_cache.shape[0],
         _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
         _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, pages_per_split, S,
         _ptr(part_o, _f32(), "part_o"), _ptr(part_lse, _f32(), "part_lse"), _stream(stream)))
@@ -236,8 +254,8 @@ def flint_attn_decode(L: FlintAttnLayer, q, k_cache, v_cache, block_tables, seq_
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().flint_attn_decode_ex(
-        C.byref(L), B, _ptr(q, _f32(), "q"), _ptr(k_cache, _b16(), "k_cache"),
-        _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        C.byref(L), B, _ptr(q, _f32(), "q"), _ptr(k_cache, _kv(L), "k_cache"),
+        _ptr(v_cache, _kv(L), "v_cache"), k_cache.shape[0],
         _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
         _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),
         _ptr(out, _f32(), "out"),
@@ -262,8 +280,8 @@ def flint_attn_decode_step(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_norm
         C.byref(L), B, _ptr(q_in, _f32(), "q_in"), _ptr(k_in, _f32(), "k_in"),
         _ptr(v_in, _f32(), "v_in"), _ptr(q_norm_w, _f32(), "q_norm_w"),
         _ptr(k_norm_w, _f32(), "k_norm_w"), _ptr(slot_mapping, _i32(), "slot_mapping"),
-        _ptr(q_out, _f32(), "q_out"), _ptr(k_cache, _b16(), "k_cache"),
-        _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        _ptr(q_out, _f32(), "q_out"), _ptr(k_cache, _kv(L), "k_cache"),
+        _ptr(v_cache, _kv(L), "v_cache"), k_cache.shape[0],
         _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
         _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),
         _ptr(out, _f32(), "out"), None if workspace is None else workspace.data_ptr(), ws_bytes,
@@ -290,7 +308,7 @@ def flint_attn_prefill(L: FlintAttnLayer, q, cu_q_lens, max_q_len: int, k_cache,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().flint_attn_prefill(
         C.byref(L), B, _ptr(q, _b16(), "q"), _ptr(cu_q_lens, _i32(), "cu_q_lens"), max_q_len,
-        _ptr(k_cache, _b16(), "k_cache"), _ptr(v_cache, _b16(), "v_cache"), k_cache.shape[0],
+        _ptr(k_cache, _kv(L), "k_cache"), _ptr(v_cache, _kv(L), "v_cache"), k_cache.shape[0],
         _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
         _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),
         _ptr(out, _f32(), "out"), None if workspace is None else workspace.data_ptr(), ws_bytes,

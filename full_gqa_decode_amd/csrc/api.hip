@@ -66,6 +66,12 @@ flint_status check_layer(const flint_attn_layer* L) {
     return fail(FLINT_ERR_INVALID_ARGUMENT, "rope_theta must be finite and > 0");
   if (!(L->rms_eps >= 0.f) || !std::isfinite(L->rms_eps))
     return fail(FLINT_ERR_INVALID_ARGUMENT, "rms_eps must be finite and >= 0");
+  if (L->kv_dtype != FLINT_KV_BF16 && L->kv_dtype != FLINT_KV_FP8_E4M3)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "kv_dtype %d (0 bf16, 1 fp8 e4m3)", L->kv_dtype);
+  if (L->kv_dtype == FLINT_KV_FP8_E4M3 &&
+      !(L->k_scale > 0.f && std::isfinite(L->k_scale) && L->v_scale > 0.f &&
+        std::isfinite(L->v_scale)))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "fp8 k_scale / v_scale must be finite and > 0");
   return FLINT_OK;
 }
 
@@ -163,7 +169,7 @@ flint_status flint_qk_norm_rope_append(const flint_attn_layer* L, int32_t num_to
                                        const float* q_norm_w, const float* k_norm_w,
                                        const int32_t* positions, const int32_t* slot_mapping,
                                        float* q_out_f32, uint16_t* q_out_bf16,
-                                       uint16_t* k_cache, uint16_t* v_cache, int32_t num_blocks,
+                                       void* k_cache, void* v_cache, int32_t num_blocks,
                                        void* stream) {
   flint_status st = check_layer(L);
   if (st != FLINT_OK) return st;
@@ -202,6 +208,9 @@ flint_status flint_qk_norm_rope_append(const flint_attn_layer* L, int32_t num_to
   a.use_rope = L->use_rope;
   a.rope_theta = L->rope_theta;
   a.rms_eps = L->rms_eps;
+  a.kv_fp8 = L->kv_dtype == FLINT_KV_FP8_E4M3;
+  a.k_scale = a.kv_fp8 ? L->k_scale : 1.f;
+  a.v_scale = a.kv_fp8 ? L->v_scale : 1.f;
   return hip_status(flint::launch_append(a, (hipStream_t)stream), "append launch");
 }
 
@@ -235,9 +244,18 @@ size_t flint_attn_decode_workspace_size(const flint_attn_layer* L, int32_t num_s
 
 namespace {
 
+// KV element format, the score scale in log2 units (an fp8 cache's k_scale
+// folded in) and the output scale.
+void set_kv_format(const flint_attn_layer* L, flint::DecodeArgs* a) {
+  a->kv_fp8 = L->kv_dtype == FLINT_KV_FP8_E4M3;
+  a->k_scale = a->kv_fp8 ? L->k_scale : 1.f;
+  a->v_scale = a->kv_fp8 ? L->v_scale : 1.f;
+  a->qscale = L->softmax_scale * 1.4426950408889634f * a->k_scale;
+}
+
 // Validation shared by the decode entry points; fills the launch arguments.
-flint_status prepare_decode(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* k_cache,
-                            const uint16_t* v_cache, int32_t num_blocks,
+flint_status prepare_decode(const flint_attn_layer* L, int32_t num_seqs, const void* k_cache,
+                            const void* v_cache, int32_t num_blocks,
                             const int32_t* block_tables, int32_t bt_stride,
                             const int32_t* seq_lens, int32_t max_seq_len, const float* sinks,
                             float* out, void* workspace, size_t workspace_bytes,
@@ -271,8 +289,8 @@ flint_status prepare_decode(const flint_attn_layer* L, int32_t num_seqs, const u
       return fail(FLINT_ERR_INVALID_ARGUMENT, "workspace must be %zu-byte aligned", kWsAlign);
   }
   *a = flint::DecodeArgs{};
-  a->k_cache = const_cast<uint16_t*>(k_cache);
-  a->v_cache = const_cast<uint16_t*>(v_cache);
+  a->k_cache = const_cast<void*>(k_cache);
+  a->v_cache = const_cast<void*>(v_cache);
   a->block_tables = block_tables;
   a->seq_lens = seq_lens;
   a->sinks = sinks;
@@ -288,7 +306,7 @@ flint_status prepare_decode(const flint_attn_layer* L, int32_t num_seqs, const u
   a->max_seq_len = max_seq_len;
   a->pages_per_split = pl.pages_per_split;
   a->num_splits = pl.num_splits;
-  a->qscale = L->softmax_scale * 1.4426950408889634f;
+  set_kv_format(L, a);
   a->use_rope = L->use_rope;
   a->rope_theta = L->rope_theta;
   a->rms_eps = L->rms_eps;
@@ -300,7 +318,7 @@ flint_status prepare_decode(const flint_attn_layer* L, int32_t num_seqs, const u
 extern "C" {
 
 flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, const float* q,
-                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const void* k_cache, const void* v_cache,
                                   int32_t num_blocks, const int32_t* block_tables,
                                   int32_t bt_stride, const int32_t* seq_lens,
                                   int32_t max_seq_len, const float* sinks, float* out,
@@ -324,7 +342,7 @@ flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
                                     const float* q_in, const float* k_in, const float* v_in,
                                     const float* q_norm_w, const float* k_norm_w,
                                     const int32_t* slot_mapping, float* q_out,
-                                    uint16_t* k_cache, uint16_t* v_cache, int32_t num_blocks,
+                                    void* k_cache, void* v_cache, int32_t num_blocks,
                                     const int32_t* block_tables, int32_t bt_stride,
                                     const int32_t* seq_lens, int32_t max_seq_len,
                                     const float* sinks, float* out, void* workspace,
@@ -354,7 +372,7 @@ flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
 }
 
 flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, const float* q,
-                               const uint16_t* k_cache, const uint16_t* v_cache,
+                               const void* k_cache, const void* v_cache,
                                int32_t num_blocks, const int32_t* block_tables,
                                int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
                                const float* sinks, float* out, void* workspace,
@@ -365,8 +383,8 @@ flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, cons
 }
 
 flint_status flint_attn_decode_partials(const flint_attn_layer* L, int32_t num_seqs,
-                                        const float* q, const uint16_t* k_cache,
-                                        const uint16_t* v_cache, int32_t num_blocks,
+                                        const float* q, const void* k_cache,
+                                        const void* v_cache, int32_t num_blocks,
                                         const int32_t* block_tables, int32_t bt_stride,
                                         const int32_t* seq_lens, int32_t max_seq_len,
                                         int32_t pages_per_split, int32_t num_splits,
@@ -397,8 +415,8 @@ flint_status flint_attn_decode_partials(const flint_attn_layer* L, int32_t num_s
     return fail(FLINT_ERR_INVALID_ARGUMENT, "misaligned pointer (q, caches, part_o need 16 B)");
   flint::DecodeArgs a{};
   a.q = q;
-  a.k_cache = const_cast<uint16_t*>(k_cache);
-  a.v_cache = const_cast<uint16_t*>(v_cache);
+  a.k_cache = const_cast<void*>(k_cache);
+  a.v_cache = const_cast<void*>(v_cache);
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.part_o = part_o;
@@ -412,7 +430,7 @@ flint_status flint_attn_decode_partials(const flint_attn_layer* L, int32_t num_s
   a.pages_per_split = pl.pages_per_split;
   a.num_splits = pl.num_splits;
   a.partials_only = 1;
-  a.qscale = L->softmax_scale * 1.4426950408889634f;
+  set_kv_format(L, &a);
   return hip_status(flint::launch_decode(a, (hipStream_t)stream), "partials launch");
 }
 
@@ -450,7 +468,7 @@ size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_
 
 flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* q,
                                 const int32_t* cu_q_lens, int32_t max_q_len,
-                                const uint16_t* k_cache, const uint16_t* v_cache,
+                                const void* k_cache, const void* v_cache,
                                 int32_t num_blocks, const int32_t* block_tables,
                                 int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
                                 const float* sinks, float* out, void* workspace,
@@ -459,6 +477,8 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
   (void)workspace_bytes;
   flint_status st = check_layer(L);
   if (st != FLINT_OK) return st;
+  if (L->kv_dtype != FLINT_KV_BF16)
+    return fail(FLINT_ERR_UNSUPPORTED, "prefill reads bf16 caches only");
   if (num_seqs < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
   if (max_seq_len < 1 || max_seq_len > kMaxContext)
     return fail(FLINT_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [1, %d]", max_seq_len,
@@ -479,8 +499,8 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
   flint::PrefillArgs a;
   a.q = q;
   a.cu_q_lens = cu_q_lens;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.sinks = sinks;

@@ -4,7 +4,8 @@
 // optimised path fuses normalisation, rotary-position and cache operations.
 // "Day-0 Support for Flint on vLLM" (hnkhoi.com), "Model architecture":
 // per-head Q/K RMSNorm; RoPE on the 35 sliding layers, none on the 14 full
-// layers.  Order: norm, then rotation, then the bf16 cache write.
+// layers.  Order: norm, then rotation, then the cache write (bf16, or fp8
+// E4M3 of the value over the layer's scale).
 //
 // One wave64 handles one head of one token: lane l holds dims l and l+64,
 // which is exactly a rotate-half RoPE pair, so the rotation needs no lane
@@ -14,7 +15,8 @@
 // fp32 q output is the correctly rounded normalised/rotated value, and the
 // bf16 K is rounded once from the fp64 value (round-to-odd to fp32, then
 // round-to-nearest-even to bf16), so it matches an exact computation except
-// on ties closer than ~1e-15 relative.
+// on ties closer than ~1e-15 relative; fp8 codes are rounded once from the
+// fp64 quotient.
 // Launch-latency bound at decode (one token per request); bandwidth bound for
 // long prefill chunks (~4.5 KB read and written per token for 32/4 heads).
 #include "device.h"
@@ -38,15 +40,22 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const bool bad = pos < 0 || (int64_t)slot >= (int64_t)a.num_blocks * kPage;
   const bool write_cache = slot >= 0 && !bad;
 
-  if (task >= hq + hkv) {  // V: round to bf16 and store dim-major
+  if (task >= hq + hkv) {  // V: round to bf16 (or fp8) and store dim-major
     if (!write_cache) return;
     const int g = task - hq - hkv;
     const float* x = a.v_in + ((int64_t)t * hkv + g) * kHeadDim;
     const float v0 = x[lane], v1 = x[lane + 64];
     const int64_t page = slot / kPage, row = slot % kPage;
-    uint16_t* dst = a.v_cache + (page * hkv + g) * (int64_t)(kHeadDim * kPage) + row;
-    dst[lane * kPage] = bf16_bits_rne(v0);
-    dst[(lane + 64) * kPage] = bf16_bits_rne(v1);
+    const int64_t o = (page * hkv + g) * (int64_t)(kHeadDim * kPage) + row;
+    if (a.kv_fp8) {
+      uint8_t* dst = (uint8_t*)a.v_cache + o;
+      dst[lane * kPage] = (uint8_t)fp8_e4m3_rne_f64((double)v0 / (double)a.v_scale);
+      dst[(lane + 64) * kPage] = (uint8_t)fp8_e4m3_rne_f64((double)v1 / (double)a.v_scale);
+    } else {
+      uint16_t* dst = (uint16_t*)a.v_cache + o;
+      dst[lane * kPage] = bf16_bits_rne(v0);
+      dst[(lane + 64) * kPage] = bf16_bits_rne(v1);
+    }
     return;
   }
 
@@ -77,9 +86,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   const int g = task - hq;
   const int64_t page = slot / kPage, row = slot % kPage;
-  uint16_t* dst = a.k_cache + ((page * hkv + g) * kPage + row) * kHeadDim;
-  dst[lane] = bf16_bits_rne_f64(y0);
-  dst[lane + 64] = bf16_bits_rne_f64(y1);
+  const int64_t o = ((page * hkv + g) * kPage + row) * kHeadDim;
+  if (a.kv_fp8) {
+    uint8_t* dst = (uint8_t*)a.k_cache + o;
+    dst[lane] = (uint8_t)fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
+    dst[lane + 64] = (uint8_t)fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
+  } else {
+    uint16_t* dst = (uint16_t*)a.k_cache + o;
+    dst[lane] = bf16_bits_rne_f64(y0);
+    dst[lane + 64] = bf16_bits_rne_f64(y1);
+  }
 }
 
 }  // namespace

@@ -37,6 +37,8 @@
 // into the cache and substitutes it in registers, so append and attention are
 // one launch.  Bound: HBM (8 KiB of K+V per page and KV head against ~20 VALU
 // and 12 MFMA instructions per wave).
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -56,7 +58,7 @@ struct PageRegs {
 __device__ __forceinline__ void load_k(const DecodeArgs& a, int pg, int g, int n, int gq,
                                        PageRegs& r) {
   const uint16_t* kp =
-      a.k_cache + (((int64_t)pg * a.num_kv_heads + g) * kPage + n) * kHeadDim + gq * 8;
+      (const uint16_t*)a.k_cache + (((int64_t)pg * a.num_kv_heads + g) * kPage + n) * kHeadDim + gq * 8;
 #pragma unroll
   for (int c = 0; c < 4; ++c) r.k[c] = __builtin_nontemporal_load((const bf16x8*)(kp + c * 32));
 }
@@ -64,10 +66,76 @@ __device__ __forceinline__ void load_k(const DecodeArgs& a, int pg, int g, int n
 __device__ __forceinline__ void load_v(const DecodeArgs& a, int pg, int g, int n, int gq,
                                        PageRegs& r) {
   const uint16_t* vp =
-      a.v_cache + (((int64_t)pg * a.num_kv_heads + g) * kHeadDim + n) * kPage + gq * 4;
+      (const uint16_t*)a.v_cache + (((int64_t)pg * a.num_kv_heads + g) * kHeadDim + n) * kPage + gq * 4;
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb)
     r.v[nb] = __builtin_nontemporal_load((const u32x2*)(vp + nb * 16 * kPage));
+}
+
+// fp8 cache (same index order, 1-byte elements).  Lane (n, gq) loads bytes
+// gq*32 .. gq*32+31 of K row n in two 16-byte loads, so the contraction's dim
+// order is permuted: element j of MFMA block c is dim gq*32 + c*8 + j, and the
+// q operand and the new token's K row follow the same order (kdim below).
+// V: the same 4 tokens x 1 dim per 16-dim block as bf16, one dword each.
+struct PageRaw8 {
+  u32x4 k[2];
+  uint32_t v[8];
+};
+
+__device__ __forceinline__ void load_k(const DecodeArgs& a, int pg, int g, int n, int gq,
+                                       PageRaw8& r) {
+  const uint8_t* kp = (const uint8_t*)a.k_cache +
+                      (((int64_t)pg * a.num_kv_heads + g) * kPage + n) * kHeadDim + gq * 32;
+  r.k[0] = __builtin_nontemporal_load((const u32x4*)kp);
+  r.k[1] = __builtin_nontemporal_load((const u32x4*)(kp + 16));
+}
+
+__device__ __forceinline__ void load_v(const DecodeArgs& a, int pg, int g, int n, int gq,
+                                       PageRaw8& r) {
+  const uint8_t* vp = (const uint8_t*)a.v_cache +
+                      (((int64_t)pg * a.num_kv_heads + g) * kHeadDim + n) * kPage + gq * 4;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+    r.v[nb] = __builtin_nontemporal_load((const uint32_t*)(vp + nb * 16 * kPage));
+}
+
+// MFMA operands of a page: bf16 registers as loaded, or fp8 codes widened
+// to bf16 (exact) right before their MFMA, so only the 4 KiB of raw codes
+// stay live between pages.
+__device__ __forceinline__ bf16x8 k_operand(const PageRegs& r, int c) { return r.k[c]; }
+__device__ __forceinline__ bf16x8 k_operand(const PageRaw8& r, int c) {
+  const bf16x4 x0 = fp8x4_to_bf16x4(r.k[c >> 1][(c & 1) * 2]);
+  const bf16x4 x1 = fp8x4_to_bf16x4(r.k[c >> 1][(c & 1) * 2 + 1]);
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x4 v_operand(const PageRegs& r, int nb) {
+  return __builtin_bit_cast(bf16x4, r.v[nb]);
+}
+__device__ __forceinline__ bf16x4 v_operand(const PageRaw8& r, int nb) {
+  return fp8x4_to_bf16x4(r.v[nb]);
+}
+
+// Zero the V elements of tokens gq*4+i with keep[i] false.
+__device__ __forceinline__ void mask_v(PageRegs& r, const bool (&keep)[4]) {
+  const uint32_t mx = (keep[0] ? 0xffffu : 0u) | (keep[1] ? 0xffff0000u : 0u);
+  const uint32_t my = (keep[2] ? 0xffffu : 0u) | (keep[3] ? 0xffff0000u : 0u);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    r.v[nb][0] &= mx;
+    r.v[nb][1] &= my;
+  }
+}
+__device__ __forceinline__ void mask_v(PageRaw8& r, const bool (&keep)[4]) {
+  const uint32_t m = (keep[0] ? 0xffu : 0u) | (keep[1] ? 0xff00u : 0u) |
+                     (keep[2] ? 0xff0000u : 0u) | (keep[3] ? 0xff000000u : 0u);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) r.v[nb] &= m;
+}
+
+// Dim held by element j of the q/K operand block c in lane group gq.
+template <bool KV8>
+__device__ __forceinline__ constexpr int kdim(int c, int gq, int j) {
+  return KV8 ? gq * 32 + c * 8 + j : c * 32 + gq * 8 + j;
 }
 
 // Page id of logical page p of request b (wave-uniform scalar load), or -1
@@ -89,14 +157,14 @@ struct WaveState {
 // One page: scores, mask of the ragged ends, online softmax, value MFMAs.
 // The K registers are dead after the score MFMAs and may be reloaded by the
 // caller from that point (done through the `after_scores` callback).
-template <typename AfterScores>
-__device__ __forceinline__ void consume_page(PageRegs& r, const bf16x8 (&qop)[4], int p, int lo,
+template <typename Regs, typename AfterScores>
+__device__ __forceinline__ void consume_page(Regs& r, const bf16x8 (&qop)[4], int p, int lo,
                                              int t, int n, int gq, WaveState& st,
                                              AfterScores after_scores) {
   f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[c], qop[c], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(r, c), qop[c], sc, 0, 0, 0);
   after_scores();
   float sv[4];
 #pragma unroll
@@ -106,20 +174,14 @@ __device__ __forceinline__ void consume_page(PageRegs& r, const bf16x8 (&qop)[4]
   // (which may hold any bits) cannot reach the accumulator
   const int tok0 = p * kPage;
   if (tok0 < lo || tok0 + kPage - 1 > t) {
-    uint32_t keep[4];
+    bool keep[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tok = tok0 + gq * 4 + i;
-      const bool ok = tok >= lo && tok <= t;
-      if (!ok) sv[i] = -INFINITY;
-      keep[i] = ok ? 0xffffu : 0u;
+      keep[i] = tok >= lo && tok <= t;
+      if (!keep[i]) sv[i] = -INFINITY;
     }
-    const uint32_t mx = keep[0] | (keep[1] << 16), my = keep[2] | (keep[3] << 16);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      r.v[nb][0] &= mx;
-      r.v[nb][1] &= my;
-    }
+    mask_v(r, keep);
   }
 
   // online softmax in log2 units (q carries scale*log2(e))
@@ -154,18 +216,19 @@ __device__ __forceinline__ void consume_page(PageRegs& r, const bf16x8 (&qop)[4]
   const bf16x4 pop = {s01[0], s01[1], s23[0], s23[1]};
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb)
-    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-        pop, __builtin_bit_cast(bf16x4, r.v[nb]), st.acc[nb], 0, 0, 0);
+    st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, v_operand(r, nb), st.acc[nb], 0,
+                                                            0, 0);
 }
 
-// The new token's K row / V column, computed by this workgroup, replace what
-// the page loads returned for row tr of the last page.
+// The new token's K row / V column, computed by this workgroup (as bf16
+// bits of the cached values), replace what the page loads returned for row
+// tr of the last page.
 __device__ __forceinline__ void substitute_new_token(PageRegs& r, const uint16_t* knew,
                                                      const uint16_t* vnew, int tr, int n,
                                                      int gq) {
   if (n == tr) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) r.k[c] = *(const bf16x8*)(knew + c * 32 + gq * 8);
+    for (int c = 0; c < 4; ++c) r.k[c] = *(const bf16x8*)(knew + kdim<false>(c, gq, 0));
   }
   if (gq == (tr >> 2)) {
     const int e = tr & 3;
@@ -179,11 +242,30 @@ __device__ __forceinline__ void substitute_new_token(PageRegs& r, const uint16_t
   }
 }
 
+// The same for an fp8 cache: knew / vnew hold the new token's fp8 codes.
+__device__ __forceinline__ void substitute_new_token(PageRaw8& r, const uint8_t* knew,
+                                                     const uint8_t* vnew, int tr, int n, int gq) {
+  if (n == tr) {
+    r.k[0] = *(const u32x4*)(knew + gq * 32);
+    r.k[1] = *(const u32x4*)(knew + gq * 32 + 16);
+  }
+  if (gq == (tr >> 2)) {
+    const int sh = (tr & 3) * 8;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      r.v[nb] = (r.v[nb] & ~(0xffu << sh)) | ((uint32_t)vnew[nb * 16 + n] << sh);
+  }
+}
+
 // K2.  WAVES waves per workgroup.  MAXP > 1: the split has at most
 // WAVES * MAXP pages and every wave issues all its page loads up front;
 // MAXP == 1: the pipelined loop.  SINGLE: the split covers the whole key
 // range, so the sink is folded in here and the output written directly.
-// FUSED: also the norm/RoPE of q and the append of the new token.
+// FUSED: also the norm/RoPE of q and the append of the new token.  KV8: the
+// cache holds fp8 codes, widened to bf16 operand by operand (exact); k_scale
+// rides in qscale and v_scale multiplies the result, and a wave keeps kAhead8
+// pages of loads in flight (a 4 KiB page needs more pages in flight per wave
+// than an 8 KiB one for the same bytes in flight).
 //
 // Start-up latency: the first loads (q, the first page ids and their K/V) are
 // issued before seq_lens[b] has arrived, for the key range of a request of
@@ -191,11 +273,17 @@ __device__ __forceinline__ void substitute_new_token(PageRegs& r, const uint16_t
 // known they are kept if it equals that bound and reissued otherwise.  Every
 // speculative page id is read inside the caller's block-table row and
 // validated before it addresses the cache.
-template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED>
-__global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_kernel(
+constexpr int kAhead8 = 2;
+
+// Launch bounds: the second figure is the least waves per SIMD.  fp8 split
+// kernels are held to 4 (128 VGPRs) so that two workgroups share a CU.
+template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED, bool KV8>
+__global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void decode_split_kernel(
     DecodeArgs a) {
   constexpr int kThreads = WAVES * 64;
-  constexpr int NR = MAXP > 1 ? MAXP : 1;  // page buffers per wave
+  // page buffers per wave
+  constexpr int NR = MAXP > 1 ? MAXP : (KV8 ? kAhead8 : 1);
+  using Raw = typename std::conditional<KV8, PageRaw8, PageRegs>::type;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -207,8 +295,10 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_ker
   __shared__ float sm_l[WAVES][kGroup];
   __shared__ int sm_bad[WAVES];
   __shared__ float sm_q[FUSED ? kGroup : 1][kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_knew[FUSED ? kHeadDim : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_vnew[FUSED ? kHeadDim : 8];
+  // the new token's K row / V column as cached (bf16 bits or fp8 codes)
+  using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
+  __shared__ __attribute__((aligned(16))) Elem sm_knew[FUSED ? kHeadDim : 16];
+  __shared__ __attribute__((aligned(16))) Elem sm_vnew[FUSED ? kHeadDim : 16];
   __shared__ int sm_fused_bad;
 
   // ---- loads that do not wait for seq_len -------------------------------
@@ -227,11 +317,11 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_ker
       }
     }
   } else {
-    const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim + gq * 8;
+    const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      qraw[2 * c] = *(const f32x4*)(qh + c * 32);
-      qraw[2 * c + 1] = *(const f32x4*)(qh + c * 32 + 4);
+      qraw[2 * c] = *(const f32x4*)(qh + kdim<KV8>(c, gq, 0));
+      qraw[2 * c + 1] = *(const f32x4*)(qh + kdim<KV8>(c, gq, 4));
     }
   }
   // page range of this split for a request whose query sits at position tt
@@ -246,7 +336,7 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_ker
   // position, computed while the loads below are in flight
   double cs = 1.0, sn = 0.0;
   if (FUSED && a.use_rope) rope_cos_sin(a.max_seq_len - 1, lane, a.rope_theta, &cs, &sn);
-  PageRegs r[NR];
+  Raw r[NR];
   int bad = 0;
   auto issue = [&](int k) {  // page id and loads of this wave's k-th page
     const int p = p_begin + w + k * WAVES;
@@ -318,33 +408,57 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_ker
         double y0, y1;
         norm_rope_head(xk[lane], xk[lane + 64], a.k_w, a.rms_eps, a.use_rope, cs, sn, lane,
                        &y0, &y1);
-        const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
-        sm_knew[lane] = k0;
-        sm_knew[lane + 64] = k1;
-        if (ok) {
-          uint16_t* dst = a.k_cache + (((int64_t)pg * a.num_kv_heads + g) * kPage + t % kPage) *
-                                          kHeadDim;
-          dst[lane] = k0;
-          dst[lane + 64] = k1;
+        const int64_t o = (((int64_t)pg * a.num_kv_heads + g) * kPage + t % kPage) * kHeadDim;
+        if (KV8) {
+          const uint32_t c0 = fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
+          const uint32_t c1 = fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
+          sm_knew[lane] = (Elem)c0;
+          sm_knew[lane + 64] = (Elem)c1;
+          if (ok) {
+            uint8_t* dst = (uint8_t*)a.k_cache + o;
+            dst[lane] = (uint8_t)c0;
+            dst[lane + 64] = (uint8_t)c1;
+          }
+        } else {
+          const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
+          sm_knew[lane] = (Elem)k0;
+          sm_knew[lane + 64] = (Elem)k1;
+          if (ok) {
+            uint16_t* dst = (uint16_t*)a.k_cache + o;
+            dst[lane] = k0;
+            dst[lane + 64] = k1;
+          }
         }
         if (lane == 0) sm_fused_bad = !ok;
       } else {
         const float* xv = a.v_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
-        const uint16_t v0 = bf16_bits_rne(xv[lane]), v1 = bf16_bits_rne(xv[lane + 64]);
-        sm_vnew[lane] = v0;
-        sm_vnew[lane + 64] = v1;
-        if (ok) {
-          uint16_t* dst = a.v_cache + ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage) +
-                          t % kPage;
-          dst[lane * kPage] = v0;
-          dst[(lane + 64) * kPage] = v1;
+        const int64_t o = ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage) + t % kPage;
+        if (KV8) {
+          const uint32_t c0 = fp8_e4m3_rne_f64((double)xv[lane] / (double)a.v_scale);
+          const uint32_t c1 = fp8_e4m3_rne_f64((double)xv[lane + 64] / (double)a.v_scale);
+          sm_vnew[lane] = (Elem)c0;
+          sm_vnew[lane + 64] = (Elem)c1;
+          if (ok) {
+            uint8_t* dst = (uint8_t*)a.v_cache + o;
+            dst[lane * kPage] = (uint8_t)c0;
+            dst[(lane + 64) * kPage] = (uint8_t)c1;
+          }
+        } else {
+          const uint16_t v0 = bf16_bits_rne(xv[lane]), v1 = bf16_bits_rne(xv[lane + 64]);
+          sm_vnew[lane] = (Elem)v0;
+          sm_vnew[lane + 64] = (Elem)v1;
+          if (ok) {
+            uint16_t* dst = (uint16_t*)a.v_cache + o;
+            dst[lane * kPage] = v0;
+            dst[(lane + 64) * kPage] = v1;
+          }
         }
       }
     }
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const float* qh = &sm_q[n & 7][c * 32 + gq * 8];
+      const float* qh = &sm_q[n & 7][kdim<KV8>(c, gq, 0)];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         const f32x2 v = {qh[j] * a.qscale, qh[j + 1] * a.qscale};
@@ -380,14 +494,45 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_ker
   st.l_part = 0.f;
   const int tr = t % kPage;
 
+  auto nothing = [] {};
   if (MAXP > 1) {
-    auto nothing = [] {};
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const int p = p_begin + w + k * WAVES;
       if (p < p_end) {
         if (FUSED && p == last_page) substitute_new_token(r[k], sm_knew, sm_vnew, tr, n, gq);
         consume_page(r[k], qop, p, lo, t, n, gq, st, nothing);
+      }
+    }
+  } else if constexpr (KV8) {
+    // fp8: a ring of NR page buffers; buffer k is consumed and refilled with
+    // the page NR rounds later (K once the score MFMAs have read it, V after
+    // the value MFMAs).  Page ids run one more round ahead of those loads.
+    int ids[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int pn = p_begin + w + (NR + k) * WAVES;
+      ids[k] = pn < p_end ? page_id(a, b, pn) : 0;
+    }
+    for (int p0 = p_begin + w; p0 < p_end; p0 += NR * WAVES) {
+#pragma unroll
+      for (int k = 0; k < NR; ++k) {
+        const int p = p0 + k * WAVES;
+        if (p < p_end) {
+          const int pn = p + NR * WAVES;
+          const bool has_next = pn < p_end;
+          bad |= has_next && ids[k] < 0;
+          const int pg_next = max(ids[k], 0);
+          if (has_next) {
+            const int pa = pn + NR * WAVES;
+            ids[k] = pa < p_end ? page_id(a, b, pa) : 0;
+          }
+          if (FUSED && p == last_page) substitute_new_token(r[k], sm_knew, sm_vnew, tr, n, gq);
+          consume_page(r[k], qop, p, lo, t, n, gq, st, [&] {
+            if (has_next) load_k(a, pg_next, g, n, gq, r[k]);
+          });
+          if (has_next) load_v(a, pg_next, g, n, gq, r[k]);
+        }
       }
     }
   } else {
@@ -456,11 +601,12 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : 2) void decode_split_ker
       const float scale_o = exp2_fast(M - M2);
       const float den = exp2_fast(sink - M2) + L * scale_o;
       float res = o * scale_o / den;
+      if (KV8) res *= a.v_scale;
       if (any_bad) res = __builtin_nanf("");
       a.out[((int64_t)b * hq + hg) * kHeadDim + d] = res;
     } else {
       const int64_t row = ((int64_t)b * a.num_splits + s) * hq + hg;
-      a.part_o[row * kHeadDim + d] = o / L;
+      a.part_o[row * kHeadDim + d] = KV8 ? o / L * a.v_scale : o / L;
       if (d == 0) a.part_lse[row] = any_bad ? __builtin_nanf("") : M + log2_fast(L);
     }
   }
@@ -615,47 +761,47 @@ hipError_t launch_merge_k(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool FUSED>
+template <bool FUSED, bool KV8>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
   const bool win = a.window > 0;
   if (!FUSED && a.partials_only) {  // every split's partial, whatever the count
     constexpr int W = kDecodeWaves;
     if (win)
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false>), grid, dim3(W * 64), 0,
-                         st, a);
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8>), grid, dim3(W * 64),
+                         0, st, a);
     else
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false>), grid, dim3(W * 64), 0,
-                         st, a);
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false, KV8>), grid, dim3(W * 64),
+                         0, st, a);
     return hipGetLastError();
   }
   if (a.num_splits == 1 && a.pages_per_split <= kSinglePages) {
     constexpr int W = kDecodeWavesSingle;
     constexpr int P = (kSinglePages + W - 1) / W;
     if (win)
-      hipLaunchKernelGGL((decode_split_kernel<W, P, true, true, FUSED>), grid, dim3(W * 64), 0, st,
-                         a);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<W, P, true, false, FUSED>), grid, dim3(W * 64), 0,
+      hipLaunchKernelGGL((decode_split_kernel<W, P, true, true, FUSED, KV8>), grid, dim3(W * 64), 0,
                          st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<W, P, true, false, FUSED, KV8>), grid, dim3(W * 64),
+                         0, st, a);
     return hipGetLastError();
   }
   constexpr int W = kDecodeWaves;
   if (a.num_splits == 1) {  // one long split: pipelined loop, sink folded in
     if (win)
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED>), grid, dim3(W * 64), 0, st,
-                         a);
-    else
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED>), grid, dim3(W * 64), 0,
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8>), grid, dim3(W * 64), 0,
                          st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED, KV8>), grid, dim3(W * 64),
+                         0, st, a);
     return hipGetLastError();
   }
   if (win)
-    hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED>), grid, dim3(W * 64), 0, st,
-                       a);
+    hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8>), grid, dim3(W * 64), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED>), grid, dim3(W * 64), 0, st,
-                       a);
+    hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED, KV8>), grid, dim3(W * 64), 0,
+                       st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_merge_k(a, st);
@@ -665,7 +811,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
-  return a.q_in ? launch_decode_t<true>(a, st) : launch_decode_t<false>(a, st);
+  if (a.kv_fp8) return a.q_in ? launch_decode_t<true, true>(a, st) : launch_decode_t<false, true>(a, st);
+  return a.q_in ? launch_decode_t<true, false>(a, st) : launch_decode_t<false, false>(a, st);
 }
 
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t st) {

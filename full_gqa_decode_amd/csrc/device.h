@@ -92,6 +92,32 @@ __device__ __forceinline__ uint16_t bf16_bits_rne_f64(double x) {
   return bf16_bits_rne(f);
 }
 
+// fp64 -> fp8 E4M3 code (OCP E4M3: bias 7, subnormals, no infinities,
+// S.1111.111 NaN): nearest, ties to the even code; |x| >= 448 saturates to
+// the largest finite code and NaN gives a NaN code.  Within a binade the
+// value is scaled by a power of two (exact) onto the integer grid of
+// mantissas and rounded by rint (ties to even), so x is rounded once.
+__device__ __forceinline__ uint32_t fp8_e4m3_rne_f64(double x) {
+  const uint32_t sign = (__builtin_bit_cast(uint64_t, x) >> 63) ? 0x80u : 0u;
+  if (x != x) return sign | 0x7Fu;
+  const double a = fabs(x);
+  if (a >= 448.0) return sign | 0x7Eu;
+  if (a < 0.015625) return sign | (uint32_t)rint(a * 512.0);  // step 2^-9 below 2^-6
+  int e;
+  (void)frexp(a, &e);                                  // a in [2^(e-1), 2^e)
+  const uint32_t m = (uint32_t)rint(ldexp(a, 4 - e));  // 8..16 (16 carries)
+  return sign | (uint32_t)(((e + 6) << 3) + (int)m - 8);
+}
+
+// Four fp8 E4M3 codes (bytes 0..3 of w) -> bf16 values in byte order.  Exact:
+// every E4M3 value, subnormals included, is a normal bf16 number.  gfx950's
+// scaled conversion with scale 1.
+__device__ __forceinline__ bf16x4 fp8x4_to_bf16x4(uint32_t w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+}
+
 // Sum over the 64 lanes, result in every lane: DPP row_ror 8/4/2/1 leaves
 // each 16-lane row's total in all its lanes, then the four row totals are
 // read as scalars.  No LDS traffic (a shuffle-based version costs ~6 LDS

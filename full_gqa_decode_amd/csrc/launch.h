@@ -17,8 +17,8 @@ struct AppendArgs {
   const int32_t* slots;
   float* q_out_f32;
   uint16_t* q_out_bf16;
-  uint16_t* k_cache;
-  uint16_t* v_cache;
+  void* k_cache;             // bf16 bits, or fp8 E4M3 codes when kv_fp8
+  void* v_cache;
   int32_t num_tokens;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -26,13 +26,16 @@ struct AppendArgs {
   int32_t use_rope;
   float rope_theta;
   float rms_eps;
+  int32_t kv_fp8;            // caches hold fp8(x / scale)
+  float k_scale;
+  float v_scale;
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
 struct DecodeArgs {
   const float* q;            // [B][Hq][128] fp32 (normalised; unfused path)
-  uint16_t* k_cache;         // [pages][Hkv][16][128] (written only by the fused path)
-  uint16_t* v_cache;         // [pages][Hkv][128][16]
+  void* k_cache;             // [pages][Hkv][16][128] (written only by the fused path)
+  void* v_cache;             // [pages][Hkv][128][16]; elements bf16 or fp8 (kv_fp8)
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const float* sinks;        // [Hq]
@@ -48,7 +51,10 @@ struct DecodeArgs {
   int32_t pages_per_split;
   int32_t num_splits;        // splits in the grid (per request)
   int32_t partials_only;     // write every split's partial (no merge, no sink)
-  float qscale;              // softmax_scale * log2(e)
+  float qscale;              // softmax_scale * log2(e) (* k_scale for an fp8 cache)
+  int32_t kv_fp8;            // 1: fp8 E4M3 codes of K / k_scale, V / v_scale
+  float k_scale;             // fp8: divides the new token's K before encoding
+  float v_scale;             // fp8: multiplies every output (1 for bf16)
   // fused append of the new token (flint_attn_decode_step); q_in == nullptr
   // selects the unfused path
   const float* q_in;         // [B][Hq][128] raw

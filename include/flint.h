@@ -27,7 +27,8 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     All work is enqueued on it; no call synchronises or reads device memory
  *     back, so every call can be captured into a HIP graph.
- *   - bf16 values are passed as their uint16 bit patterns.
+ *   - bf16 values are passed as their uint16 bit patterns; cache pointers are
+ *     untyped (void*), their element type set by the layer's kv_dtype.
  *   - Arguments the host can see are checked before anything is launched and
  *     a status is returned; flint_last_error() then describes the problem.
  *     Device-resident indices (positions, slots, page ids, seq_lens) are
@@ -47,6 +48,18 @@
  *   K rows feed the q.K contraction over dims; V is stored dim-major because
  *   the P.V contraction runs over tokens, so both operands of the matrix
  *   cores load straight from HBM with full coalescing.
+ *
+ * KV element formats (flint_attn_layer.kv_dtype)
+ *   FLINT_KV_BF16: 2-byte bf16 elements (uint16 bit patterns), 4 KiB tiles.
+ *   FLINT_KV_FP8_E4M3: 1-byte elements in the same index order (2 KiB
+ *   tiles), halving the bytes decode streams ("Recursive Flint" model JSON,
+ *   "kvCacheGiBPerRequest" lists an fp8 column beside bf16).  Reading of the
+ *   format: OCP E4M3 -- sign, 4 exponent bits of bias 7, 3 mantissa bits,
+ *   subnormals, no infinities, S.1111.111 is NaN, largest finite 448.  The
+ *   cache holds K / k_scale and V / v_scale (one pair of scales per layer):
+ *   an element reads back as code value * scale.  Writes round to nearest,
+ *   ties to the even code, once from the exact (fp64) quotient; magnitudes
+ *   at or above 448 saturate to +-448 and NaN stays NaN.
  */
 #ifndef FLINT_H
 #define FLINT_H
@@ -58,7 +71,7 @@
 extern "C" {
 #endif
 
-#define FLINT_ABI_VERSION 1
+#define FLINT_ABI_VERSION 2
 
 typedef enum {
   FLINT_OK = 0,
@@ -81,7 +94,12 @@ typedef struct {
   float rope_theta;      /* RoPE base (10000)                                */
   float rms_eps;         /* RMSNorm epsilon (1e-6)                           */
   float softmax_scale;   /* multiplies q.k (1/sqrt(128))                     */
-} flint_attn_layer;
+  int32_t kv_dtype;      /* FLINT_KV_BF16 or FLINT_KV_FP8_E4M3               */
+  float k_scale;         /* fp8 cache: K = code value * k_scale (finite > 0) */
+  float v_scale;         /* fp8 cache: V = code value * v_scale (finite > 0) */
+} flint_attn_layer;     /* the scales are ignored for a bf16 cache         */
+
+enum { FLINT_KV_BF16 = 0, FLINT_KV_FP8_E4M3 = 1 };
 
 /*
  * Fused per-head Q/K RMSNorm, optional RoPE and paged KV append for
@@ -99,6 +117,7 @@ typedef struct {
  * position) when use_rope, computed in fp64; q_out is y rounded once to fp32
  * (or bf16), K is y rounded once to bf16 (round-to-nearest-even) and V is v
  * rounded to bf16; K and V are written at the slot.  V is not normalised.
+ * An fp8 cache receives fp8(y / k_scale) and fp8(v / v_scale) instead.
  * A slot >= num_blocks*16 or a negative position is not written and the
  * token's q_out row is set to NaN.
  */
@@ -107,11 +126,12 @@ flint_status flint_qk_norm_rope_append(const flint_attn_layer* L, int32_t num_to
                                        const float* q_norm_w, const float* k_norm_w,
                                        const int32_t* positions, const int32_t* slot_mapping,
                                        float* q_out_f32, uint16_t* q_out_bf16,
-                                       uint16_t* k_cache, uint16_t* v_cache, int32_t num_blocks,
+                                       void* k_cache, void* v_cache, int32_t num_blocks,
                                        void* stream);
 
 /*
- * Decode attention: one new query per request over its paged bf16 KV.
+ * Decode attention: one new query per request over its paged KV (bf16 or
+ * fp8; for fp8, K_j and V_j below are the scaled code values).
  * Request b's query sits at position t = seq_lens[b] - 1 (seq_lens counts the
  * new token, which must already be appended) and attends to keys lo..t,
  * lo = 0 (window 0) or max(0, t - window + 1).  For query head h of KV group
@@ -134,7 +154,7 @@ flint_status flint_qk_norm_rope_append(const flint_attn_layer* L, int32_t num_to
 size_t flint_attn_decode_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                         int32_t max_seq_len);
 flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, const float* q,
-                               const uint16_t* k_cache, const uint16_t* v_cache,
+                               const void* k_cache, const void* v_cache,
                                int32_t num_blocks, const int32_t* block_tables,
                                int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
                                const float* sinks, float* out, void* workspace,
@@ -146,7 +166,7 @@ flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, cons
 size_t flint_attn_decode_workspace_size_ex(const flint_attn_layer* L, int32_t num_seqs,
                                            int32_t max_seq_len, int32_t pages_per_split);
 flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, const float* q,
-                                  const uint16_t* k_cache, const uint16_t* v_cache,
+                                  const void* k_cache, const void* v_cache,
                                   int32_t num_blocks, const int32_t* block_tables,
                                   int32_t bt_stride, const int32_t* seq_lens,
                                   int32_t max_seq_len, const float* sinks, float* out,
@@ -174,7 +194,7 @@ flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
                                     const float* q_in, const float* k_in, const float* v_in,
                                     const float* q_norm_w, const float* k_norm_w,
                                     const int32_t* slot_mapping, float* q_out,
-                                    uint16_t* k_cache, uint16_t* v_cache, int32_t num_blocks,
+                                    void* k_cache, void* v_cache, int32_t num_blocks,
                                     const int32_t* block_tables, int32_t bt_stride,
                                     const int32_t* seq_lens, int32_t max_seq_len,
                                     const float* sinks, float* out, void* workspace,
@@ -209,8 +229,8 @@ flint_status flint_attn_decode_plan(const flint_attn_layer* L, int32_t num_seqs,
  *   part_o [B][S][num_q_heads][128] fp32, part_lse [B][S][num_q_heads] fp32
  */
 flint_status flint_attn_decode_partials(const flint_attn_layer* L, int32_t num_seqs,
-                                        const float* q, const uint16_t* k_cache,
-                                        const uint16_t* v_cache, int32_t num_blocks,
+                                        const float* q, const void* k_cache,
+                                        const void* v_cache, int32_t num_blocks,
                                         const int32_t* block_tables, int32_t bt_stride,
                                         const int32_t* seq_lens, int32_t max_seq_len,
                                         int32_t pages_per_split, int32_t num_splits,
@@ -240,12 +260,13 @@ flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32
  * Same per-row result as decode; the sink joins every row's denominator.
  * Rows of a request with q_len > seq_len or seq_len > max_seq_len, or whose
  * pages include an id outside [0, num_blocks), are set to NaN.
+ * bf16 caches only: an fp8 layer returns FLINT_ERR_UNSUPPORTED.
  */
 size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_seq_len);
 flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* q,
                                 const int32_t* cu_q_lens, int32_t max_q_len,
-                                const uint16_t* k_cache, const uint16_t* v_cache,
+                                const void* k_cache, const void* v_cache,
                                 int32_t num_blocks, const int32_t* block_tables,
                                 int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
                                 const float* sinks, float* out, void* workspace,

@@ -8,8 +8,9 @@ import numpy as np
 import oracle
 import synth
 
-TOL = 4e-3          # max |GPU - oracle| on fp32 attention outputs (bf16 KV)
-SENTINEL = 0x7FC1   # NaN bit pattern in every cache slot nobody wrote
+TOL = 4e-3          # max |GPU - oracle| on fp32 attention outputs
+SENTINEL = 0x7FC1   # NaN bit pattern in every bf16 cache slot nobody wrote
+SENTINEL8 = 0x7F    # the NaN code in every fp8 cache slot nobody wrote
 
 
 def dev():
@@ -30,13 +31,38 @@ def down16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def layers(window):
+def layers(window, fp8=None):
+    """(oracle layer, library layer); fp8 = (k_scale, v_scale) selects an fp8
+    E4M3 cache with those scales (fp32 values, passed to both sides)."""
     import full_gqa_decode_amd as fl
     rope = 1 if window else 0
     # the library receives eps as fp32; the oracle uses that same value
     eps = float(np.float32(1e-6))
-    return (oracle.layer(window=window, use_rope=rope, eps=eps),
-            fl.layer(window=window, use_rope=rope, rms_eps=eps))
+    if fp8 is None:
+        return (oracle.layer(window=window, use_rope=rope, eps=eps),
+                fl.layer(window=window, use_rope=rope, rms_eps=eps))
+    ks, vs = (float(np.float32(x)) for x in fp8)
+    return (oracle.layer(window=window, use_rope=rope, eps=eps, kv_fp8=1, k_scale=ks, v_scale=vs),
+            fl.layer(window=window, use_rope=rope, rms_eps=eps, kv_dtype=fl.FLINT_KV_FP8_E4M3,
+                     k_scale=ks, v_scale=vs))
+
+
+def empty_caches(L, num_blocks, device=False):
+    """K and V caches of num_blocks pages filled with the format's NaN
+    sentinel, on the host (numpy) or the GPU (torch)."""
+    fill = SENTINEL8 if L.kv_fp8 else SENTINEL
+    shapes = (oracle.k_cache_shape(num_blocks), oracle.v_cache_shape(num_blocks))
+    if not device:
+        return tuple(np.full(sh, fill, oracle.cache_dtype(L)) for sh in shapes)
+    import torch
+    dt = torch.uint8 if L.kv_fp8 else torch.int16
+    return tuple(torch.full(sh, fill, dtype=dt, device=dev()) for sh in shapes)
+
+
+def down(t):
+    """cache tensor -> numpy codes (uint16 bf16 bits or uint8 fp8 codes)."""
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if a.dtype == np.int16 else a
 
 
 class DecodeCase:
@@ -44,9 +70,10 @@ class DecodeCase:
     cache.  Raw q/k/v ~ N(0,1); every token a request still needs is appended
     (both sides); the new token of request b is at position ctxs[b]-1."""
 
-    def __init__(self, seed, ctxs, window=0, ring=False, weights_one=True, extra_pages=3):
+    def __init__(self, seed, ctxs, window=0, ring=False, weights_one=True, extra_pages=3,
+                 fp8=None):
         self.seed, self.ctxs, self.window = seed, list(ctxs), window
-        self.L, self.FL = layers(window)
+        self.L, self.FL = layers(window, fp8)
         B = len(ctxs)
         self.B = B
         tag = (hash((tuple(ctxs), window, ring)) & 0xFFFF,)
@@ -95,8 +122,7 @@ class DecodeCase:
     def oracle_cache(self):
         """O4 for every token's K/V; q only for each request's new token.
         Returns (q_hat of the new tokens [B,32,128] fp64, K cache, V cache)."""
-        kc = np.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, np.uint16)
-        vc = np.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, np.uint16)
+        kc, vc = empty_caches(self.L, self.num_blocks)
         oracle.append(self.L, self.q_in[:1], self.k_in, self.v_in, self.qw, self.kw, self.pos,
                       self.slots, kc, vc, want_q=False)
         r = self.last_row
@@ -113,10 +139,7 @@ class DecodeCase:
         """append every token, then decode; returns (out, q_out, kc, vc) tensors."""
         import torch
         import full_gqa_decode_amd as fl
-        kd = torch.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
-                        device=dev())
-        vd = torch.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
-                        device=dev())
+        kd, vd = empty_caches(self.L, self.num_blocks, device=True)
         qd = up(self.q_in)
         fl.flint_qk_norm_rope_append(self.FL, qd, up(self.k_in), up(self.v_in), up(self.qw),
                                      up(self.kw), up(self.pos), up(self.slots), qd, kd, vd)
@@ -134,10 +157,7 @@ class DecodeCase:
         step (append of the new token + decode in one launch)."""
         import torch
         import full_gqa_decode_amd as fl
-        kd = torch.full(oracle.k_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
-                        device=dev())
-        vd = torch.full(oracle.v_cache_shape(self.num_blocks), SENTINEL, dtype=torch.int16,
-                        device=dev())
+        kd, vd = empty_caches(self.L, self.num_blocks, device=True)
         keep = np.ones(self.T, bool)
         keep[self.last_row] = False
         pre = np.nonzero(keep)[0]
@@ -161,11 +181,12 @@ class DecodeCase:
 
 
 class CacheDecodeCase:
-    """Decode only: the bf16 cache and the fp32 q are drawn directly (no
-    append), so K2/K3 are tested on their own."""
+    """Decode only: the cache and the fp32 q are drawn directly (no append),
+    so K2/K3 are tested on their own.  fp8 = (k_scale, v_scale): an fp8 cache
+    of random codes (K magnitudes below 2, V below 30, before scaling)."""
 
-    def __init__(self, seed, ctxs, window=0, ring=False, q_scale=1.0):
-        self.L, self.FL = layers(window)
+    def __init__(self, seed, ctxs, window=0, ring=False, q_scale=1.0, fp8=None):
+        self.L, self.FL = layers(window, fp8)
         self.ctxs = list(ctxs)
         B = len(ctxs)
         self.B = B
@@ -179,8 +200,12 @@ class CacheDecodeCase:
             self.bt, nb = synth.shuffled_block_table(seed, tag + (synth.PERM,), B,
                                                      [-(-c // 16) for c in ctxs], self.bt_stride)
         self.num_blocks = nb
-        self.kc = synth.normal_bf16_bits(seed, tag + (synth.KC,), oracle.k_cache_shape(nb))
-        self.vc = synth.normal_bf16_bits(seed, tag + (synth.VC,), oracle.v_cache_shape(nb))
+        if fp8 is None:
+            self.kc = synth.normal_bf16_bits(seed, tag + (synth.KC,), oracle.k_cache_shape(nb))
+            self.vc = synth.normal_bf16_bits(seed, tag + (synth.VC,), oracle.v_cache_shape(nb))
+        else:
+            self.kc = synth.fp8_codes(seed, tag + (synth.KC,), oracle.k_cache_shape(nb), 0x3F)
+            self.vc = synth.fp8_codes(seed, tag + (synth.VC,), oracle.v_cache_shape(nb), 0x5F)
         self.q = synth.normal(seed, tag + (synth.Q,), (B, 32, 128)) * np.float32(q_scale)
         self.sinks = synth.normal(seed, tag + (synth.SINK,), 32)
         self.seq_lens = np.array(ctxs, np.int32)

@@ -32,7 +32,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = fl.lib()
-    assert lib.flint_abi_version() == 1
+    assert lib.flint_abi_version() == 2
+    # 12 four-byte fields, in the header's order
+    assert C.sizeof(fl.FlintAttnLayer) == 48
+    assert [f[0] for f in fl.FlintAttnLayer._fields_][-3:] == ["kv_dtype", "k_scale", "v_scale"]
     for s, name in fl.STATUS_NAMES.items():
         assert lib.flint_status_string(s).decode() == name
 
@@ -92,11 +95,31 @@ def test_decode_workspace_too_small():
     ("window", -1, INVALID),
     ("use_rope", 2, INVALID),
     ("softmax_scale", float("inf"), INVALID),
+    ("kv_dtype", 2, INVALID),
+    ("kv_dtype", -1, INVALID),
 ])
 def test_layer_validation(field, value, status):
     L = fl.full_layer()
     setattr(L, field, value)
     assert _decode(L) == status
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(0.0, 1.0), (1.0, -2.0), (float("inf"), 1.0),
+                                             (1.0, float("nan"))])
+def test_fp8_layer_needs_positive_finite_scales(k_scale, v_scale):
+    L = fl.full_layer(kv_dtype=fl.FLINT_KV_FP8_E4M3, k_scale=k_scale, v_scale=v_scale)
+    assert _decode(L) == INVALID
+    # a bf16 layer ignores the scales
+    L = fl.full_layer(k_scale=k_scale, v_scale=v_scale)
+    assert _decode(L, q=None) == INVALID and "NULL" in fl.lib().flint_last_error().decode()
+
+
+def test_prefill_rejects_an_fp8_layer():
+    lib = fl.lib()
+    L = fl.full_layer(kv_dtype=fl.FLINT_KV_FP8_E4M3, k_scale=0.5, v_scale=2.0)
+    args = [C.byref(L), 1, P, P + 0x10000, 32, Q, Q + 0x10000, 4, P + 0x20000, 4, P + 0x30000,
+            64, P + 0x40000, P + 0x50000, None, 0, None]
+    assert lib.flint_attn_prefill(*args) == UNSUPPORTED
 
 
 def test_zero_requests_is_a_no_op():

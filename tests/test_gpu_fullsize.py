@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import synth
-from flint_cases import TOL, dev, layers, up
+from flint_cases import TOL, dev, down, layers, up
 
 pytestmark = pytest.mark.gpu
 
@@ -24,12 +24,12 @@ PAGE = 16
 
 
 class BigStep:
-    def __init__(self, tag, ctxs, window, full_table):
+    def __init__(self, tag, ctxs, window, full_table, fp8=None):
         import torch
         self.ctxs = np.asarray(ctxs, np.int32)
         B = len(ctxs)
         self.B = B
-        self.L, self.FL = layers(window)
+        self.L, self.FL = layers(window, fp8)
         logical = -(-int(self.ctxs.max()) // PAGE)
         self.bt_stride = logical
         if full_table:
@@ -38,12 +38,19 @@ class BigStep:
         else:
             self.bt, nb = synth.ring_block_table(0, tag + (synth.PERM,), B, logical, 33, logical)
         self.nb = nb
-        self.kd = synth.normal_bf16_bits_torch(0, tag + (synth.KC,), oracle.k_cache_shape(nb), dev())
-        self.vd = synth.normal_bf16_bits_torch(0, tag + (synth.VC,), oracle.v_cache_shape(nb), dev())
+        if fp8 is None:
+            self.kd = synth.normal_bf16_bits_torch(0, tag + (synth.KC,), oracle.k_cache_shape(nb),
+                                                   dev())
+            self.vd = synth.normal_bf16_bits_torch(0, tag + (synth.VC,), oracle.v_cache_shape(nb),
+                                                   dev())
+        else:
+            self.kd = synth.fp8_codes_torch(0, tag + (synth.KC,), oracle.k_cache_shape(nb), dev())
+            self.vd = synth.fp8_codes_torch(0, tag + (synth.VC,), oracle.v_cache_shape(nb), dev(),
+                                            0x5F)
         torch.cuda.synchronize()
         # pristine host copies for the oracle (taken before the step appends)
-        self.kc = self.kd.cpu().numpy().view(np.uint16)
-        self.vc = self.vd.cpu().numpy().view(np.uint16)
+        self.kc = down(self.kd)
+        self.vc = down(self.vd)
         self.q_in = synth.normal(0, tag + (synth.Q,), (B, 32, 128))
         self.k_in = synth.normal(0, tag + (synth.K,), (B, 4, 128))
         self.v_in = synth.normal(0, tag + (synth.V,), (B, 4, 128))
@@ -74,21 +81,27 @@ class BigStep:
                                   self.sinks)
 
     def check_written_rows(self):
-        """The new tokens' cache rows: V bit-exact, K within one bf16 ulp of
-        the oracle's correctly rounded value (ties of the fp64 value aside)."""
-        k_gpu = self.kd.cpu().numpy().view(np.uint16) if self.nb * 4 * 16 * 128 < (1 << 28) else None
+        """The new tokens' cache rows: V bit-exact, K within one bf16 ulp (one
+        fp8 grid step) of the oracle's correctly rounded value (ties of the
+        fp64 value aside)."""
+        k_gpu = down(self.kd) if self.nb * 4 * 16 * 128 < (1 << 28) else None
         for b in range(self.B):
             page, row = divmod(int(self.slots[b]), PAGE)
             v_ref = self.vc.reshape(self.nb, 4, 128, PAGE)[page, :, :, row]
-            v_got = self.vd.view(self.nb, 4, 128, PAGE)[page, :, :, row].cpu().numpy().view(np.uint16)
+            v_got = down(self.vd.view(self.nb, 4, 128, PAGE)[page, :, :, row])
             assert np.array_equal(v_got, v_ref), f"V row of request {b}"
             k_ref = self.kc.reshape(self.nb, 4, PAGE, 128)[page, :, row, :]
             if k_gpu is not None:
                 k_got = k_gpu.reshape(self.nb, 4, PAGE, 128)[page, :, row, :]
             else:
-                k_got = self.kd.view(self.nb, 4, PAGE, 128)[page, :, row, :].cpu().numpy().view(np.uint16)
-            diff = np.abs(k_got.astype(np.int32) - k_ref.astype(np.int32))
-            assert diff.max() <= 1, f"K row of request {b}"
+                k_got = down(self.kd.view(self.nb, 4, PAGE, 128)[page, :, row, :])
+            if self.L.kv_fp8:
+                a, r = oracle.fp8_value(k_got), oracle.fp8_value(k_ref)
+                step = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0**-6))) - 3)
+                assert np.all(np.abs(a - r) <= step), f"K row of request {b}"
+            else:
+                diff = np.abs(k_got.astype(np.int32) - k_ref.astype(np.int32))
+                assert diff.max() <= 1, f"K row of request {b}"
         return k_gpu
 
 
@@ -150,5 +163,34 @@ def test_ragged_64_requests_sliding_layer_full_size():
     ref = case.oracle_step(np.arange(64))
     err = float(np.abs(got - ref).max())
     print(f"64 ragged requests, sliding layer: max err {err:.3e}", flush=True)
+    assert err <= TOL
+    case.check_written_rows()
+
+
+def test_bs1_100k_full_layer_step_fp8():
+    # the fp8 cache of the same workload: 102.4 MB of codes (K below 2 and V
+    # below 30 before the scales)
+    import full_gqa_decode_amd as fl
+    case = BigStep((11, 7), [100_000], window=0, full_table=True, fp8=(1.0, 0.25))
+    got = case.run_gpu()
+    ref = case.oracle_step(np.arange(1))
+    err = float(np.abs(got - ref).max())
+    print(f"bs1 100K full layer, fp8 cache: max err {err:.3e}", flush=True)
+    assert err <= TOL
+    k_gpu = case.check_written_rows()
+    slot = int(case.slots[0])
+    kr = k_gpu.reshape(case.nb, 4, PAGE, 128).copy()
+    kh = case.kc.reshape(case.nb, 4, PAGE, 128)
+    kr[slot // PAGE, :, slot % PAGE, :] = kh[slot // PAGE, :, slot % PAGE, :]
+    assert np.array_equal(kr, kh)
+
+
+def test_ragged_64_requests_sliding_layer_fp8():
+    lens = ragged_lengths()
+    case = BigStep((11, 8), lens, window=513, full_table=False, fp8=(1.0 / 16, 0.25))
+    got = case.run_gpu()
+    ref = case.oracle_step(np.arange(64))
+    err = float(np.abs(got - ref).max())
+    print(f"64 ragged requests, sliding layer, fp8 cache: max err {err:.3e}", flush=True)
     assert err <= TOL
     case.check_written_rows()
