@@ -749,11 +749,64 @@ __global__ __launch_bounds__(kSmallMergeThreads) void decode_merge_small_kernel(
   a.out[bh * kHeadDim + d] = nan ? __builtin_nanf("") : o / den;
 }
 
+// K3 for plans of kSmallMergeSplits+1 .. kMidMergeSplits splits (batch 1: the
+// 100K full layer's 64 splits, the window's 17): one wave per (request, query
+// head), with no LDS and no barrier.  Lane l holds split l's lse; the max, the
+// weights and the denominator come from wave reductions.  For the values,
+// lane (c, sg) = (l & 31, l >> 5) sums dims 4c..4c+3 over the splits of
+// parity sg; every load is issued before the max is known (one memory round
+// trip), and the two halves meet across lanes l and l^32.
+constexpr int kMidMergeSplits = 64;
+
+__global__ __launch_bounds__(64) void decode_merge_mid_kernel(DecodeArgs a) {
+  const int hq = a.num_kv_heads * kGroup;
+  const int ns = a.num_splits;
+  const int bh = blockIdx.x;  // b * hq + h
+  const int h = bh % hq, b = bh / hq;
+  const int l = threadIdx.x, c = l & 31, sg = l >> 5;
+  const int64_t base = (int64_t)b * ns * hq + h;  // split s: row base + s * hq
+  // loads past the last split re-read it (no branch between the loads); their
+  // weights are 0
+  float lse = a.part_lse[base + (int64_t)min(l, ns - 1) * hq];
+  if (l >= ns) lse = -INFINITY;
+  f32x4 ov[kMidMergeSplits / 2];
+#pragma unroll
+  for (int j = 0; j < kMidMergeSplits / 2; ++j) {
+    const int s = min(2 * j + sg, ns - 1);
+    ov[j] = *(const f32x4*)(a.part_o + (base + (int64_t)s * hq) * kHeadDim + 4 * c);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the reductions
+  const bool nan = __any(lse != lse);
+  const float sink = a.sinks[h] * kLog2e;
+  const float M = fmaxf(sink, wave_max_f32(lse));
+  // an empty split (lse -inf, output never written) contributes 0
+  const float w = lse > -INFINITY ? exp2_fast(lse - M) : 0.f;
+  const float den = exp2_fast(sink - M) + wave_sum_f32(w);
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMidMergeSplits / 2; ++j) {
+    const float w0 = readlane_f32(w, 2 * j), w1 = readlane_f32(w, 2 * j + 1);
+    const float ws = sg ? w1 : w0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] += ws > 0.f ? ws * ov[j][i] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = sum_xor32(o[i]);
+  if (sg == 0) {
+    const f32x4 r = nan ? f32x4{NAN, NAN, NAN, NAN} : o / den;
+    *(f32x4*)(a.out + (int64_t)bh * kHeadDim + 4 * c) = r;
+  }
+}
+
 hipError_t launch_merge_k(const DecodeArgs& a, hipStream_t st) {
+  const bool al16 = ((uintptr_t)a.part_o % 16 == 0) && ((uintptr_t)a.out % 16 == 0);
   if (a.num_splits <= kSmallMergeSplits) {
     const int64_t n = (int64_t)a.num_seqs * a.num_kv_heads * kGroup * kHeadDim;
     const dim3 grid((unsigned)((n + kSmallMergeThreads - 1) / kSmallMergeThreads));
     hipLaunchKernelGGL(decode_merge_small_kernel, grid, dim3(kSmallMergeThreads), 0, st, a);
+  } else if (a.num_splits <= kMidMergeSplits && al16) {
+    const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * kGroup));
+    hipLaunchKernelGGL(decode_merge_mid_kernel, grid, dim3(64), 0, st, a);
   } else {
     const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
     hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);

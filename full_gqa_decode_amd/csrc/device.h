@@ -75,6 +75,33 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return a + b;
 }
 
+// Within each row of 16 lanes, the value of lane (i + K) mod 16 (DPP row_ror).
+template <int K>
+__device__ __forceinline__ float row_ror(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + K, 0xF, 0xF, false));
+}
+
+// Max / sum over the 64 lanes, result in every lane, without LDS.
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  x = fmaxf(x, row_ror<1>(x));
+  return max_xor32(max_xor16(x));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  x += row_ror<1>(x);
+  return sum_xor32(sum_xor16(x));
+}
+
+__device__ __forceinline__ float readlane_f32(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -93,12 +93,14 @@ def test_merge_of_oracle_partials_matches_oracle(window, ctxs, pps):
     assert np.abs(got - case.expected()).max() <= TOL
 
 
-def test_nan_partial_makes_its_output_nan():
+@pytest.mark.parametrize("ctx,pps", [(300, 5), (300, 1), (2000, 1)])
+def test_nan_partial_makes_its_output_nan(ctx, pps):
+    # 4, 19 and 125 splits: the three merge kernels (up to 8, up to 64, more)
     import torch
     import full_gqa_decode_amd as fl
-    case = CacheDecodeCase(23, [300], window=0)
+    case = CacheDecodeCase(23, [ctx], window=0)
     po, pl = fl.flint_attn_decode_partials(case.FL, up(case.q), up(case.kc), up(case.vc),
-                                           up(case.bt), up(case.seq_lens), 300, 5)
+                                           up(case.bt), up(case.seq_lens), ctx, pps)
     pl[0, 1, 7] = float("nan")
     out = fl.flint_attn_merge(case.FL, po, pl, up(case.sinks))
     torch.cuda.synchronize()
@@ -120,3 +122,26 @@ def test_partials_then_merge_equal_decode_bitwise(window, ctxs, pps):
                          pages_per_split=pps)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("ctx,pps", [(300, 1), (4096, 4)])
+def test_merge_of_unaligned_buffers(ctx, pps):
+    # part_o and out only 4-byte aligned: the launcher falls back from the
+    # 16-byte-load kernel; same result within rounding, and against the oracle
+    import torch
+    import full_gqa_decode_amd as fl
+    case = CacheDecodeCase(25, [ctx], window=0)
+    po, pl = fl.flint_attn_decode_partials(case.FL, up(case.q), up(case.kc), up(case.vc),
+                                           up(case.bt), up(case.seq_lens), ctx, pps)
+    ref = fl.flint_attn_merge(case.FL, po, pl, up(case.sinks))
+    big = torch.empty(po.numel() + 1, dtype=torch.float32, device=po.device)
+    po1 = big[1:].view(po.shape)
+    po1.copy_(po)
+    ob = torch.empty(ref.numel() + 1, dtype=torch.float32, device=po.device)
+    out1 = ob[1:].view(ref.shape)
+    fl.flint_attn_merge(case.FL, po1, pl, up(case.sinks), out=out1)
+    torch.cuda.synchronize()
+    assert po1.data_ptr() % 16 != 0 and out1.data_ptr() % 16 != 0
+    got, want = out1.cpu().numpy(), ref.cpu().numpy()
+    assert np.abs(got - want).max() <= 1e-5
+    assert np.abs(got.astype(np.float64) - case.expected()).max() <= TOL
