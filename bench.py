@@ -9,8 +9,9 @@ order, the fused norm/RoPE/append of the new token and then split-K decode
 attention with the sink merge; the 49 layers are captured into one HIP graph.
 
 Prints one JSON line.  `value` is microseconds per step (lower is better).
-All inputs are seeded synthetic tensors (~N(0,1)); KV pages are drawn on the
-host and are resident in HBM before timing starts.
+All inputs are seeded synthetic tensors (~N(0,1)); the KV pages are drawn on
+the GPU by torch's seeded generator and are resident in HBM before timing
+starts.
 """
 from __future__ import annotations
 
@@ -115,6 +116,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only run the prefill leg (for counter runs of the prefill kernel)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times (the "
                          "known-size kernel that calibrates HBM byte counters) and exit")
@@ -131,6 +134,9 @@ def main():
     import full_gqa_decode_amd as fl
     fl.lib()
     dev = torch.device("cuda:0")
+    if args.prefill_only:
+        print(json.dumps(bench_prefill(fl, dev, None)), flush=True)
+        return
     eps = float(np.float32(1e-6))
     FULL = fl.layer(window=0, use_rope=0, rms_eps=eps)
     SLIDE = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps)
@@ -223,6 +229,24 @@ def main():
     us_unfused = e0.elapsed_time(e1) * 1e3 / args.steps
     log(f"bench: unfused (append, then decode) {us_unfused:.1f} us/step")
 
+    # K1 alone: the 49 appends of the new token, one graph
+    def appends():
+        for L in layers:
+            fl.flint_qk_norm_rope_append(FULL if L["full"] else SLIDE, L["q_in"], L["k_in"],
+                                         L["v_in"], ones, ones, pos, L["slots"], L["q_out"],
+                                         L["kc"], L["vc"])
+    g_app = capture(appends)
+    g_app.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(args.steps):
+            g_app.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us_append = e0.elapsed_time(e1) * 1e3 / args.steps
+    log(f"bench: append alone (49 layers) {us_append:.1f} us/step")
+
     # dominant kernel: the split-K kernel (K2) of a full layer, alone, through
     # flint_attn_decode_partials -- 14 full layers back to back in one graph,
     # timed on the stream it runs on; and the launch pair of the fused step
@@ -288,6 +312,7 @@ def main():
         "us_per_step_p10": round(float(np.percentile(per, 10)), 2),
         "us_per_step_p90": round(float(np.percentile(per, 90)), 2),
         "us_per_step_unfused": round(us_unfused, 2),
+        "us_per_step_append_alone": round(us_append, 2),
         "roofline": {"kernel": "decode_split_kernel (K2, split-K flash decode) of one full "
                                "layer over 100,000 keys, alone: 64 splits x 4 KV heads, launched "
                                "through flint_attn_decode_partials",
@@ -398,12 +423,19 @@ def copy_probe(dev):
 
 
 def bench_prefill(fl, dev, stream):
-    """Causal prefill of a 32,768-token prompt on one full layer (MFMA-bound):
-    append all tokens (bf16 q), then time the attention kernel alone."""
+    """Causal prefill of a 32,768-token prompt on one full layer (MFMA-bound)
+    and on one sliding layer (window 513, RoPE; near the balance of MFMA and
+    HBM): append all tokens (bf16 q), then time the attention kernel alone."""
+    full = prefill_leg(fl, dev, window=0)
+    full["sliding"] = prefill_leg(fl, dev, window=WINDOW)
+    return full
+
+
+def prefill_leg(fl, dev, window):
     import torch
     T = 32768
     eps = float(np.float32(1e-6))
-    L = fl.layer(window=0, use_rope=0, rms_eps=eps)
+    L = fl.layer(window=window, use_rope=1 if window else 0, rms_eps=eps)
     pages = T // PAGE
     bt, nb = synth.shuffled_block_table(SEED, (4, 0, synth.PERM), 1, [pages], pages)
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -434,15 +466,25 @@ def bench_prefill(fl, dev, stream):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    pairs = T * (T + 1) // 2
+    # (query, key) pairs the causal (windowed) mask keeps, 4*D flops each
+    i = np.arange(T, dtype=np.int64)
+    pairs = int(np.minimum(i + 1, window).sum()) if window else T * (T + 1) // 2
     flops = 4.0 * D * pairs * HQ
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"bench: prefill 32768 full layer {ms:.2f} ms, {tflops:.1f} TFLOP/s")
-    return {"workload": "causal prefill, 32,768-token prompt, one full layer (32 q / 4 KV heads)",
-            "ms": round(ms, 3), "flops": flops, "tflops": round(tflops, 1),
-            "bound": "mfma", "peak_tflops": BF16_DENSE_TFLOPS,
-            "mfma_frac": round(tflops / BF16_DENSE_TFLOPS, 4),
-            "finite": bool(torch.isfinite(out).all().item())}
+    # HBM bytes the kernel must move: q (bf16) in, out (fp32), K/V read once
+    nbytes = T * HQ * D * 2 + T * HQ * D * 4 + T * KV_BYTES_PER_TOKEN_LAYER
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    kind = f"sliding layer (window {window}, RoPE)" if window else "full layer"
+    log(f"bench: prefill 32768 {kind} {ms:.2f} ms, {tflops:.1f} TFLOP/s, {gbps:.0f} GB/s")
+    res = {"workload": f"causal prefill, 32,768-token prompt, one {kind} (32 q / 4 KV heads)",
+           "ms": round(ms, 3), "flops": flops, "tflops": round(tflops, 1),
+           "bound": "mfma", "peak_tflops": BF16_DENSE_TFLOPS,
+           "mfma_frac": round(tflops / BF16_DENSE_TFLOPS, 4),
+           "finite": bool(torch.isfinite(out).all().item())}
+    if window:
+        res.update({"bound": "mfma+hbm", "hbm_bytes": nbytes, "hbm_gbps": round(gbps, 1),
+                    "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    return res
 
 
 def cpu_baseline(layers, eps):
