@@ -46,13 +46,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const float* x = a.v_in + ((int64_t)t * hkv + g) * kHeadDim;
     const float v0 = x[lane], v1 = x[lane + 64];
     const int64_t page = slot / kPage, row = slot % kPage;
-    const int64_t o = (page * hkv + g) * (int64_t)(kHeadDim * kPage) + row;
+    const int64_t tile = (page * hkv + g) * (int64_t)(kHeadDim * kPage);
     if (a.kv_fp8) {
-      uint8_t* dst = (uint8_t*)a.v_cache + o;
-      dst[lane * kPage] = (uint8_t)fp8_e4m3_rne_f64((double)v0 / (double)a.v_scale);
-      dst[(lane + 64) * kPage] = (uint8_t)fp8_e4m3_rne_f64((double)v1 / (double)a.v_scale);
+      uint8_t* dst = (uint8_t*)a.v_cache + tile;
+      dst[fp8_v_off(row, lane)] = (uint8_t)fp8_e4m3_rne_f64((double)v0 / (double)a.v_scale);
+      dst[fp8_v_off(row, lane + 64)] =
+          (uint8_t)fp8_e4m3_rne_f64((double)v1 / (double)a.v_scale);
     } else {
-      uint16_t* dst = (uint16_t*)a.v_cache + o;
+      uint16_t* dst = (uint16_t*)a.v_cache + tile + row;
       dst[lane * kPage] = bf16_bits_rne(v0);
       dst[(lane + 64) * kPage] = bf16_bits_rne(v1);
     }
@@ -86,13 +87,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 
   const int g = task - hq;
   const int64_t page = slot / kPage, row = slot % kPage;
-  const int64_t o = ((page * hkv + g) * kPage + row) * kHeadDim;
+  const int64_t tile = (page * hkv + g) * (int64_t)(kHeadDim * kPage);
   if (a.kv_fp8) {
-    uint8_t* dst = (uint8_t*)a.k_cache + o;
-    dst[lane] = (uint8_t)fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
-    dst[lane + 64] = (uint8_t)fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
+    uint8_t* dst = (uint8_t*)a.k_cache + tile;
+    dst[fp8_k_off(row, lane)] = (uint8_t)fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
+    dst[fp8_k_off(row, lane + 64)] = (uint8_t)fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
   } else {
-    uint16_t* dst = (uint16_t*)a.k_cache + o;
+    uint16_t* dst = (uint16_t*)a.k_cache + tile + row * kHeadDim;
     dst[lane] = bf16_bits_rne_f64(y0);
     dst[lane + 64] = bf16_bits_rne_f64(y1);
   }

@@ -72,11 +72,12 @@ __device__ __forceinline__ void load_v(const DecodeArgs& a, int pg, int g, int n
     r.v[nb] = __builtin_nontemporal_load((const u32x2*)(vp + nb * 16 * kPage));
 }
 
-// fp8 cache (same index order, 1-byte elements).  Lane (n, gq) loads bytes
-// gq*32 .. gq*32+31 of K row n in two 16-byte loads, so the contraction's dim
-// order is permuted: element j of MFMA block c is dim gq*32 + c*8 + j, and the
-// q operand and the new token's K row follow the same order (kdim below).
-// V: the same 4 tokens x 1 dim per 16-dim block as bf16, one dword each.
+// fp8 cache, in its MFMA-native tile order (fp8_k_off / fp8_v_off): lane
+// (n, gq) gets dims gq*32 .. gq*32+31 of K row n, and 4 tokens x 1 dim of V
+// per 16-dim block (one dword each), from two 16-byte loads per tile, each
+// load instruction reading 1 KiB of contiguous bytes.  The contraction's dim
+// order is permuted to match: element j of MFMA block c is dim gq*32 + c*8 +
+// j, and the q operand and the new token's K row follow it (kdim below).
 struct PageRaw8 {
   u32x4 k[2];
   uint32_t v[8];
@@ -85,18 +86,22 @@ struct PageRaw8 {
 __device__ __forceinline__ void load_k(const DecodeArgs& a, int pg, int g, int n, int gq,
                                        PageRaw8& r) {
   const uint8_t* kp = (const uint8_t*)a.k_cache +
-                      (((int64_t)pg * a.num_kv_heads + g) * kPage + n) * kHeadDim + gq * 32;
+                      ((int64_t)pg * a.num_kv_heads + g) * (kPage * kHeadDim) + (gq * 16 + n) * 16;
   r.k[0] = __builtin_nontemporal_load((const u32x4*)kp);
-  r.k[1] = __builtin_nontemporal_load((const u32x4*)(kp + 16));
+  r.k[1] = __builtin_nontemporal_load((const u32x4*)(kp + 1024));
 }
 
 __device__ __forceinline__ void load_v(const DecodeArgs& a, int pg, int g, int n, int gq,
                                        PageRaw8& r) {
   const uint8_t* vp = (const uint8_t*)a.v_cache +
-                      (((int64_t)pg * a.num_kv_heads + g) * kHeadDim + n) * kPage + gq * 4;
+                      ((int64_t)pg * a.num_kv_heads + g) * (kPage * kHeadDim) + (gq * 16 + n) * 16;
+  const u32x4 lo = __builtin_nontemporal_load((const u32x4*)vp);
+  const u32x4 hi = __builtin_nontemporal_load((const u32x4*)(vp + 1024));
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
-    r.v[nb] = __builtin_nontemporal_load((const uint32_t*)(vp + nb * 16 * kPage));
+  for (int i = 0; i < 4; ++i) {
+    r.v[i] = lo[i];
+    r.v[4 + i] = hi[i];
+  }
 }
 
 // MFMA operands of a page: bf16 registers as loaded, or fp8 codes widened
@@ -415,9 +420,10 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
           sm_knew[lane] = (Elem)c0;
           sm_knew[lane + 64] = (Elem)c1;
           if (ok) {
-            uint8_t* dst = (uint8_t*)a.k_cache + o;
-            dst[lane] = (uint8_t)c0;
-            dst[lane + 64] = (uint8_t)c1;
+            uint8_t* dst = (uint8_t*)a.k_cache +
+                           ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage);
+            dst[fp8_k_off(t % kPage, lane)] = (uint8_t)c0;
+            dst[fp8_k_off(t % kPage, lane + 64)] = (uint8_t)c1;
           }
         } else {
           const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
@@ -439,9 +445,10 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
           sm_vnew[lane] = (Elem)c0;
           sm_vnew[lane + 64] = (Elem)c1;
           if (ok) {
-            uint8_t* dst = (uint8_t*)a.v_cache + o;
-            dst[lane * kPage] = (uint8_t)c0;
-            dst[(lane + 64) * kPage] = (uint8_t)c1;
+            uint8_t* dst = (uint8_t*)a.v_cache +
+                           ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage);
+            dst[fp8_v_off(t % kPage, lane)] = (uint8_t)c0;
+            dst[fp8_v_off(t % kPage, lane + 64)] = (uint8_t)c1;
           }
         } else {
           const uint16_t v0 = bf16_bits_rne(xv[lane]), v1 = bf16_bits_rne(xv[lane + 64]);

@@ -136,6 +136,19 @@ __device__ __forceinline__ uint32_t fp8_e4m3_rne_f64(double x) {
   return sign | (uint32_t)(((e + 6) << 3) + (int)m - 8);
 }
 
+// Byte offsets of K and V element (row, dim) inside the 2048-byte fp8 tile of
+// one (page, KV head).  Lane l = gq * 16 + n of a wave reads 16 contiguous
+// bytes at l * 16 and at 1024 + l * 16: for K, dims gq * 32 .. gq * 32 + 31 of
+// row n; for V, tokens gq * 4 .. gq * 4 + 3 of dims nb * 16 + n, nb = 0..7,
+// one dword per nb.  Each of those loads reads 1 KiB of contiguous bytes.
+__device__ __forceinline__ int fp8_k_off(int row, int dim) {
+  return ((dim >> 4) & 1) * 1024 + (dim >> 5) * 256 + row * 16 + (dim & 15);
+}
+__device__ __forceinline__ int fp8_v_off(int row, int dim) {
+  return (dim >> 6) * 1024 + ((row >> 2) * 16 + (dim & 15)) * 16 + ((dim >> 4) & 3) * 4 +
+         (row & 3);
+}
+
 // Four fp8 E4M3 codes (bytes 0..3 of w) -> bf16 values in byte order.  Exact:
 // every E4M3 value, subnormals included, is a normal bf16 number.  gfx950's
 // scaled conversion with scale 1.

@@ -51,9 +51,16 @@
  *
  * KV element formats (flint_attn_layer.kv_dtype)
  *   FLINT_KV_BF16: 2-byte bf16 elements (uint16 bit patterns), 4 KiB tiles.
- *   FLINT_KV_FP8_E4M3: 1-byte elements in the same index order (2 KiB
- *   tiles), halving the bytes decode streams ("Recursive Flint" model JSON,
- *   "kvCacheGiBPerRequest" lists an fp8 column beside bf16).  Reading of the
+ *   FLINT_KV_FP8_E4M3: 1-byte elements, still one contiguous tile per
+ *   (page, KV head), now 2 KiB, halving the bytes decode streams ("Recursive
+ *   Flint" model JSON, "kvCacheGiBPerRequest" lists an fp8 column beside
+ *   bf16).  Inside a tile the order is the one the matrix-core operands are
+ *   loaded in, so that every 64-lane load reads 1 KiB of contiguous bytes:
+ *     K[row][dim] at ((dim >> 4) & 1) * 1024 + (dim >> 5) * 256 + row * 16
+ *                    + (dim & 15)
+ *     V[row][dim] at (dim >> 6) * 1024 + ((row >> 2) * 16 + (dim & 15)) * 16
+ *                    + ((dim >> 4) & 3) * 4 + (row & 3)
+ *   (row = token within the page, tile at ((page * num_kv_heads + g) * 2048)).  Reading of the
  *   format: OCP E4M3 -- sign, 4 exponent bits of bias 7, 3 mantissa bits,
  *   subnormals, no infinities, S.1111.111 is NaN, largest finite 448.  The
  *   cache holds K / k_scale and V / v_scale (one pair of scales per layer):

@@ -73,6 +73,10 @@ def lib():
         L.orc_bf16_value.restype = C.c_double
         L.orc_bf16_value.argtypes = [C.c_uint16]
         L.orc_bf16_rne_array.argtypes = [P, P, C.c_int64]
+        for name in ("orc_k_offset", "orc_v_offset"):
+            f = getattr(L, name)
+            f.restype = C.c_int64
+            f.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_int]
         L.orc_fp8_rne.restype = C.c_uint8
         L.orc_fp8_rne.argtypes = [C.c_double]
         L.orc_fp8_value.restype = C.c_double
@@ -162,6 +166,8 @@ def append(L: Layer, q_in, k_in, v_in, qw, kw, positions, slots, k_cache, v_cach
     rc = lib().orc_append(C.byref(L), T, _p(q_in), _p(k_in), _p(v_in), _p(_c(qw, np.float32)),
                           _p(_c(kw, np.float32)), _p(positions), _p(slots), _p(q_out),
                           _p(k_cache), _p(v_cache), num_blocks)
+    if rc == -2:
+        raise ValueError("oracle append: an fp8 cache needs d = 128 and bs = 16")
     if rc != 0:
         raise ValueError("oracle append: slot out of range")
     return q_out
@@ -179,6 +185,8 @@ def attn_decode(L: Layer, q, k_cache, v_cache, block_tables, seq_lens, sinks, nt
     rc = lib().orc_attn_decode(C.byref(L), B, _p(q), _p(_cache(L, k_cache)),
                                _p(_cache(L, v_cache)), num_blocks,
                                _p(bt), bt.shape[1], _p(sl), _p(sk), _p(out), int(nthreads))
+    if rc == -2:
+        raise ValueError("oracle decode: an fp8 cache needs d = 128 and bs = 16")
     if rc != 0:
         raise ValueError("oracle decode: bad page id or seq_len")
     return out
@@ -222,9 +230,40 @@ def attn_prefill(L: Layer, q, cu_q_lens, k_cache, v_cache, block_tables, seq_len
                                 _p(_cache(L, v_cache)),
                                 num_blocks, _p(bt), bt.shape[1], _p(sl), _p(sk), _p(out), _p(r),
                                 0 if r is None else r.shape[0], int(nthreads))
+    if rc == -2:
+        raise ValueError("oracle prefill: an fp8 cache needs d = 128 and bs = 16")
     if rc != 0:
         raise ValueError("oracle prefill: bad row, page id or seq_len")
     return out
+
+
+# --- cache layout ----------------------------------------------------------------
+def k_offsets(L: Layer, page, g, row) -> np.ndarray:
+    """Element offsets, in dim order, of one K row in its cache array."""
+    f = lib().orc_k_offset
+    return np.array([f(C.byref(L), int(page), int(g), int(row), i) for i in range(L.d)], np.int64)
+
+
+def v_offsets(L: Layer, page, g, row) -> np.ndarray:
+    """Element offsets, in dim order, of one token's V values in its cache array."""
+    f = lib().orc_v_offset
+    return np.array([f(C.byref(L), int(page), int(g), int(row), i) for i in range(L.d)], np.int64)
+
+
+def k_row(L: Layer, cache, page, g, row) -> np.ndarray:
+    return np.asarray(cache).reshape(-1)[k_offsets(L, page, g, row)]
+
+
+def v_row(L: Layer, cache, page, g, row) -> np.ndarray:
+    return np.asarray(cache).reshape(-1)[v_offsets(L, page, g, row)]
+
+
+def put_k_row(L: Layer, cache, page, g, row, values) -> None:
+    cache.reshape(-1)[k_offsets(L, page, g, row)] = values
+
+
+def put_v_row(L: Layer, cache, page, g, row, values) -> None:
+    cache.reshape(-1)[v_offsets(L, page, g, row)] = values
 
 
 # --- fp8 E4M3 ------------------------------------------------------------------

@@ -147,14 +147,28 @@ int64_t orc_slot(const int32_t* bt, int bt_stride, int bs, int b, int pos) {
   return (int64_t)page * bs + pos % bs;
 }
 
-/* K element (page, g, row, dim) sits at k_index + dim; V element at
- * v_index + dim * bs (V pages are stored dim-major). */
-static inline int64_t k_index(const orc_layer* L, int64_t page, int g, int row) {
-  return ((page * L->hkv + g) * L->bs + row) * L->d;
+/* Cache layout (the library's own convention; the pages fix none).  Each
+ * (page, KV head g) owns one contiguous tile of bs * d elements.
+ * bf16: K is token-major (element row * d + dim), V dim-major (dim * bs + row).
+ * fp8 (d = 128, bs = 16 only), within the 2048-byte tile:
+ *   K: ((dim >> 4) & 1) * 1024 + (dim >> 5) * 256 + row * 16 + (dim & 15)
+ *   V: (dim >> 6) * 1024 + ((row >> 2) * 16 + (dim & 15)) * 16
+ *      + ((dim >> 4) & 3) * 4 + (row & 3) */
+int64_t orc_k_offset(const orc_layer* L, int64_t page, int g, int row, int dim) {
+  const int64_t tile = (page * L->hkv + g) * (int64_t)L->bs * L->d;
+  if (L->kv_fp8) return tile + ((dim >> 4) & 1) * 1024 + (dim >> 5) * 256 + row * 16 + (dim & 15);
+  return tile + (int64_t)row * L->d + dim;
 }
-static inline int64_t v_index(const orc_layer* L, int64_t page, int g, int row) {
-  return (page * L->hkv + g) * (int64_t)L->d * L->bs + row;
+int64_t orc_v_offset(const orc_layer* L, int64_t page, int g, int row, int dim) {
+  const int64_t tile = (page * L->hkv + g) * (int64_t)L->bs * L->d;
+  if (L->kv_fp8)
+    return tile + (dim >> 6) * 1024 + ((row >> 2) * 16 + (dim & 15)) * 16 + ((dim >> 4) & 3) * 4 +
+           (row & 3);
+  return tile + (int64_t)dim * L->bs + row;
 }
+
+/* the fp8 tile order above is defined for d = 128 and bs = 16 only */
+static int bad_shape(const orc_layer* L) { return L->kv_fp8 && (L->d != 128 || L->bs != 16); }
 
 /* O4: norm -> rope -> cache write, in that order (reading of the vLLM day-0
  * post, "What happened": fused normalisation, rotary and cache operations). */
@@ -163,6 +177,7 @@ int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
                const int32_t* positions, const int32_t* slots,
                double* q_out, void* kc, void* vc, int num_blocks) {
   const int d = L->d;
+  if (bad_shape(L)) return -2;
   double* tmp = (double*)malloc(sizeof(double) * d);
   int rc = 0;
   for (int t = 0; t < T; ++t) {
@@ -182,15 +197,15 @@ int orc_append(const orc_layer* L, int T, const float* q_in, const float* k_in,
     for (int g = 0; g < L->hkv; ++g) {
       orc_rmsnorm(k_in + ((int64_t)t * L->hkv + g) * d, kw, d, L->eps, tmp);
       if (L->use_rope) orc_rope(tmp, d, pos, L->theta);
-      const int64_t kr = k_index(L, page, g, row), vr = v_index(L, page, g, row);
       const float* v = v_in + ((int64_t)t * L->hkv + g) * d;
       for (int i = 0; i < d; ++i) {
+        const int64_t ko = orc_k_offset(L, page, g, row, i), vo = orc_v_offset(L, page, g, row, i);
         if (L->kv_fp8) {
-          ((uint8_t*)kc)[kr + i] = orc_fp8_rne(tmp[i] / L->k_scale);
-          ((uint8_t*)vc)[vr + (int64_t)i * L->bs] = orc_fp8_rne((double)v[i] / L->v_scale);
+          ((uint8_t*)kc)[ko] = orc_fp8_rne(tmp[i] / L->k_scale);
+          ((uint8_t*)vc)[vo] = orc_fp8_rne((double)v[i] / L->v_scale);
         } else {
-          ((uint16_t*)kc)[kr + i] = bf16_rne_double(tmp[i]);
-          ((uint16_t*)vc)[vr + (int64_t)i * L->bs] = orc_bf16_rne(v[i]);
+          ((uint16_t*)kc)[ko] = bf16_rne_double(tmp[i]);
+          ((uint16_t*)vc)[vo] = orc_bf16_rne(v[i]);
         }
       }
     }
@@ -213,15 +228,14 @@ static int attend_row(const orc_layer* L, const double* qh, int h, const void* k
   if (lo < 0) lo = 0;
   int n = t - lo + 1;
   double* s = (double*)malloc(sizeof(double) * (size_t)n);
-  int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+  int32_t* pages = (int32_t*)malloc(sizeof(int32_t) * (size_t)n);
   double m = sink;
   for (int j = lo; j <= t; ++j) {
     int32_t page = bt[(int64_t)b * bt_stride + j / L->bs];
-    if (page < 0 || page >= num_blocks) { free(s); free(rows); return -1; }
-    int64_t r = k_index(L, page, g, j % L->bs);
-    rows[j - lo] = v_index(L, page, g, j % L->bs);
+    if (page < 0 || page >= num_blocks) { free(s); free(pages); return -1; }
+    pages[j - lo] = page;
     double dot = 0.0;
-    for (int i = 0; i < d; ++i) dot += qh[i] * k_at(L, kc, r + i);
+    for (int i = 0; i < d; ++i) dot += qh[i] * k_at(L, kc, orc_k_offset(L, page, g, j % L->bs, i));
     s[j - lo] = L->scale * dot;
     if (s[j - lo] > m) m = s[j - lo];
   }
@@ -230,11 +244,12 @@ static int attend_row(const orc_layer* L, const double* qh, int h, const void* k
   for (int j = 0; j < n; ++j) {
     double e = exp(s[j] - m);
     z += e;
-    for (int i = 0; i < d; ++i) out[i] += e * v_at(L, vc, rows[j] + (int64_t)i * L->bs);
+    const int row = (lo + j) % L->bs;
+    for (int i = 0; i < d; ++i) out[i] += e * v_at(L, vc, orc_v_offset(L, pages[j], g, row, i));
   }
   for (int i = 0; i < d; ++i) out[i] /= z;
   free(s);
-  free(rows);
+  free(pages);
   return 0;
 }
 
@@ -249,6 +264,7 @@ int orc_default_threads(void) {
 int orc_attn_decode(const orc_layer* L, int B, const double* q, const void* kc,
                     const void* vc, int num_blocks, const int32_t* bt, int bt_stride,
                     const int32_t* seq_lens, const float* sinks, double* out, int nthreads) {
+  if (bad_shape(L)) return -2;
   if (nthreads <= 0) nthreads = orc_default_threads();
   int bad = 0;
   const int64_t items = (int64_t)B * L->hq;
@@ -272,23 +288,25 @@ void orc_attn_partial(const orc_layer* L, const double* qh, int h, const void* k
                       int j0, int j1, double* ot, double* lse) {
   const int d = L->d, g = h / (L->hq / L->hkv);
   for (int i = 0; i < d; ++i) ot[i] = 0.0;
+  if (bad_shape(L)) { *lse = NAN; return; }
   if (j1 <= j0) { *lse = -INFINITY; return; }
   int n = j1 - j0;
   double* s = (double*)malloc(sizeof(double) * (size_t)n);
   double m = -INFINITY;
   for (int j = j0; j < j1; ++j) {
-    int64_t r = k_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
+    const int32_t page = bt[(int64_t)b * bt_stride + j / L->bs];
     double dot = 0.0;
-    for (int i = 0; i < d; ++i) dot += qh[i] * k_at(L, kc, r + i);
+    for (int i = 0; i < d; ++i) dot += qh[i] * k_at(L, kc, orc_k_offset(L, page, g, j % L->bs, i));
     s[j - j0] = L->scale * dot;
     if (s[j - j0] > m) m = s[j - j0];
   }
   double l = 0.0;
   for (int j = j0; j < j1; ++j) {
-    int64_t r = v_index(L, bt[(int64_t)b * bt_stride + j / L->bs], g, j % L->bs);
+    const int32_t page = bt[(int64_t)b * bt_stride + j / L->bs];
     double e = exp(s[j - j0] - m);
     l += e;
-    for (int i = 0; i < d; ++i) ot[i] += e * v_at(L, vc, r + (int64_t)i * L->bs);
+    for (int i = 0; i < d; ++i)
+      ot[i] += e * v_at(L, vc, orc_v_offset(L, page, g, j % L->bs, i));
   }
   for (int i = 0; i < d; ++i) ot[i] /= l;
   *lse = m + log(l);
@@ -316,6 +334,7 @@ int orc_attn_prefill(const orc_layer* L, int B, const double* q, const int32_t* 
                      const int32_t* bt, int bt_stride, const int32_t* seq_lens,
                      const float* sinks, double* out, const int32_t* rows, int nrows,
                      int nthreads) {
+  if (bad_shape(L)) return -2;
   if (nthreads <= 0) nthreads = orc_default_threads();
   const int64_t total_q = cu[B];
   const int64_t nr = rows ? nrows : total_q;

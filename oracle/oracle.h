@@ -64,6 +64,18 @@ void orc_bf16_rne_array(const double* x, uint16_t* y, int64_t n);
 uint8_t orc_fp8_rne(double x);
 double orc_fp8_value(uint8_t c);
 
+/* Cache layout (the library's convention): element offset of K / V element
+ * (page, KV head g, row, dim) in its cache array.  Each (page, g) owns one
+ * contiguous tile of bs * d elements.  bf16: K token-major (row * d + dim), V
+ * dim-major (dim * bs + row).  fp8 E4M3 (d = 128, bs = 16 only; the other
+ * functions return -2, or a NaN lse, for an fp8 layer of another shape), in
+ * the 2048-byte tile:
+ *   K: ((dim >> 4) & 1) * 1024 + (dim >> 5) * 256 + row * 16 + (dim & 15)
+ *   V: (dim >> 6) * 1024 + ((row >> 2) * 16 + (dim & 15)) * 16
+ *      + ((dim >> 4) & 3) * 4 + (row & 3) */
+int64_t orc_k_offset(const orc_layer* L, int64_t page, int g, int row, int dim);
+int64_t orc_v_offset(const orc_layer* L, int64_t page, int g, int row, int dim);
+
 /* O2: per-head RMSNorm: y = x / sqrt(mean(x^2) + eps) * w, n values. */
 void orc_rmsnorm(const float* x, const float* w, int n, double eps, double* y);
 

@@ -566,6 +566,39 @@ def _fp8_layer(**kw):
     return oracle.layer(kv_fp8=1, **kw)
 
 
+def test_cache_tile_orders_follow_the_abi_header():
+    # the layouts include/flint.h documents, written out here from that text:
+    # bf16 K token-major, V dim-major; fp8 in its MFMA-native tile order.
+    # Every (row, dim) of a tile lands on a distinct element of that tile.
+    for fp8 in (0, 1):
+        L = oracle.layer(kv_fp8=fp8, hkv=4)
+        for page, g in ((0, 0), (5, 3)):
+            tile = (page * 4 + g) * 2048
+            ks, vs = set(), set()
+            for r in range(16):
+                ko, vo = oracle.k_offsets(L, page, g, r), oracle.v_offsets(L, page, g, r)
+                for d in range(128):
+                    if fp8:
+                        k_ref = ((d >> 4) & 1) * 1024 + (d >> 5) * 256 + r * 16 + (d & 15)
+                        v_ref = ((d >> 6) * 1024 + ((r >> 2) * 16 + (d & 15)) * 16
+                                 + ((d >> 4) & 3) * 4 + (r & 3))
+                    else:
+                        k_ref, v_ref = r * 128 + d, d * 16 + r
+                    assert ko[d] == tile + k_ref and vo[d] == tile + v_ref
+                ks.update(ko.tolist())
+                vs.update(vo.tolist())
+            assert ks == vs == set(range(tile, tile + 2048))
+
+
+def test_fp8_needs_the_flint_tile_shape():
+    L = _fp8_layer(hq=4, hkv=2, d=8, bs=4)
+    kc = np.zeros((2, 2, 4, 8), np.uint8)
+    x = np.zeros((1, 2, 8), np.float32)
+    with pytest.raises(ValueError):
+        oracle.append(L, np.zeros((1, 4, 8), np.float32), x, x, np.ones(8), np.ones(8), [0], [0],
+                      kc, kc.copy())
+
+
 def test_fp8_append_places_scaled_codes():
     # V codes are the rounding of v / v_scale (fp32 inputs: torch rounds the
     # same real when v_scale is a power of two); K codes are within one code of
@@ -583,49 +616,53 @@ def test_fp8_append_places_scaled_codes():
     kc = np.full((nb, 4, 16, 128), 0x5A, np.uint8)
     vc = np.full((nb, 4, 128, 16), 0x5A, np.uint8)
     oracle.append(L, q, k, v, ones, ones, pos, slots, kc, vc)
-    written = np.zeros((nb, 16), bool)
+    kw = np.zeros(kc.size, bool)
+    vw = np.zeros(vc.size, bool)
     for t in range(T):
         if slots[t] < 0:
             continue
         pg, r = divmod(int(slots[t]), 16)
-        written[pg, r] = True
-        assert np.array_equal(vc[pg, :, :, r], _torch_fp8_codes(v[t] / np.float32(2.0)))
         for g in range(4):
+            kw[oracle.k_offsets(L, pg, g, r)] = True
+            vw[oracle.v_offsets(L, pg, g, r)] = True
+            assert np.array_equal(oracle.v_row(L, vc, pg, g, r),
+                                  _torch_fp8_codes(v[t, g] / np.float32(2.0)))
             kk = oracle.rope(oracle.rmsnorm(k[t, g], ones), pos[t]) / 0.25
             ref = _torch_fp8_values(_torch_fp8_codes(kk.astype(np.float32)))
-            got = oracle.fp8_value(kc[pg, g, r])
+            got = oracle.fp8_value(oracle.k_row(L, kc, pg, g, r))
             ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0**-6))) - 3)
             assert np.all(np.abs(got - ref) <= ulp)
-    assert np.all(kc.transpose(0, 2, 1, 3)[~written] == 0x5A)
-    assert np.all(vc.transpose(0, 3, 1, 2)[~written] == 0x5A)
+    assert kw.sum() == vw.sum() == (T - 1) * 4 * 128
+    assert np.all(kc.reshape(-1)[~kw] == 0x5A) and np.all(vc.reshape(-1)[~vw] == 0x5A)
     # values beyond 448 * v_scale saturate instead of turning into NaN
     v2 = np.full((1, 4, 128), 2000.0, np.float32)
     oracle.append(L, q[:1], k[:1], v2, ones, ones, pos[:1], slots[:1], kc, vc)
     pg, r = divmod(int(slots[0]), 16)
-    assert (vc[pg, :, :, r] == 0x7E).all()
+    assert all((oracle.v_row(L, vc, pg, g, r) == 0x7E).all() for g in range(4))
 
 
 def test_fp8_attention_is_bf16_attention_of_the_dequantised_cache():
     # attention over fp8 codes with scales equals attention over a bf16 cache
     # holding code value x scale (exact in bf16 for power-of-two scales),
-    # which the brute-force pins above tie to the definition
+    # which the brute-force pins above tie to the definition; one KV group of
+    # the Flint tile shape (d = 128, 16-token pages), two pages
     for window in (0, 5):
-        L8 = _fp8_layer(window=window, hq=4, hkv=2, d=8, bs=4, k_scale=0.5, v_scale=4.0)
-        L16 = _small_layer(window)
-        n = 11
-        kcode = synth.fp8_codes(42, (1, window), (n, L8.hkv, L8.d))          # |k| < 2
-        vcode = synth.fp8_codes(42, (2, window), (n, L8.hkv, L8.d), 0x7E)    # all finite codes
+        L8 = _fp8_layer(window=window, hq=8, hkv=1, k_scale=0.5, v_scale=4.0)
+        L16 = oracle.layer(window=window, hq=8, hkv=1)
+        n = 21
+        kcode = synth.fp8_codes(42, (1, window), (n, 1, 128))          # |k| < 2
+        vcode = synth.fp8_codes(42, (2, window), (n, 1, 128), 0x7E)    # all finite codes
         kb = _torch_bf16_bits(oracle.fp8_value(kcode) * 0.5)
         vb = _torch_bf16_bits(oracle.fp8_value(vcode) * 4.0)
-        q = synth.normal(42, (3, window), (L8.hq, L8.d)).astype(np.float64)
-        sinks = synth.normal(42, (4, window), L8.hq)
+        q = synth.normal(42, (3, window), (8, 128)).astype(np.float64) * 0.1
+        sinks = synth.normal(42, (4, window), 8)
         kc16, vc16, bt = _paged(L16, kb, vb, seed=9)
         kc8 = np.zeros(kc16.shape, np.uint8)
         vc8 = np.zeros(vc16.shape, np.uint8)
         for p in range(n):
-            pg, r = bt[0, p // 4], p % 4
-            kc8[pg, :, r, :] = kcode[p]
-            vc8[pg, :, :, r] = vcode[p]
+            pg, r = bt[0, p // 16], p % 16
+            oracle.put_k_row(L8, kc8, pg, 0, r, kcode[p, 0])
+            oracle.put_v_row(L8, vc8, pg, 0, r, vcode[p, 0])
         sl = np.array([n], np.int32)
         out8 = oracle.attn_decode(L8, q[None], kc8, vc8, bt, sl, sinks)[0]
         out16 = oracle.attn_decode(L16, q[None], kc16, vc16, bt, sl, sinks)[0]
