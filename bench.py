@@ -428,14 +428,17 @@ def bench_prefill(fl, dev, stream):
     HBM): append all tokens (bf16 q), then time the attention kernel alone."""
     full = prefill_leg(fl, dev, window=0)
     full["sliding"] = prefill_leg(fl, dev, window=WINDOW)
+    full["fp8"] = prefill_leg(fl, dev, window=0, fp8=True)
     return full
 
 
-def prefill_leg(fl, dev, window):
+def prefill_leg(fl, dev, window, fp8=False):
     import torch
     T = 32768
     eps = float(np.float32(1e-6))
-    L = fl.layer(window=window, use_rope=1 if window else 0, rms_eps=eps)
+    kv = dict(kv_dtype=fl.FLINT_KV_FP8_E4M3, k_scale=FP8_SCALES[0], v_scale=FP8_SCALES[1]) \
+        if fp8 else {}
+    L = fl.layer(window=window, use_rope=1 if window else 0, rms_eps=eps, **kv)
     pages = T // PAGE
     bt, nb = synth.shuffled_block_table(SEED, (4, 0, synth.PERM), 1, [pages], pages)
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -447,8 +450,9 @@ def prefill_leg(fl, dev, window):
                .astype(np.int32))
     pos = up(np.arange(T, dtype=np.int32))
     ones = torch.ones(D, dtype=torch.float32, device=dev)
-    kc = torch.empty((nb, HKV, PAGE, D), dtype=torch.int16, device=dev)
-    vc = torch.empty((nb, HKV, D, PAGE), dtype=torch.int16, device=dev)
+    cdt = torch.uint8 if fp8 else torch.int16
+    kc = torch.empty((nb, HKV, PAGE, D), dtype=cdt, device=dev)
+    vc = torch.empty((nb, HKV, D, PAGE), dtype=cdt, device=dev)
     qb = torch.empty((T, HQ, D), dtype=torch.int16, device=dev)
     fl.flint_qk_norm_rope_append(L, q, k, v, ones, ones, pos, slots, qb, kc, vc)
     out = torch.empty((T, HQ, D), dtype=torch.float32, device=dev)
@@ -472,9 +476,11 @@ def prefill_leg(fl, dev, window):
     flops = 4.0 * D * pairs * HQ
     tflops = flops / (ms * 1e-3) / 1e12
     # HBM bytes the kernel must move: q (bf16) in, out (fp32), K/V read once
-    nbytes = T * HQ * D * 2 + T * HQ * D * 4 + T * KV_BYTES_PER_TOKEN_LAYER
+    nbytes = T * HQ * D * 2 + T * HQ * D * 4 + T * KV_BYTES_PER_TOKEN_LAYER // (2 if fp8 else 1)
     gbps = nbytes / (ms * 1e-3) / 1e9
     kind = f"sliding layer (window {window}, RoPE)" if window else "full layer"
+    if fp8:
+        kind += ", fp8 E4M3 cache"
     log(f"bench: prefill 32768 {kind} {ms:.2f} ms, {tflops:.1f} TFLOP/s, {gbps:.0f} GB/s")
     res = {"workload": f"causal prefill, 32,768-token prompt, one {kind} (32 q / 4 KV heads)",
            "ms": round(ms, 3), "flops": flops, "tflops": round(tflops, 1),

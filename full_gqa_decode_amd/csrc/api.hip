@@ -477,8 +477,6 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
   (void)workspace_bytes;
   flint_status st = check_layer(L);
   if (st != FLINT_OK) return st;
-  if (L->kv_dtype != FLINT_KV_BF16)
-    return fail(FLINT_ERR_UNSUPPORTED, "prefill reads bf16 caches only");
   if (num_seqs < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
   if (max_seq_len < 1 || max_seq_len > kMaxContext)
     return fail(FLINT_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [1, %d]", max_seq_len,
@@ -499,8 +497,8 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
   flint::PrefillArgs a;
   a.q = q;
   a.cu_q_lens = cu_q_lens;
-  a.k_cache = (const uint16_t*)k_cache;
-  a.v_cache = (const uint16_t*)v_cache;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.sinks = sinks;
@@ -512,7 +510,9 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
   a.window = L->window;
   a.max_q_len = max_q_len;
   a.max_seq_len = max_seq_len;
-  a.qscale = L->softmax_scale * 1.4426950408889634f;
+  a.kv_fp8 = L->kv_dtype == FLINT_KV_FP8_E4M3;
+  a.qscale = L->softmax_scale * 1.4426950408889634f * (a.kv_fp8 ? L->k_scale : 1.f);
+  a.v_scale = a.kv_fp8 ? L->v_scale : 1.f;
   return hip_status(flint::launch_prefill(a, (hipStream_t)stream), "prefill launch");
 }
 

@@ -75,8 +75,8 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 struct PrefillArgs {
   const uint16_t* q;         // [total_q][Hq][128] bf16
   const int32_t* cu_q_lens;  // [B+1]
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  const void* k_cache;       // bf16 bits, or fp8 codes in the fp8 tile order (kv_fp8)
+  const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
   const float* sinks;
@@ -88,7 +88,9 @@ struct PrefillArgs {
   int32_t window;
   int32_t max_q_len;
   int32_t max_seq_len;
-  float qscale;              // softmax_scale * log2(e)
+  float qscale;              // softmax_scale * log2(e) (* k_scale for an fp8 cache)
+  int32_t kv_fp8;
+  float v_scale;             // multiplies the output (1 for bf16)
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 

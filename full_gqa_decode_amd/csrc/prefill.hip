@@ -24,7 +24,9 @@
 // is split into bf16(p) and its bf16 remainder (two MFMAs) so the value
 // product is fp32-accurate.  Online softmax in log2 units with a lazy
 // reference max (moved only when a score exceeds it by 2^8), the sink joining
-// the denominator in the epilogue.
+// the denominator in the epilogue.  An fp8 E4M3 cache is widened to bf16
+// (exactly) as its pages are staged, with k_scale in the score scale and
+// v_scale applied to the output.
 // Bound: the matrix cores for full layers (4*D flops per (query, key) pair).
 #include "device.h"
 #include "launch.h"
@@ -53,19 +55,44 @@ struct PairRegs {
   u32x4 v[8];           // V: keys gq*4..+3 of page a and of page b, one dim
 };
 
-// This thread's 16-byte K and V chunks of the pair (pga, pgb).
+// This thread's chunks of the pair (pga, pgb): K row c>>4, dims
+// (c&15)*8 .. +7 and V dim c>>1, keys (c&1)*8 .. +7 of page sel.  bf16: one
+// 16-byte load each.  fp8 (KV8): the same elements as codes, 8 bytes of K and
+// two 4-byte runs of V in the fp8 tile order, held in the low dwords and
+// widened to bf16 when staged.
+template <bool KV8>
 __device__ __forceinline__ void fetch_pair(const PrefillArgs& a, int pga, int pgb, int g, int tid,
                                            u32x4& kr, u32x4& vr) {
   const int sel = tid >> 8, c = tid & 255;
   const int64_t pg = sel ? pgb : pga;
   const int64_t tile = (pg * a.num_kv_heads + g) * (kPage * kHeadDim);
-  kr = *(const u32x4*)(a.k_cache + tile + (c >> 4) * kHeadDim + (c & 15) * 8);
-  vr = *(const u32x4*)(a.v_cache + tile + (c >> 1) * kPage + (c & 1) * 8);
+  if constexpr (KV8) {
+    const uint8_t* kt = (const uint8_t*)a.k_cache + tile;
+    const uint8_t* vt = (const uint8_t*)a.v_cache + tile;
+    const u32x2 k8 = *(const u32x2*)(kt + fp8_k_off(c >> 4, (c & 15) * 8));
+    const int d = c >> 1, key = (c & 1) * 8;
+    kr = u32x4{k8[0], k8[1], 0u, 0u};
+    vr = u32x4{*(const uint32_t*)(vt + fp8_v_off(key, d)),
+               *(const uint32_t*)(vt + fp8_v_off(key + 4, d)), 0u, 0u};
+  } else {
+    const uint16_t* kt = (const uint16_t*)a.k_cache + tile;
+    const uint16_t* vt = (const uint16_t*)a.v_cache + tile;
+    kr = *(const u32x4*)(kt + (c >> 4) * kHeadDim + (c & 15) * 8);
+    vr = *(const u32x4*)(vt + (c >> 1) * kPage + (c & 1) * 8);
+  }
 }
 
-__device__ __forceinline__ void stage_pair(unsigned char* buf, int tid, const u32x4& kr,
-                                           const u32x4& vr) {
+template <bool KV8>
+__device__ __forceinline__ void stage_pair(unsigned char* buf, int tid, u32x4 kr, u32x4 vr) {
   const int sel = tid >> 8, c = tid & 255;
+  if constexpr (KV8) {  // codes -> bf16 (exact), same elements in the same order
+    const u32x2 k0 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(kr[0]));
+    const u32x2 k1 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(kr[1]));
+    const u32x2 v0 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(vr[0]));
+    const u32x2 v1 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(vr[1]));
+    kr = u32x4{k0[0], k0[1], k1[0], k1[1]};
+    vr = u32x4{v0[0], v0[1], v1[0], v1[1]};
+  }
   *(u32x4*)(buf + (sel * kPage + (c >> 4)) * kKStride + (c & 15) * 16) = kr;
   // V chunk: dim c>>1, keys h*8..h*8+7 = key groups 2h and 2h+1 of page sel
   unsigned char* vrow = buf + kKBytes + (c >> 1) * kVStride + sel * 8;
@@ -85,7 +112,7 @@ __device__ __forceinline__ void read_pair(const unsigned char* buf, int n, int g
     r.v[nb] = *(const u32x4*)(buf + kKBytes + (nb * 16 + n) * kVStride + gq * 16);
 }
 
-template <bool WINDOWED>
+template <bool WINDOWED, bool KV8>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sm[2][kBufBytes];
   const int ntile = gridDim.x;
@@ -176,7 +203,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     if (j < npairs) {
       int pga, pgb;
       check_ids(j, ia, ib, pga, pgb);
-      fetch_pair(a, pga, pgb, g, tid, kr, vr);
+      fetch_pair<KV8>(a, pga, pgb, g, tid, kr, vr);
     }
   };
 
@@ -302,7 +329,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     load_ids(1, ia1, ib1);
     load_ids(2, ia2, ib2);
     fetch(0, ia0, ib0, kr0, vr0);
-    stage_pair(sm[0], tid, kr0, vr0);
+    stage_pair<KV8>(sm[0], tid, kr0, vr0);
     fetch(1, ia1, ib1, kr1, vr1);
     fetch(2, ia2, ib2, kr0, vr0);
     load_ids(3, ia1, ib1);
@@ -311,13 +338,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   __syncthreads();
   for (int i = 0; i < npairs; i += 2) {
     compute(i);
-    if (i + 1 < npairs) stage_pair(sm[1], tid, kr1, vr1);
+    if (i + 1 < npairs) stage_pair<KV8>(sm[1], tid, kr1, vr1);
     fetch(i + 3, ia1, ib1, kr1, vr1);
     load_ids(i + 5, ia1, ib1);
     __syncthreads();
     if (i + 1 >= npairs) break;
     compute(i + 1);
-    if (i + 2 < npairs) stage_pair(sm[0], tid, kr0, vr0);
+    if (i + 2 < npairs) stage_pair<KV8>(sm[0], tid, kr0, vr0);
     fetch(i + 4, ia0, ib0, kr0, vr0);
     load_ids(i + 6, ia0, ib0);
     __syncthreads();
@@ -342,10 +369,11 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       const float M2 = fmaxf(m, sink);
       const float so = exp2_fast(m - M2);
       const float inv = 1.f / (l * so + exp2_fast(sink - M2));
+      const float vs = KV8 ? a.v_scale : 1.f;
       float* dst = a.out + ((int64_t)(q0 + r) * hq + h) * kHeadDim + n;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
-        dst[nb * 16] = bad ? __builtin_nanf("") : acc[mt][nb][i] * so * inv;
+        dst[nb * 16] = bad ? __builtin_nanf("") : acc[mt][nb][i] * so * inv * vs;
     }
   }
 }
@@ -355,8 +383,16 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
   const dim3 grid((a.max_q_len + kRows - 1) / kRows, a.num_kv_heads, a.num_seqs);
-  if (a.window > 0) hipLaunchKernelGGL((prefill_kernel<true>), grid, dim3(kPThreads), 0, st, a);
-  else hipLaunchKernelGGL((prefill_kernel<false>), grid, dim3(kPThreads), 0, st, a);
+  if (a.kv_fp8) {
+    if (a.window > 0)
+      hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kPThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<false, true>), grid, dim3(kPThreads), 0, st, a);
+  } else if (a.window > 0) {
+    hipLaunchKernelGGL((prefill_kernel<true, false>), grid, dim3(kPThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<false, false>), grid, dim3(kPThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

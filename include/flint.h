@@ -267,7 +267,7 @@ flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32
  * Same per-row result as decode; the sink joins every row's denominator.
  * Rows of a request with q_len > seq_len or seq_len > max_seq_len, or whose
  * pages include an id outside [0, num_blocks), are set to NaN.
- * bf16 caches only: an fp8 layer returns FLINT_ERR_UNSUPPORTED.
+ * An fp8 cache is widened to bf16 (exactly) as its pages are staged.
  */
 size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_seq_len);

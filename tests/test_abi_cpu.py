@@ -114,12 +114,12 @@ def test_fp8_layer_needs_positive_finite_scales(k_scale, v_scale):
     assert _decode(L, q=None) == INVALID and "NULL" in fl.lib().flint_last_error().decode()
 
 
-def test_prefill_rejects_an_fp8_layer():
+def test_prefill_checks_fp8_scales():
     lib = fl.lib()
-    L = fl.full_layer(kv_dtype=fl.FLINT_KV_FP8_E4M3, k_scale=0.5, v_scale=2.0)
+    L = fl.full_layer(kv_dtype=fl.FLINT_KV_FP8_E4M3, k_scale=0.0, v_scale=2.0)
     args = [C.byref(L), 1, P, P + 0x10000, 32, Q, Q + 0x10000, 4, P + 0x20000, 4, P + 0x30000,
             64, P + 0x40000, P + 0x50000, None, 0, None]
-    assert lib.flint_attn_prefill(*args) == UNSUPPORTED
+    assert lib.flint_attn_prefill(*args) == INVALID
 
 
 def test_zero_requests_is_a_no_op():
