@@ -93,9 +93,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     dst[fp8_k_off(row, lane)] = (uint8_t)fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
     dst[fp8_k_off(row, lane + 64)] = (uint8_t)fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
   } else {
-    uint16_t* dst = (uint16_t*)a.k_cache + tile + row * kHeadDim;
-    dst[lane] = bf16_bits_rne_f64(y0);
-    dst[lane + 64] = bf16_bits_rne_f64(y1);
+    uint16_t* dst = (uint16_t*)a.k_cache + tile;
+    dst[bf16_k_off(row, lane)] = bf16_bits_rne_f64(y0);
+    dst[bf16_k_off(row, lane + 64)] = bf16_bits_rne_f64(y1);
   }
 }
 

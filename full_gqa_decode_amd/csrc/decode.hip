@@ -20,9 +20,10 @@
 //   values  O[16 x 128]    += Phl[16 x 16 tok] . V_page[16 tok x 128]
 //           (8 x v_mfma_f32_16x16x16_bf16; rows 0-7 bf16(p), rows 8-15 the
 //           bf16 remainder of p, summed at the end)
-// K is token-major and V dim-major in the cache, so lane l loads its operand
-// straight from HBM: 16 contiguous bytes of K row l%16 and 8 contiguous bytes
-// (4 tokens) of V dim-row per MFMA, with no LDS staging and no transposes.
+// K is stored in the order of the score MFMA's operands (bf16_k_off) and V
+// dim-major, so lane l loads its operand straight from HBM: 16 contiguous
+// bytes of K row l%16 and 8 contiguous bytes (4 tokens) of V dim-row per MFMA,
+// with no LDS staging and no transposes.
 // The score tile lands in exactly the lanes that need it as the P operand of
 // the value MFMA, so the online softmax (DPP row_ror:8 for the hi+lo sum,
 // wavefront shuffles for the page max) never moves P between lanes.
@@ -57,10 +58,12 @@ struct PageRegs {
 
 __device__ __forceinline__ void load_k(const DecodeArgs& a, int pg, int g, int n, int gq,
                                        PageRegs& r) {
-  const uint16_t* kp =
-      (const uint16_t*)a.k_cache + (((int64_t)pg * a.num_kv_heads + g) * kPage + n) * kHeadDim + gq * 8;
+  // the bf16 tile order (bf16_k_off): block c of row n is 16 bytes at
+  // c * 1024 + lane * 16, so each load reads 1 KiB of contiguous bytes
+  const uint16_t* kp = (const uint16_t*)a.k_cache +
+                       ((int64_t)pg * a.num_kv_heads + g) * (kPage * kHeadDim) + (gq * 16 + n) * 8;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) r.k[c] = __builtin_nontemporal_load((const bf16x8*)(kp + c * 32));
+  for (int c = 0; c < 4; ++c) r.k[c] = __builtin_nontemporal_load((const bf16x8*)(kp + c * 512));
 }
 
 __device__ __forceinline__ void load_v(const DecodeArgs& a, int pg, int g, int n, int gq,
@@ -413,15 +416,14 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
         double y0, y1;
         norm_rope_head(xk[lane], xk[lane + 64], a.k_w, a.rms_eps, a.use_rope, cs, sn, lane,
                        &y0, &y1);
-        const int64_t o = (((int64_t)pg * a.num_kv_heads + g) * kPage + t % kPage) * kHeadDim;
+        const int64_t o = ((int64_t)pg * a.num_kv_heads + g) * (kPage * kHeadDim);
         if (KV8) {
           const uint32_t c0 = fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
           const uint32_t c1 = fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
           sm_knew[lane] = (Elem)c0;
           sm_knew[lane + 64] = (Elem)c1;
           if (ok) {
-            uint8_t* dst = (uint8_t*)a.k_cache +
-                           ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage);
+            uint8_t* dst = (uint8_t*)a.k_cache + o;
             dst[fp8_k_off(t % kPage, lane)] = (uint8_t)c0;
             dst[fp8_k_off(t % kPage, lane + 64)] = (uint8_t)c1;
           }
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
           sm_knew[lane + 64] = (Elem)k1;
           if (ok) {
             uint16_t* dst = (uint16_t*)a.k_cache + o;
-            dst[lane] = k0;
-            dst[lane + 64] = k1;
+            dst[bf16_k_off(t % kPage, lane)] = k0;
+            dst[bf16_k_off(t % kPage, lane + 64)] = k1;
           }
         }
         if (lane == 0) sm_fused_bad = !ok;

@@ -136,6 +136,16 @@ __device__ __forceinline__ uint32_t fp8_e4m3_rne_f64(double x) {
   return sign | (uint32_t)(((e + 6) << 3) + (int)m - 8);
 }
 
+// Element offset of K element (row, dim) inside the 2048-element bf16 tile of
+// one (page, KV head): blocks of 32 dims, each in groups of 8 dims, each group
+// holding the 8 dims of every row in turn.  Lane l = gq * 16 + n of a wave
+// reads K row n's dims c * 32 + gq * 8 .. + 7 (the score MFMA's A operand for
+// block c) as 16 contiguous bytes at c * 1024 + l * 16, so each of the four
+// loads reads 1 KiB of contiguous bytes.  (V tiles stay dim-major.)
+__device__ __forceinline__ int bf16_k_off(int row, int dim) {
+  return (dim >> 5) * 512 + ((dim >> 3) & 3) * 128 + row * 8 + (dim & 7);
+}
+
 // Byte offsets of K and V element (row, dim) inside the 2048-byte fp8 tile of
 // one (page, KV head).  Lane l = gq * 16 + n of a wave reads 16 contiguous
 // bytes at l * 16 and at 1024 + l * 16: for K, dims gq * 32 .. gq * 32 + 31 of

@@ -77,7 +77,7 @@ __device__ __forceinline__ void fetch_pair(const PrefillArgs& a, int pga, int pg
   } else {
     const uint16_t* kt = (const uint16_t*)a.k_cache + tile;
     const uint16_t* vt = (const uint16_t*)a.v_cache + tile;
-    kr = *(const u32x4*)(kt + (c >> 4) * kHeadDim + (c & 15) * 8);
+    kr = *(const u32x4*)(kt + bf16_k_off(c >> 4, (c & 15) * 8));
     vr = *(const u32x4*)(vt + (c >> 1) * kPage + (c & 1) * 8);
   }
 }

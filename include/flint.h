@@ -40,14 +40,17 @@
  * Paged KV cache layout (one K array and one V array per layer)
  *   A page holds 16 consecutive tokens of one request.  Logical token p of
  *   request b lives in physical page block_tables[b * bt_stride + p / 16],
- *   row p % 16.  Per page and KV head the data is one contiguous 4 KiB tile:
- *     K: k_cache[((page * num_kv_heads + g) * 16 + row) * 128 + dim]
- *        (token-major: each token's 128-dim row is 256 contiguous bytes)
- *     V: v_cache[((page * num_kv_heads + g) * 128 + dim) * 16 + row]
- *        (dim-major: the 16 tokens of one dim are 32 contiguous bytes)
- *   K rows feed the q.K contraction over dims; V is stored dim-major because
- *   the P.V contraction runs over tokens, so both operands of the matrix
- *   cores load straight from HBM with full coalescing.
+ *   row p % 16.  Per page and KV head the data is one contiguous 4 KiB tile
+ *   at element (page * num_kv_heads + g) * 2048:
+ *     K: element (row, dim) at (dim >> 5) * 512 + ((dim >> 3) & 3) * 128
+ *        + row * 8 + (dim & 7) in the tile (blocks of 32 dims, each of four
+ *        groups of 8 dims holding those dims of all 16 rows in turn)
+ *     V: element (row, dim) at dim * 16 + row (dim-major: the 16 tokens of
+ *        one dim are 32 contiguous bytes)
+ *   This is the order the matrix cores take their operands in: each 64-lane
+ *   K load reads one 32-dim block of all 16 rows (1 KiB contiguous), and V
+ *   is dim-major because the P.V contraction runs over tokens, so both
+ *   operands load straight from HBM with full coalescing.
  *
  * KV element formats (flint_attn_layer.kv_dtype)
  *   FLINT_KV_BF16: 2-byte bf16 elements (uint16 bit patterns), 4 KiB tiles.

@@ -250,6 +250,35 @@ def v_offsets(L: Layer, page, g, row) -> np.ndarray:
     return np.array([f(C.byref(L), int(page), int(g), int(row), i) for i in range(L.d)], np.int64)
 
 
+def _tile_patterns(L: Layer):
+    """Offsets of (row, dim) inside one (page, KV head) tile, for K and V."""
+    fk, fv = lib().orc_k_offset, lib().orc_v_offset
+    k = np.array([[fk(C.byref(L), 0, 0, r, d) for d in range(L.d)] for r in range(L.bs)], np.int64)
+    v = np.array([[fv(C.byref(L), 0, 0, r, d) for d in range(L.d)] for r in range(L.bs)], np.int64)
+    return k, v
+
+
+def k_to_cache(L: Layer, rows) -> np.ndarray:
+    """K rows in logical order [pages, hkv, bs, d] -> the cache array (same
+    shape and dtype) in the layout the library and the oracle read."""
+    rows = np.ascontiguousarray(rows)
+    kp, _ = _tile_patterns(L)
+    n = rows.shape[0] * rows.shape[1]
+    out = np.empty((n, L.bs * L.d), rows.dtype)
+    out[:, kp.reshape(-1)] = rows.reshape(n, L.bs * L.d)
+    return out.reshape(rows.shape)
+
+
+def k_from_cache(L: Layer, cache) -> np.ndarray:
+    """The cache array -> K rows in logical order [pages, hkv, bs, d]."""
+    cache = np.asarray(cache)
+    kp, _ = _tile_patterns(L)
+    n = cache.size // (L.bs * L.d)
+    flat = cache.reshape(n, L.bs * L.d)
+    nb = cache.size // (L.hkv * L.bs * L.d)
+    return flat[:, kp.reshape(-1)].reshape(nb, L.hkv, L.bs, L.d)
+
+
 def k_row(L: Layer, cache, page, g, row) -> np.ndarray:
     return np.asarray(cache).reshape(-1)[k_offsets(L, page, g, row)]
 

@@ -149,7 +149,10 @@ int64_t orc_slot(const int32_t* bt, int bt_stride, int bs, int b, int pos) {
 
 /* Cache layout (the library's own convention; the pages fix none).  Each
  * (page, KV head g) owns one contiguous tile of bs * d elements.
- * bf16: K is token-major (element row * d + dim), V dim-major (dim * bs + row).
+ * bf16 (d a multiple of 8): K in blocks of 32 dims, each in groups of 8 dims,
+ * each group holding the 8 dims of every row in turn:
+ *   (dim >> 5) * bs * 32 + ((dim >> 3) & 3) * bs * 8 + row * 8 + (dim & 7);
+ * V dim-major: dim * bs + row.
  * fp8 (d = 128, bs = 16 only), within the 2048-byte tile:
  *   K: ((dim >> 4) & 1) * 1024 + (dim >> 5) * 256 + row * 16 + (dim & 15)
  *   V: (dim >> 6) * 1024 + ((row >> 2) * 16 + (dim & 15)) * 16
@@ -157,7 +160,7 @@ int64_t orc_slot(const int32_t* bt, int bt_stride, int bs, int b, int pos) {
 int64_t orc_k_offset(const orc_layer* L, int64_t page, int g, int row, int dim) {
   const int64_t tile = (page * L->hkv + g) * (int64_t)L->bs * L->d;
   if (L->kv_fp8) return tile + ((dim >> 4) & 1) * 1024 + (dim >> 5) * 256 + row * 16 + (dim & 15);
-  return tile + (int64_t)row * L->d + dim;
+  return tile + (int64_t)(dim >> 5) * L->bs * 32 + ((dim >> 3) & 3) * L->bs * 8 + row * 8 + (dim & 7);
 }
 int64_t orc_v_offset(const orc_layer* L, int64_t page, int g, int row, int dim) {
   const int64_t tile = (page * L->hkv + g) * (int64_t)L->bs * L->d;

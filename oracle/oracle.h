@@ -66,7 +66,8 @@ double orc_fp8_value(uint8_t c);
 
 /* Cache layout (the library's convention): element offset of K / V element
  * (page, KV head g, row, dim) in its cache array.  Each (page, g) owns one
- * contiguous tile of bs * d elements.  bf16: K token-major (row * d + dim), V
+ * contiguous tile of bs * d elements.  bf16 (d a multiple of 8): K at
+ * (dim >> 5) * bs * 32 + ((dim >> 3) & 3) * bs * 8 + row * 8 + (dim & 7), V
  * dim-major (dim * bs + row).  fp8 E4M3 (d = 128, bs = 16 only; the other
  * functions return -2, or a NaN lse, for an fp8 layer of another shape), in
  * the 2048-byte tile:

@@ -145,13 +145,13 @@ def _paged(L, dense_k_bits, dense_v_bits, seed, perm=True):
     order = synth.permutation(seed, (77,), pages + extra) if perm else np.arange(pages + extra)
     bt = np.full((1, pages + 2), -1, np.int32)
     bt[0, :pages] = order[:pages]
-    kc = np.full((pages + extra, L.hkv, L.bs, L.d), 0x7FC0, np.uint16)  # NaN where unused
+    kl = np.full((pages + extra, L.hkv, L.bs, L.d), 0x7FC0, np.uint16)  # NaN where unused
     vc = np.full((pages + extra, L.hkv, L.d, L.bs), 0x7FC0, np.uint16)
     for p in range(n):
         pg, r = bt[0, p // L.bs], p % L.bs
-        kc[pg, :, r, :] = dense_k_bits[p]
+        kl[pg, :, r, :] = dense_k_bits[p]
         vc[pg, :, :, r] = dense_v_bits[p]
-    return kc, vc, bt
+    return oracle.k_to_cache(L, kl), vc, bt
 
 
 def _brute(L, q, kbits, vbits, t, sinks, lo=None):
@@ -378,6 +378,7 @@ def test_ring_aliasing_outside_window_is_bit_identical():
         pg = rbt[0, p // 16]
         rk[pg, :, p % 16] = kb[p]
         rv[pg, :, :, p % 16] = vb[p]
+    rk = oracle.k_to_cache(Ls, rk)
     sl = np.array([n], np.int32)
     assert np.array_equal(oracle.attn_decode(Ls, q, kc, vc, bt, sl, sinks),
                           oracle.attn_decode(Ls, q, rk, rv, rbt, sl, sinks))
@@ -408,6 +409,7 @@ def test_append_places_rows_and_rounds_v_like_torch():
     kc = np.full((nb, 4, 16, 128), 0xBEEF, np.uint16)
     vc = np.full((nb, 4, 128, 16), 0xBEEF, np.uint16)
     qo = oracle.append(L, q, k, v, ones, ones, pos, slots, kc, vc)
+    kl = oracle.k_from_cache(L, kc)
     written = np.zeros((nb, 16), bool)
     for t in range(T):
         if slots[t] < 0:
@@ -419,9 +421,9 @@ def test_append_places_rows_and_rounds_v_like_torch():
             kk = oracle.rope(oracle.rmsnorm(k[t, g], ones), pos[t])
             # the oracle rounds the fp64 value once; torch rounds its fp32 image
             ref = _torch_bf16_bits(kk.astype(np.float32)).astype(int)
-            assert np.max(np.abs(kc[pg, g, r].astype(int) - ref)) <= 1
+            assert np.max(np.abs(kl[pg, g, r].astype(int) - ref)) <= 1
     untouched = ~written
-    assert np.all(kc.transpose(0, 2, 1, 3)[untouched] == 0xBEEF)
+    assert np.all(kl.transpose(0, 2, 1, 3)[untouched] == 0xBEEF)
     assert np.all(vc.transpose(0, 3, 1, 2)[untouched] == 0xBEEF)
     # q out: norm then rope; norms are preserved by the rotation
     for t in (0, 17):
@@ -568,7 +570,8 @@ def _fp8_layer(**kw):
 
 def test_cache_tile_orders_follow_the_abi_header():
     # the layouts include/flint.h documents, written out here from that text:
-    # bf16 K token-major, V dim-major; fp8 in its MFMA-native tile order.
+    # bf16 K in blocks of 32 dims of 8-dim groups, V dim-major; fp8 in its
+    # MFMA-native tile order.
     # Every (row, dim) of a tile lands on a distinct element of that tile.
     for fp8 in (0, 1):
         L = oracle.layer(kv_fp8=fp8, hkv=4)
@@ -583,7 +586,8 @@ def test_cache_tile_orders_follow_the_abi_header():
                         v_ref = ((d >> 6) * 1024 + ((r >> 2) * 16 + (d & 15)) * 16
                                  + ((d >> 4) & 3) * 4 + (r & 3))
                     else:
-                        k_ref, v_ref = r * 128 + d, d * 16 + r
+                        k_ref = (d >> 5) * 512 + ((d >> 3) & 3) * 128 + r * 8 + (d & 7)
+                        v_ref = d * 16 + r
                     assert ko[d] == tile + k_ref and vo[d] == tile + v_ref
                 ks.update(ko.tolist())
                 vs.update(vo.tolist())
