@@ -66,7 +66,7 @@ def test_split_counts_agree(pps):
     assert max_err(got, ref) <= TOL
 
 
-def test_config0_full_layer_4096():
+def test_full_layer_bs1_ctx4096():
     # one full NoPE layer, one decode step, batch 1, context 4096, seed 0
     case = DecodeCase(0, [4096], window=0)
     ref, _, _, _ = case.expected()
@@ -74,7 +74,7 @@ def test_config0_full_layer_4096():
     assert max_err(out.cpu().numpy(), ref) <= TOL
 
 
-def test_config1_sliding_layer_32768():
+def test_sliding_layer_bs1_ctx32768():
     # one sliding RoPE layer, context 32768, window 513, full page table
     case = DecodeCase(0, [32768], window=513, ring=False)
     ref, _, _, _ = case.expected()
@@ -112,7 +112,7 @@ def test_deterministic():
     assert np.array_equal(a, b)
 
 
-def test_ragged_64_requests_config3_scaled():
+def test_ragged_64_requests_scaled_lengths():
     # 64 requests, lengths uniform in [1024, 8192] (config 3's mix, scaled down),
     # one full and one sliding layer, random physical page order
     import synth

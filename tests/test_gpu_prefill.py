@@ -119,7 +119,7 @@ def test_last_prefill_row_matches_decode_at_same_position():
 
 
 @pytest.mark.parametrize("window", [0, 513])
-def test_prefill_config4_32768_sampled_rows(window):
+def test_prefill_32768_token_prompt_sampled_rows(window):
     # causal prefill of a 32,768-token prompt; the oracle checks sampled rows
     case = PrefillCase(0, [(32768, 32768)], window=window)
     got, _, _, _ = case.run_gpu()
