@@ -19,16 +19,18 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SO = os.path.join(HERE, "liboracle.so")
 SRC = os.path.join(HERE, "oracle.c")
+SRCS = [SRC, os.path.join(HERE, "moe.c")]
 
 
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (OpenMP for the
     independent per-(query, head) work items)."""
-    if not force and os.path.exists(SO) and os.path.getmtime(SO) >= os.path.getmtime(SRC):
+    if not force and os.path.exists(SO) and all(os.path.getmtime(SO) >= os.path.getmtime(f)
+                                                 for f in SRCS):
         return SO
     tmp = SO + ".tmp"
     subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
-                           "-Wall", "-Werror", "-o", tmp, SRC, "-lm"], cwd=HERE)
+                           "-Wall", "-Werror", "-o", tmp, *SRCS, "-lm"], cwd=HERE)
     os.replace(tmp, SO)
     return SO
 
@@ -307,6 +309,50 @@ def fp8_value(codes) -> np.ndarray:
     c = np.asarray(codes, dtype=np.uint8)
     f = lib().orc_fp8_value
     return np.array([f(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+# --- O9 / O10: MoE sublayer -------------------------------------------------------
+class Moe(C.Structure):
+    _fields_ = [("hidden", C.c_int), ("experts", C.c_int), ("top_k", C.c_int),
+                ("inter", C.c_int), ("shared", C.c_int)]
+
+
+def moe(hidden: int = 2048, experts: int = 256, top_k: int = 6, inter: int = 512,
+        shared: int = 1) -> Moe:
+    return Moe(hidden, experts, top_k, inter, shared)
+
+
+def gate_up_shape(M: Moe):
+    return (M.experts + M.shared, 2, M.inter, M.hidden)
+
+
+def down_shape(M: Moe):
+    return (M.experts + M.shared, M.hidden, M.inter)
+
+
+def moe_route(M: Moe, x, w_router):
+    """One token: (ids [top_k] int32, weights [top_k] fp64)."""
+    x = _c(x, np.float32)
+    ids = np.empty(M.top_k, np.int32)
+    w = np.empty(M.top_k, np.float64)
+    if lib().orc_moe_route(C.byref(M), _p(x), _p(_c(w_router, np.uint16)), _p(ids), _p(w)) != 0:
+        raise ValueError("oracle moe_route: bad top_k")
+    return ids, w
+
+
+def moe_forward(M: Moe, x, w_router, w_gate_up, w_down, nthreads=0):
+    """x [T, hidden] fp32 -> (ids [T, top_k], weights [T, top_k], y [T, hidden] fp64)."""
+    x = _c(x, np.float32)
+    T = x.shape[0]
+    ids = np.empty((T, M.top_k), np.int32)
+    w = np.empty((T, M.top_k), np.float64)
+    y = np.empty((T, M.hidden), np.float64)
+    rc = lib().orc_moe_forward(C.byref(M), T, _p(x), _p(_c(w_router, np.uint16)),
+                               _p(_c(w_gate_up, np.uint16)), _p(_c(w_down, np.uint16)), _p(ids),
+                               _p(w), _p(y), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle moe_forward: bad top_k")
+    return ids, w, y
 
 
 # --- O8 / footprint -----------------------------------------------------------

@@ -19,11 +19,13 @@
  *                "architecture" (GQA 4 KV x 128) and "kvCacheGiBPerRequest".
  * Where the pages leave a step open the reading taken is stated next to it.
  *
- * Cache layout (the oracle's own statement of the library's format): for each
- * layer K is an array of bf16 bit patterns indexed
- * [page][kv_head][row 0..15][dim 0..127] and V one indexed
- * [page][kv_head][dim 0..127][row 0..15]; logical token p of request b lives
- * in physical page block_tables[b][p/16], row p%16.
+ * Cache layout (the oracle's own statement of the library's format): one K
+ * and one V array per layer, one contiguous tile of bs * d elements per
+ * (page, KV head), elements placed as orc_k_offset / orc_v_offset below
+ * state; logical token p of request b lives in physical page
+ * block_tables[b][p/16], row p%16.
+ *
+ * moe.c adds the MoE sublayer (O9, O10) with its own sources and readings.
  */
 #ifndef FLINT_ORACLE_H
 #define FLINT_ORACLE_H
@@ -140,6 +142,32 @@ int64_t orc_kv_bytes_per_request(int64_t ctx, int full_layers, int sliding_layer
 
 /* Number of threads the parallel oracle calls use for nthreads <= 0. */
 int orc_default_threads(void);
+
+/* O9/O10 (moe.c): Flint's MoE sublayer at decode.  Shapes: hidden 2048, 256
+ * routed experts, top 6, one shared expert; `inter` is the expert FFN width
+ * (a reading: 512).  Weights are bf16 bit patterns:
+ *   w_router [experts][hidden], w_gate_up [experts + shared][2][inter][hidden]
+ *   (gate rows then up rows), w_down [experts + shared][hidden][inter]. */
+typedef struct {
+  int hidden;
+  int experts;   /* routed experts                   */
+  int top_k;     /* experts selected per token       */
+  int inter;     /* FFN width of every expert         */
+  int shared;    /* always-active experts (weight 1)  */
+} orc_moe;
+
+/* O9: logits z_e = <x, w_router[e]> (fp64); the top_k experts by z rounded
+ * to fp32, ties to the lower index; weights sigmoid(z) normalised over the
+ * selected experts.  Returns 0, or -1 if top_k is outside [1, experts]. */
+int orc_moe_route(const orc_moe* M, const float* x, const uint16_t* w_router, int32_t* ids,
+                  double* weights);
+
+/* O10: y[t] = sum_k weights[t][k] E_{ids[t][k]}(x[t]) + sum_s E_{experts+s}(x[t]),
+ * E(x) = W_down (silu(W_gate x) * (W_up x)), fp64 throughout.  ids, weights
+ * are outputs ([T][top_k]); y [T][hidden].  Returns 0 or -1. */
+int orc_moe_forward(const orc_moe* M, int T, const float* x, const uint16_t* w_router,
+                    const uint16_t* w_gate_up, const uint16_t* w_down, int32_t* ids,
+                    double* weights, double* y, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -673,3 +673,110 @@ def test_fp8_attention_is_bf16_attention_of_the_dequantised_cache():
         assert np.array_equal(out8, out16)
         ref = _brute(L16, q, kb, vb, n - 1, sinks)
         assert np.max(np.abs(out8 - ref)) < 1e-13 * max(1.0, np.abs(ref).max())
+
+
+# ---------------------------------------------------------------------------
+# MoE sublayer (O9 router + top-k, O10 experts): closed forms from rank-one
+# weights whose products are exact, ties, invariants
+# ---------------------------------------------------------------------------
+
+def _bf16_exact(vals):
+    """Values that bf16 holds exactly (3 significant bits), as (bits, values)."""
+    v = np.asarray(vals, np.float64)
+    b = _torch_bf16_bits(v.astype(np.float32))
+    return b, synth.bf16_bits_to_f32(b).astype(np.float64)
+
+
+def _rank_one_moe(M, seed):
+    """Weights where every product is exact: router row e = c_e * e_0, gate /
+    up row j of expert e = a_j^e * e_0 / b_j^e * e_0, down row r of expert e
+    = c_r^e * v^e.  With x[0] = 1: z_e = c_e, g_j = a_j, u_j = b_j and
+    E_e(x)_r = c_r^e * sum_j v_j^e silu(a_j^e) b_j^e."""
+    rng = synth.rng(seed, 1)
+    H, I, E, S = M.hidden, M.inter, M.experts, M.shared
+    quant = lambda a: np.round(a * 8) / 8                    # multiples of 1/8, small: exact
+    c_route = rng.permutation(E) / 8.0 - E / 16.0            # distinct router logits
+    a = quant(rng.uniform(-2, 2, (E + S, I)))
+    bu = quant(rng.uniform(-2, 2, (E + S, I)))
+    c = quant(rng.uniform(-1, 1, (E + S, H)))
+    v = quant(rng.uniform(-1, 1, (E + S, I)))
+    wr = np.zeros((E, H), np.uint16)
+    wr[:, 0] = _bf16_exact(c_route)[0]
+    wgu = np.zeros((E + S, 2, I, H), np.uint16)
+    wgu[:, 0, :, 0] = _bf16_exact(a)[0]
+    wgu[:, 1, :, 0] = _bf16_exact(bu)[0]
+    # c_r * v_j: a product of two multiples of 1/8 below 2, exact in bf16
+    c32, v32 = c.astype(np.float32), v.astype(np.float32)
+    wd = _torch_bf16_bits(np.einsum("er,ej->erj", c32, v32))
+    x = synth.normal(seed, (2,), (1, H))   # coordinates 1.. meet zero weights
+    x[0, 0] = 1.0
+    silu = lambda g: g / (1.0 + np.exp(-g))
+    expert = np.array([c[e] * float(np.sum(v[e] * silu(a[e]) * bu[e])) for e in range(E + S)])
+    return wr, wgu, wd, x, c_route, expert
+
+
+@pytest.mark.parametrize("shape", [dict(hidden=64, experts=16, top_k=3, inter=8, shared=1),
+                                   dict(hidden=2048, experts=16, top_k=6, inter=512, shared=1),
+                                   dict(hidden=64, experts=16, top_k=6, inter=8, shared=2)])
+def test_moe_closed_form(shape):
+    # catches a dropped term (shared expert, a routed slot), swapped gate/up,
+    # a transposed down projection, unnormalised or wrongly paired weights
+    M = oracle.moe(**shape)
+    wr, wgu, wd, x, z, expert = _rank_one_moe(M, 50 + shape["top_k"])
+    ids, w, y = oracle.moe_forward(M, x, wr, wgu, wd)
+    top = np.argsort(-z, kind="stable")[:M.top_k]
+    assert ids[0].tolist() == top.tolist()
+    s = 1.0 / (1.0 + np.exp(-z[top]))
+    assert np.allclose(w[0], s / s.sum(), rtol=0, atol=1e-15)
+    ref = (s / s.sum()) @ expert[top] + expert[M.experts:].sum(axis=0)
+    assert np.max(np.abs(y[0] - ref)) <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_moe_route_ties_go_to_the_lower_index():
+    M = oracle.moe(hidden=64, experts=16, top_k=6, inter=8, shared=1)
+    wr = np.zeros((16, 64), np.uint16)
+    wr[:, 0] = _bf16_exact(np.full(16, 0.5))[0]
+    wr[[3, 11], 0] = _bf16_exact([0.75, 0.75])[0]
+    x = np.zeros(64, np.float32)
+    x[0] = 1.0
+    ids, w = oracle.moe_route(M, x, wr)
+    assert ids.tolist() == [3, 11, 0, 1, 2, 4]
+    assert abs(w.sum() - 1.0) < 1e-15 and w[0] == w[1] and w[2] == w[5]
+
+
+def test_moe_route_matches_a_sort_of_the_logits():
+    # random router: the selection is the stable descending order of the
+    # fp32-rounded logits, computed here by numpy's matmul and argsort
+    M = oracle.moe()
+    wr = synth.normal_bf16_bits(51, (1,), (256, 2048))
+    for t in range(4):
+        x = synth.normal(51, (2, t), 2048) * np.float32(0.03)
+        ids, w = oracle.moe_route(M, x, wr)
+        z = synth.bf16_bits_to_f32(wr).astype(np.float64) @ x.astype(np.float64)
+        top = np.argsort(-z.astype(np.float32), kind="stable")[:6]
+        assert ids.tolist() == top.tolist()
+        s = 1.0 / (1.0 + np.exp(-z[top]))
+        assert np.allclose(w, s / s.sum(), rtol=1e-12, atol=0)
+        assert len(set(ids.tolist())) == 6
+
+
+def test_moe_is_linear_in_the_down_projection_and_the_shared_expert_adds():
+    M = oracle.moe(hidden=64, experts=16, top_k=3, inter=16, shared=1)
+    wr = synth.normal_bf16_bits(52, (1,), (16, 64))
+    wgu = synth.normal_bf16_bits(52, (2,), oracle.gate_up_shape(M))
+    wd = synth.normal_bf16_bits(52, (3,), oracle.down_shape(M))
+    x = synth.normal(52, (4,), (3, 64)) * np.float32(0.2)
+    _, _, y = oracle.moe_forward(M, x, wr, wgu, wd)
+    # doubling every bf16 down weight (exact: exponent + 1) doubles y
+    wd2 = (wd.astype(np.uint32) + (1 << 7)).astype(np.uint16)
+    _, _, y2 = oracle.moe_forward(M, x, wr, wgu, wd2)
+    assert np.max(np.abs(y2 - 2 * y)) <= 1e-12 * np.abs(y).max()
+    # zero routed down projections: only the shared expert remains
+    wd0 = wd.copy()
+    wd0[:16] = 0
+    _, _, y0 = oracle.moe_forward(M, x, wr, wgu, wd0)
+    wd_s = np.zeros_like(wd)
+    wd_s[16] = wd[16]
+    _, _, ys = oracle.moe_forward(M, x, wr, wgu, wd_s)
+    assert np.array_equal(y0, ys)
+    assert np.abs(ys).max() > 0
