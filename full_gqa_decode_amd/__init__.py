@@ -8,6 +8,7 @@ been built this module raises on first use; there is no fallback.
 Functions carry the C names of include/flint.h:
     flint_qk_norm_rope_append, flint_attn_decode, flint_attn_prefill,
     flint_attn_decode_step (append + decode fused into one launch),
+    flint_attn_decode_partials, flint_attn_merge, flint_moe_forward,
 plus the size / plan queries.  bf16 tensors (K/V caches, prefill q) may be
 torch.bfloat16, torch.int16 or torch.uint16, and fp8 caches torch.uint8 or
 torch.float8_e4m3fn: only their bits are used.
@@ -68,11 +69,24 @@ def sliding_layer(**kw) -> FlintAttnLayer:
     return layer(window=513, use_rope=1, **kw)
 
 
+class FlintMoeLayer(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
+                ("inter", C.c_int32), ("num_shared", C.c_int32)]
+
+
+def moe_layer(hidden: int = 2048, num_experts: int = 256, top_k: int = 6, inter: int = 512,
+              num_shared: int = 1) -> FlintMoeLayer:
+    """Flint's MoE sublayer: 256 routed experts, top 6, one shared expert,
+    hidden 2048; the expert FFN width 512 is a reading (the pages give none)."""
+    return FlintMoeLayer(hidden, num_experts, top_k, inter, num_shared)
+
+
 _lib = None
 _P = C.c_void_p
 _I = C.c_int32
 _SZ = C.c_size_t
 _LP = C.POINTER(FlintAttnLayer)
+_MP = C.POINTER(FlintMoeLayer)
 
 # (name, restype, argtypes) of every symbol include/flint.h declares
 SIGNATURES = [
@@ -92,6 +106,8 @@ SIGNATURES = [
     ("flint_attn_prefill_workspace_size", _SZ, [_LP, _I, _I, _I]),
     ("flint_attn_prefill", C.c_int,
      [_LP, _I, _P, _P, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+    ("flint_moe_workspace_size", _SZ, [_MP, _I]),
+    ("flint_moe_forward", C.c_int, [_MP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("flint_status_string", C.c_char_p, [C.c_int]),
     ("flint_last_error", C.c_char_p, []),
     ("flint_abi_version", _I, []),
@@ -314,6 +330,37 @@ def flint_attn_prefill(L: FlintAttnLayer, q, cu_q_lens, max_q_len: int, k_cache,
         _ptr(out, _f32(), "out"), None if workspace is None else workspace.data_ptr(), ws_bytes,
         _stream(stream)))
     return out
+
+
+def flint_moe_workspace_size(M: FlintMoeLayer, num_tokens: int) -> int:
+    return int(lib().flint_moe_workspace_size(C.byref(M), num_tokens))
+
+
+def flint_moe_forward(M: FlintMoeLayer, x, w_router, w_gate_up, w_down, out=None, topk_ids=None,
+                      topk_weights=None, workspace=None, stream=None):
+    """MoE sublayer for x [T, hidden] fp32 (T <= 8); weights are bf16-bits
+    tensors in the layout of include/flint.h.  Returns (out [T, hidden] fp32,
+    topk_ids [T, top_k] int32, topk_weights [T, top_k] fp32)."""
+    torch = _torch()
+    T = x.shape[0]
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, M.hidden), dtype=torch.float32, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty((T, M.top_k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, M.top_k), dtype=torch.float32, device=dev)
+    need = flint_moe_workspace_size(M, T)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().flint_moe_forward(
+        C.byref(M), T, _ptr(x, _f32(), "x"), _ptr(w_router, _b16(), "w_router"),
+        _ptr(w_gate_up, _b16(), "w_gate_up"), _ptr(w_down, _b16(), "w_down"),
+        _ptr(topk_ids, _i32(), "topk_ids"), _ptr(topk_weights, _f32(), "topk_weights"),
+        _ptr(out, _f32(), "out"), None if workspace is None else workspace.data_ptr(), ws_bytes,
+        _stream(stream)))
+    return out, topk_ids, topk_weights
 
 
 def abi_version() -> int:

@@ -1,0 +1,278 @@
+// moe.hip -- Flint's MoE sublayer at small-batch decode (1..8 tokens):
+// router GEMV, sigmoid top-k, routed and shared SwiGLU expert GEMVs.
+//
+// What is computed ("Day-0 Support for Flint on vLLM", hnkhoi.com, "Model
+// architecture": hidden size 2048, 256 experts, sigmoid top-6, a shared
+// expert; newruntime.com, "What happened": small-batch MoE and dense GEMV
+// kernels), with the readings the oracle states (no router bias; top-k on the
+// fp32 logits, ties to the lower index; weights = selected sigmoid scores
+// normalised to sum 1; SwiGLU experts; the shared expert with weight 1):
+//   z_e = <x, Wr_e>,  w_k = s_{id_k} / sum_j s_{id_j},  s = sigmoid(z)
+//   y = sum_k w_k Wd_{id_k} (silu(Wg_{id_k} x) * (Wu_{id_k} x)) + shared terms
+//
+// Design for gfx950.  At 1..8 tokens every weight row feeds at most a few dot
+// products, so the sublayer is a stream of bf16 weight rows from HBM (45 MB
+// per token at Flint's shape) and the work goes on the vector ALU, not the
+// matrix cores.  Each wave owns whole weight rows and reads a row with
+// 16-byte lane loads -- one 1 KiB contiguous load per instruction --, widens
+// bf16 to fp32 exactly (a shift) and accumulates fp32 FMAs against x; a
+// DPP/permlane reduction gives the dot product.  Three launches:
+//   K5a router logits (one wave per expert row, every token);
+//   K5b top-k -- recomputed by every wave from the token's logits, so no
+//       launch is spent on it -- then the gate and up rows and SwiGLU (one
+//       wave per (FFN row, slot, token));
+//   K5c down rows and the weighted combine (one wave per (output row, token)).
+// Every wave issues all of its row loads before it waits for any, so each
+// launch costs one dependent memory round trip after its inputs arrive.
+#include <climits>
+
+#include "device.h"
+#include "launch.h"
+
+namespace flint {
+
+namespace {
+
+constexpr int kMoeWaves = 4;  // waves per workgroup
+
+// 8 bf16 (one 16-byte load) -> 8 fp32, exactly.
+__device__ __forceinline__ void widen8(const u32x4& w, float (&f)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float dot8(const u32x4& w, const f32x4& x0, const f32x4& x1,
+                                      float acc) {
+  float f[8];
+  widen8(w, f);
+  acc = fmaf(f[0], x0[0], acc);
+  acc = fmaf(f[1], x0[1], acc);
+  acc = fmaf(f[2], x0[2], acc);
+  acc = fmaf(f[3], x0[3], acc);
+  acc = fmaf(f[4], x1[0], acc);
+  acc = fmaf(f[5], x1[1], acc);
+  acc = fmaf(f[6], x1[2], acc);
+  return fmaf(f[7], x1[3], acc);
+}
+
+__device__ __forceinline__ int wave_min_i32(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x128, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x122, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x121, 0xF, 0xF, false));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// K5a: z[t][e] = <x_t, Wr_e> for every token; one wave per expert row.
+__global__ __launch_bounds__(kMoeWaves * 64) void moe_router_kernel(MoeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * kMoeWaves + (threadIdx.x >> 6);
+  if (e >= a.num_experts) return;
+  const int H = a.hidden;
+  const uint16_t* w = a.w_router + (int64_t)e * H + lane * 8;
+  u32x4 wv[kMoeMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMoeMaxChunks; ++c)
+    if (c * 512 < H) wv[c] = __builtin_nontemporal_load((const u32x4*)(w + c * 512));
+  for (int t = 0; t < a.num_tokens; ++t) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMoeMaxChunks; ++c) {
+      if (c * 512 < H) {
+        const float* xp = a.x + (int64_t)t * H + c * 512 + lane * 8;
+        acc = dot8(wv[c], *(const f32x4*)xp, *(const f32x4*)(xp + 4), acc);
+      }
+    }
+    const float z = wave_sum_f32(acc);
+    if (lane == 0) a.logits[(int64_t)t * a.num_experts + e] = z;
+  }
+}
+
+// The top_k experts of token t (largest logit first, lower index on ties) and
+// their normalised sigmoid weights; every lane gets the same.  Lane l holds
+// experts l, l+64, l+128, l+192 (at most 256 experts).
+struct TopK {
+  int ids[kMoeMaxTopK];
+  float weights[kMoeMaxTopK];
+};
+
+__device__ __forceinline__ TopK select_topk(const MoeArgs& a, int t, int lane) {
+  const int E = a.num_experts;
+  float z[4], zs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    z[i] = e < E ? a.logits[(int64_t)t * E + e] : -INFINITY;
+    if (z[i] != z[i]) z[i] = -INFINITY;  // a NaN logit ranks last
+    zs[i] = z[i];
+  }
+  TopK r;
+  float ssum = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMoeMaxTopK; ++k) {
+    if (k >= a.top_k) break;
+    float v = z[0];
+    int idx = lane;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (z[i] > v) {  // strict: the lower index wins among equals
+        v = z[i];
+        idx = lane + 64 * i;
+      }
+    const float m = wave_max_f32(v);
+    int win = wave_min_i32(v == m ? idx : INT_MAX);
+    win = win < E ? win : 0;  // unreachable for finite logits; keeps the index valid
+    float zw = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (lane + 64 * i == win) {
+        zw = zs[i];
+        z[i] = -INFINITY;  // taken
+      }
+    }
+    zw = wave_sum_f32(zw);  // the winner's logit, from its lane
+    r.ids[k] = win;
+    r.weights[k] = 1.f / (1.f + __expf(-zw));
+    ssum += r.weights[k];
+  }
+#pragma unroll
+  for (int k = 0; k < kMoeMaxTopK; ++k)
+    if (k < a.top_k) r.weights[k] /= ssum;
+  return r;
+}
+
+// K5b: h[t][slot][j] = silu(<x_t, Wg_j>) * <x_t, Wu_j> for the expert of the
+// slot (slots top_k.. are the shared experts).  Grid (FFN rows / 4, slots,
+// tokens); one wave per FFN row j.  The first wave of each token's grid row
+// also writes the token's top-k ids and weights.
+__global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int slot = blockIdx.y, t = blockIdx.z;
+  const int j = blockIdx.x * kMoeWaves + w;
+  const int H = a.hidden, I = a.inter;
+  const int nslots = a.top_k + a.num_shared;
+  // x does not wait for the selection
+  f32x4 x0[kMoeMaxChunks], x1[kMoeMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMoeMaxChunks; ++c) {
+    if (c * 512 < H) {
+      const float* xp = a.x + (int64_t)t * H + c * 512 + lane * 8;
+      x0[c] = *(const f32x4*)xp;
+      x1[c] = *(const f32x4*)(xp + 4);
+    }
+  }
+  int expert = a.num_experts + (slot - a.top_k);
+  if (slot < a.top_k) {
+    const TopK tk = select_topk(a, t, lane);
+#pragma unroll
+    for (int k = 0; k < kMoeMaxTopK; ++k)
+      if (k == slot) expert = tk.ids[k];
+    if (blockIdx.x == 0 && w == 0 && slot == 0) {
+      int id = 0;
+      float wt = 0.f;
+#pragma unroll
+      for (int k = 0; k < kMoeMaxTopK; ++k)
+        if (k == lane) {
+          id = tk.ids[k];
+          wt = tk.weights[k];
+        }
+      if (lane < a.top_k) {
+        a.topk_ids[t * a.top_k + lane] = id;
+        a.topk_weights[t * a.top_k + lane] = wt;
+      }
+    }
+  }
+  if (j >= I) return;
+  const uint16_t* wg = a.w_gate_up + ((int64_t)expert * 2 * I + j) * H + lane * 8;
+  const uint16_t* wu = wg + (int64_t)I * H;
+  u32x4 gv[kMoeMaxChunks], uv[kMoeMaxChunks];
+#pragma unroll
+  for (int c = 0; c < kMoeMaxChunks; ++c) {
+    if (c * 512 < H) {
+      gv[c] = __builtin_nontemporal_load((const u32x4*)(wg + c * 512));
+      uv[c] = __builtin_nontemporal_load((const u32x4*)(wu + c * 512));
+    }
+  }
+  float g = 0.f, u = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMoeMaxChunks; ++c) {
+    if (c * 512 < H) {
+      g = dot8(gv[c], x0[c], x1[c], g);
+      u = dot8(uv[c], x0[c], x1[c], u);
+    }
+  }
+  g = wave_sum_f32(g);
+  u = wave_sum_f32(u);
+  if (lane == 0) a.h[((int64_t)t * nslots + slot) * I + j] = g / (1.f + __expf(-g)) * u;
+}
+
+// K5c: out[t][r] = sum_k w_k <Wd_{id_k}[r], h[t][k]> + sum_s <Wd_s[r], h[t][s]>.
+// One wave per (output row r, token t), every slot's row loaded up front.
+__global__ __launch_bounds__(kMoeWaves * 64) void moe_down_kernel(MoeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * kMoeWaves + (threadIdx.x >> 6);
+  const int t = blockIdx.y;
+  const int H = a.hidden, I = a.inter;
+  if (r >= H) return;
+  const int nslots = a.top_k + a.num_shared;
+  constexpr int kSlots = kMoeMaxTopK + kMoeMaxShared;
+  constexpr int kIC = kMoeMaxInter / 512;
+  u32x4 wv[kSlots][kIC];
+  f32x4 h0[kSlots][kIC], h1[kSlots][kIC];
+  float wk[kSlots];
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) {
+    if (k < nslots) {
+      const bool routed = k < a.top_k;
+      const int e = routed ? a.topk_ids[t * a.top_k + k] : a.num_experts + (k - a.top_k);
+      wk[k] = routed ? a.topk_weights[t * a.top_k + k] : 1.f;
+      const uint16_t* wd = a.w_down + ((int64_t)e * H + r) * I + lane * 8;
+      const float* hp = a.h + ((int64_t)t * nslots + k) * I + lane * 8;
+#pragma unroll
+      for (int c = 0; c < kIC; ++c) {
+        if (c * 512 < I) {
+          wv[k][c] = __builtin_nontemporal_load((const u32x4*)(wd + c * 512));
+          h0[k][c] = *(const f32x4*)(hp + c * 512);
+          h1[k][c] = *(const f32x4*)(hp + c * 512 + 4);
+        }
+      }
+    }
+  }
+  float y = 0.f;
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) {
+    if (k < nslots) {
+      float d = 0.f;
+#pragma unroll
+      for (int c = 0; c < kIC; ++c)
+        if (c * 512 < I) d = dot8(wv[k][c], h0[k][c], h1[k][c], d);
+      y = fmaf(wk[k], wave_sum_f32(d), y);
+    }
+  }
+  if (lane == 0) a.out[(int64_t)t * H + r] = y;
+}
+
+}  // namespace
+
+hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const dim3 block(kMoeWaves * 64);
+  hipLaunchKernelGGL(moe_router_kernel, dim3((a.num_experts + kMoeWaves - 1) / kMoeWaves), block,
+                     0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2((a.inter + kMoeWaves - 1) / kMoeWaves, a.top_k + a.num_shared, a.num_tokens);
+  hipLaunchKernelGGL(moe_gate_up_kernel, g2, block, 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(moe_down_kernel, dim3((a.hidden + kMoeWaves - 1) / kMoeWaves, a.num_tokens),
+                     block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace flint

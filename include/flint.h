@@ -282,6 +282,43 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
                                 const float* sinks, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * MoE sublayer at small-batch decode (1..8 tokens): router, sigmoid top-k,
+ * routed and shared SwiGLU experts ("Day-0 Support for Flint on vLLM",
+ * hnkhoi.com, "Model architecture": hidden size 2048, 256 experts, sigmoid
+ * top-6, a shared expert; newruntime.com, "What happened": small-batch MoE and
+ * dense GEMV kernels).  Readings where the pages are silent: router logits
+ * z_e = <x, w_router[e]> with no bias; the top_k experts by z (fp32), ties to
+ * the lower index; weights sigmoid(z_id) normalised over the selection; each
+ * expert E(x) = W_down (silu(W_gate x) * (W_up x)) with silu(g) = g/(1+e^-g);
+ * shared experts join with weight 1:
+ *   out[t] = sum_k weight[t][k] E_{id[t][k]}(x[t]) + sum_s E_{experts+s}(x[t])
+ * Weights are bf16 bit patterns, row-major, shared experts after the routed:
+ *   w_router  [num_experts][hidden]
+ *   w_gate_up [num_experts + num_shared][2][inter][hidden]  (gate, then up)
+ *   w_down    [num_experts + num_shared][hidden][inter]
+ *   x [T][hidden] fp32 in; out [T][hidden] fp32; topk_ids [T][top_k] int32 and
+ *   topk_weights [T][top_k] fp32 out.  All 16-byte aligned.
+ * Supported: hidden a multiple of 512 up to 4096, inter 512, 1..256 routed
+ * experts, top_k 1..8, num_shared 0..2, num_tokens 0..8.  workspace: at least
+ * flint_moe_workspace_size bytes, 256-byte aligned, contents irrelevant.
+ * A NaN logit is never selected; NaN inputs give NaN outputs.
+ */
+typedef struct {
+  int32_t hidden;       /* 2048                               */
+  int32_t num_experts;  /* routed experts: 256                */
+  int32_t top_k;        /* experts selected per token: 6      */
+  int32_t inter;        /* FFN width of every expert: 512     */
+  int32_t num_shared;   /* always-active experts: 1           */
+} flint_moe_layer;
+
+size_t flint_moe_workspace_size(const flint_moe_layer* M, int32_t num_tokens);
+flint_status flint_moe_forward(const flint_moe_layer* M, int32_t num_tokens, const float* x,
+                               const uint16_t* w_router, const uint16_t* w_gate_up,
+                               const uint16_t* w_down, int32_t* topk_ids, float* topk_weights,
+                               float* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Status text, thread-local detail of the last non-OK status on this thread,
  * and the ABI version (FLINT_ABI_VERSION). */
 const char* flint_status_string(flint_status s);

@@ -20,6 +20,9 @@ GQA with 32 query and 4 KV heads of dim 128, bf16 KV, learned sinks):
   * fp8 cache contents     uniform random E4M3 codes: a random sign and a
                            magnitude code uniform in [0, max_code] (default
                            0x3F, |x| < 2), so no NaN code is ever drawn
+  * MoE weights            N(0, 1/fan_in) bf16, drawn like the bf16 caches
+                           (x ~ N(0,1), so router logits and FFN
+                           activations are O(1))
   * page tables            a seeded permutation of the physical pages
   * ragged lengths         uniform integers in [lo, hi], inclusive
 """
@@ -52,14 +55,16 @@ def torch_seed(seed: int, stream: tuple) -> int:
     return int(st) & ((1 << 63) - 1)
 
 
-def normal_bf16_bits_torch(seed: int, stream: tuple, shape, device="cpu"):
+def normal_bf16_bits_torch(seed: int, stream: tuple, shape, device="cpu", std: float = 1.0):
     """Like normal_bf16_bits but drawn by torch's generator on `device` (for
-    multi-GB caches: fast on the GPU).  Returns an int16 tensor of bf16 bit
-    patterns: N(0,1) fp32 draws truncated to their top 16 bits."""
+    multi-GB caches and weights: fast on the GPU).  Returns an int16 tensor of
+    bf16 bit patterns: N(0, std^2) fp32 draws truncated to their top 16 bits."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(torch_seed(seed, stream))
     x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
+    if std != 1.0:
+        x *= std
     return (x.view(torch.int32) >> 16).to(torch.int16)
 
 

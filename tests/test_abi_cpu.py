@@ -213,3 +213,51 @@ def test_merge_rejects_bad_arguments(kw):
     a.update(kw)
     assert fl.lib().flint_attn_merge(C.byref(fl.full_layer()), a["num_seqs"], a["ns"], a["po"],
                                      a["pl"], a["sinks"], a["out"], None) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# MoE sublayer
+# ---------------------------------------------------------------------------
+
+def _moe(M, **kw):
+    a = dict(T=1, x=P, wr=Q, wgu=Q + 0x100000, wd=Q + 0x200000, ids=P + 0x10000,
+             wts=P + 0x20000, out=P + 0x30000, ws=WS, ws_bytes=1 << 20)
+    a.update(kw)
+    return fl.lib().flint_moe_forward(C.byref(M), a["T"], a["x"], a["wr"], a["wgu"], a["wd"],
+                                      a["ids"], a["wts"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("field,value", [("hidden", 1000), ("hidden", 8192), ("inter", 256),
+                                         ("num_experts", 257), ("num_experts", 0), ("top_k", 9),
+                                         ("top_k", 0), ("num_shared", 3)])
+def test_moe_rejects_unsupported_shapes(field, value):
+    M = fl.moe_layer()
+    setattr(M, field, value)
+    assert _moe(M) == UNSUPPORTED
+    assert fl.flint_moe_workspace_size(M, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=9), UNSUPPORTED),
+    (dict(x=None), INVALID),
+    (dict(wd=None), INVALID),
+    (dict(ids=None), INVALID),
+    (dict(x=P + 4), INVALID),
+    (dict(wgu=Q + 8), INVALID),
+    (dict(out=P), INVALID),              # aliases x
+    (dict(ws_bytes=16), WS_SMALL),
+    (dict(ws=None), WS_SMALL),
+    (dict(ws=WS + 64), INVALID),
+])
+def test_moe_rejects_bad_arguments(kw, status):
+    assert _moe(fl.moe_layer(), **kw) == status
+    assert fl.lib().flint_last_error().decode() != ""
+
+
+def test_moe_zero_tokens_is_a_no_op_and_workspace_grows_with_tokens():
+    M = fl.moe_layer()
+    assert _moe(M, T=0, x=None, out=None) == 0
+    w1, w8 = fl.flint_moe_workspace_size(M, 1), fl.flint_moe_workspace_size(M, 8)
+    # logits and the SwiGLU activations, fp32, each part 256-byte aligned
+    assert w1 == 1024 + 7 * 512 * 4
+    assert w8 == 8 * 256 * 4 + 8 * 7 * 512 * 4
