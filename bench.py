@@ -116,6 +116,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill leg (for counter runs of the prefill kernel)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -334,6 +335,9 @@ def main():
         result["fp8"] = bench_fp8(fl, dev, layers, ws, ones, seq_lens, capture, time_graph,
                                   args.steps, stream, eps)
 
+    if not args.no_moe:
+        result["moe"] = bench_moe(fl, dev, capture, stream)
+
     if not args.no_prefill:
         result["prefill"] = bench_prefill(fl, dev, stream)
 
@@ -405,6 +409,73 @@ def bench_fp8(fl, dev, layers, ws, ones, seq_lens, capture, time_graph, steps, s
                             "achieved": round(achieved, 1),
                             "frac": round(achieved / HBM_PEAK_GBPS, 4)}}
     del l8, g8
+    return res
+
+
+MOE_LAYERS = 8
+
+
+def bench_moe(fl, dev, capture, stream):
+    """Flint's MoE sublayer at 1 and 8 tokens: 8 distinct layers of synthetic
+    N(0, 1/fan_in) bf16 weights (1.6 GB each, so the 256 MB last-level cache
+    cannot hold a cycle of them), each with its own x ~ N(0,1), in one graph.
+    HBM bytes per layer are algorithmic: the router, the gate/up/down rows of
+    every distinct expert the tokens selected plus the shared expert, x and
+    the outputs."""
+    import torch
+    M = fl.moe_layer()
+    H, E, I, S, K = M.hidden, M.num_experts, M.inter, M.num_shared, M.top_k
+    res = {"workload": "MoE sublayer: hidden 2048, 256 routed experts, sigmoid top-6, one "
+                       "shared expert, SwiGLU width 512 (a reading); 8 distinct layers",
+           "bound": "hbm", "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
+    ws = torch.empty(fl.flint_moe_workspace_size(M, 8), dtype=torch.uint8, device=dev)
+    layers = []
+    for l in range(MOE_LAYERS):
+        layers.append(dict(
+            wr=synth.normal_bf16_bits_torch(SEED, (6, l, 1), (E, H), dev, std=H ** -0.5),
+            wgu=synth.normal_bf16_bits_torch(SEED, (6, l, 2), (E + S, 2, I, H), dev,
+                                             std=H ** -0.5),
+            wd=synth.normal_bf16_bits_torch(SEED, (6, l, 3), (E + S, H, I), dev, std=I ** -0.5)))
+    torch.cuda.synchronize()
+    expert_bytes = (2 * I * H + H * I) * 2
+    for T in (1, 8):
+        for l, L in enumerate(layers):
+            L["x"] = torch.from_numpy(synth.normal(SEED, (6, l, 4, T), (T, H))).to(dev)
+            L["out"] = torch.empty((T, H), dtype=torch.float32, device=dev)
+            L["ids"] = torch.empty((T, K), dtype=torch.int32, device=dev)
+            L["w"] = torch.empty((T, K), dtype=torch.float32, device=dev)
+
+        def run():
+            for L in layers:
+                fl.flint_moe_forward(M, L["x"], L["wr"], L["wgu"], L["wd"], out=L["out"],
+                                     topk_ids=L["ids"], topk_weights=L["w"], workspace=ws)
+        run()
+        torch.cuda.synchronize()
+        g = capture(run)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * MOE_LAYERS)
+        nbytes = [E * H * 2 + (len(np.unique(L["ids"].cpu().numpy())) + S) * expert_bytes
+                  + T * H * 4 * 2 + T * K * 8 for L in layers]
+        per = float(np.mean(nbytes))
+        gbps = per / (us * 1e-6) / 1e9
+        finite = all(bool(torch.isfinite(L["out"]).all()) for L in layers)
+        log(f"bench: MoE sublayer, {T} token(s): {us:.2f} us/layer, {per / 1e6:.1f} MB, "
+            f"{gbps:.0f} GB/s")
+        res[f"tokens_{T}"] = {"us_per_layer": round(us, 2), "bytes_per_layer": round(per),
+                              "achieved": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                              "finite": finite}
+    del layers
+    torch.cuda.empty_cache()
     return res
 
 

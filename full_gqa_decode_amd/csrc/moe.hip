@@ -17,10 +17,10 @@
 // 16-byte lane loads -- one 1 KiB contiguous load per instruction --, widens
 // bf16 to fp32 exactly (a shift) and accumulates fp32 FMAs against x; a
 // DPP/permlane reduction gives the dot product.  Three launches:
-//   K5a router logits (one wave per expert row, every token);
-//   K5b top-k -- recomputed by every wave from the token's logits, so no
-//       launch is spent on it -- then the gate and up rows and SwiGLU (one
-//       wave per (FFN row, slot, token));
+//   K5a router logits (one single-wave workgroup per expert row, every token);
+//   K5b top-k -- recomputed by one wave of every workgroup from the token's
+//       logits, so no launch is spent on it -- then the gate and up rows and
+//       SwiGLU (each wave two FFN rows of one (slot, token));
 //   K5c down rows and the weighted combine (one wave per (output row, token)).
 // Every wave issues all of its row loads before it waits for any, so each
 // launch costs one dependent memory round trip after its inputs arrive.
@@ -67,11 +67,11 @@ __device__ __forceinline__ int wave_min_i32(int x) {
              min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
-// K5a: z[t][e] = <x_t, Wr_e> for every token; one wave per expert row.
-__global__ __launch_bounds__(kMoeWaves * 64) void moe_router_kernel(MoeArgs a) {
+// K5a: z[t][e] = <x_t, Wr_e> for every token; one single-wave workgroup per
+// expert row, so the 1 MB of router rows spreads over every CU.
+__global__ __launch_bounds__(64) void moe_router_kernel(MoeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * kMoeWaves + (threadIdx.x >> 6);
-  if (e >= a.num_experts) return;
+  const int e = blockIdx.x;
   const int H = a.hidden;
   const uint16_t* w = a.w_router + (int64_t)e * H + lane * 8;
   u32x4 wv[kMoeMaxChunks];
@@ -146,16 +146,20 @@ __device__ __forceinline__ TopK select_topk(const MoeArgs& a, int t, int lane) {
 }
 
 // K5b: h[t][slot][j] = silu(<x_t, Wg_j>) * <x_t, Wu_j> for the expert of the
-// slot (slots top_k.. are the shared experts).  Grid (FFN rows / 4, slots,
-// tokens); one wave per FFN row j.  The first wave of each token's grid row
-// also writes the token's top-k ids and weights.
+// slot (slots top_k.. are the shared experts).  Grid (FFN rows / (4 * kJW),
+// slots, tokens); each wave takes kJW FFN rows j.  Wave 0 selects the token's
+// experts and passes the slot's expert to the others through LDS; the first
+// workgroup of each token also writes the token's top-k ids and weights.
+constexpr int kJW = 2;  // FFN rows per wave
+
 __global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int slot = blockIdx.y, t = blockIdx.z;
-  const int j = blockIdx.x * kMoeWaves + w;
+  const int j0 = (blockIdx.x * kMoeWaves + w) * kJW;
   const int H = a.hidden, I = a.inter;
   const int nslots = a.top_k + a.num_shared;
+  __shared__ int sm_expert;
   // x does not wait for the selection
   f32x4 x0[kMoeMaxChunks], x1[kMoeMaxChunks];
 #pragma unroll
@@ -168,47 +172,55 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) 
   }
   int expert = a.num_experts + (slot - a.top_k);
   if (slot < a.top_k) {
-    const TopK tk = select_topk(a, t, lane);
-#pragma unroll
-    for (int k = 0; k < kMoeMaxTopK; ++k)
-      if (k == slot) expert = tk.ids[k];
-    if (blockIdx.x == 0 && w == 0 && slot == 0) {
-      int id = 0;
-      float wt = 0.f;
+    if (w == 0) {
+      const TopK tk = select_topk(a, t, lane);
 #pragma unroll
       for (int k = 0; k < kMoeMaxTopK; ++k)
-        if (k == lane) {
-          id = tk.ids[k];
-          wt = tk.weights[k];
+        if (k == slot) expert = tk.ids[k];
+      if (lane == 0) sm_expert = expert;
+      if (blockIdx.x == 0 && slot == 0) {
+        int id = 0;
+        float wt = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMoeMaxTopK; ++k)
+          if (k == lane) {
+            id = tk.ids[k];
+            wt = tk.weights[k];
+          }
+        if (lane < a.top_k) {
+          a.topk_ids[t * a.top_k + lane] = id;
+          a.topk_weights[t * a.top_k + lane] = wt;
         }
-      if (lane < a.top_k) {
-        a.topk_ids[t * a.top_k + lane] = id;
-        a.topk_weights[t * a.top_k + lane] = wt;
       }
     }
+    __syncthreads();
+    expert = sm_expert;
   }
-  if (j >= I) return;
-  const uint16_t* wg = a.w_gate_up + ((int64_t)expert * 2 * I + j) * H + lane * 8;
-  const uint16_t* wu = wg + (int64_t)I * H;
-  u32x4 gv[kMoeMaxChunks], uv[kMoeMaxChunks];
+  for (int jj = 0; jj < kJW; ++jj) {
+    const int j = j0 + jj;
+    if (j >= I) break;
+    const uint16_t* wg = a.w_gate_up + ((int64_t)expert * 2 * I + j) * H + lane * 8;
+    const uint16_t* wu = wg + (int64_t)I * H;
+    u32x4 gv[kMoeMaxChunks], uv[kMoeMaxChunks];
 #pragma unroll
-  for (int c = 0; c < kMoeMaxChunks; ++c) {
-    if (c * 512 < H) {
-      gv[c] = __builtin_nontemporal_load((const u32x4*)(wg + c * 512));
-      uv[c] = __builtin_nontemporal_load((const u32x4*)(wu + c * 512));
+    for (int c = 0; c < kMoeMaxChunks; ++c) {
+      if (c * 512 < H) {
+        gv[c] = __builtin_nontemporal_load((const u32x4*)(wg + c * 512));
+        uv[c] = __builtin_nontemporal_load((const u32x4*)(wu + c * 512));
+      }
     }
-  }
-  float g = 0.f, u = 0.f;
+    float g = 0.f, u = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMoeMaxChunks; ++c) {
-    if (c * 512 < H) {
-      g = dot8(gv[c], x0[c], x1[c], g);
-      u = dot8(uv[c], x0[c], x1[c], u);
+    for (int c = 0; c < kMoeMaxChunks; ++c) {
+      if (c * 512 < H) {
+        g = dot8(gv[c], x0[c], x1[c], g);
+        u = dot8(uv[c], x0[c], x1[c], u);
+      }
     }
+    g = wave_sum_f32(g);
+    u = wave_sum_f32(u);
+    if (lane == 0) a.h[((int64_t)t * nslots + slot) * I + j] = g / (1.f + __expf(-g)) * u;
   }
-  g = wave_sum_f32(g);
-  u = wave_sum_f32(u);
-  if (lane == 0) a.h[((int64_t)t * nslots + slot) * I + j] = g / (1.f + __expf(-g)) * u;
 }
 
 // K5c: out[t][r] = sum_k w_k <Wd_{id_k}[r], h[t][k]> + sum_s <Wd_s[r], h[t][s]>.
@@ -262,11 +274,11 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_down_kernel(MoeArgs a) {
 hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   const dim3 block(kMoeWaves * 64);
-  hipLaunchKernelGGL(moe_router_kernel, dim3((a.num_experts + kMoeWaves - 1) / kMoeWaves), block,
-                     0, s, a);
+  hipLaunchKernelGGL(moe_router_kernel, dim3(a.num_experts), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g2((a.inter + kMoeWaves - 1) / kMoeWaves, a.top_k + a.num_shared, a.num_tokens);
+  const int rows_per_wg = kMoeWaves * kJW;
+  const dim3 g2((a.inter + rows_per_wg - 1) / rows_per_wg, a.top_k + a.num_shared, a.num_tokens);
   hipLaunchKernelGGL(moe_gate_up_kernel, g2, block, 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
