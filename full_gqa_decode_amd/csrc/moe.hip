@@ -69,26 +69,38 @@ __device__ __forceinline__ int wave_min_i32(int x) {
 
 // K5a: z[t][e] = <x_t, Wr_e> for every token; one single-wave workgroup per
 // expert row, so the 1 MB of router rows spreads over every CU.
+// CH = hidden / 512 (one 16-byte lane load per 512 elements of a row), a
+// template argument so that no register is held for
+// chunks a shape does not have.
+template <int CH>
 __global__ __launch_bounds__(64) void moe_router_kernel(MoeArgs a) {
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x;
   const int H = a.hidden;
   const uint16_t* w = a.w_router + (int64_t)e * H + lane * 8;
-  u32x4 wv[kMoeMaxChunks];
+  u32x4 wv[CH];
 #pragma unroll
-  for (int c = 0; c < kMoeMaxChunks; ++c)
-    if (c * 512 < H) wv[c] = __builtin_nontemporal_load((const u32x4*)(w + c * 512));
-  for (int t = 0; t < a.num_tokens; ++t) {
-    float acc = 0.f;
+  for (int c = 0; c < CH; ++c)
+    wv[c] = __builtin_nontemporal_load((const u32x4*)(w + c * 512));
+  // every token unrolled, so all of x is requested before any of it is used
+  float acc[kMoeMaxTokens];
 #pragma unroll
-    for (int c = 0; c < kMoeMaxChunks; ++c) {
-      if (c * 512 < H) {
+  for (int t = 0; t < kMoeMaxTokens; ++t) {
+    acc[t] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (t < a.num_tokens) {
         const float* xp = a.x + (int64_t)t * H + c * 512 + lane * 8;
-        acc = dot8(wv[c], *(const f32x4*)xp, *(const f32x4*)(xp + 4), acc);
+        acc[t] = dot8(wv[c], *(const f32x4*)xp, *(const f32x4*)(xp + 4), acc[t]);
       }
     }
-    const float z = wave_sum_f32(acc);
-    if (lane == 0) a.logits[(int64_t)t * a.num_experts + e] = z;
+  }
+#pragma unroll
+  for (int t = 0; t < kMoeMaxTokens; ++t) {
+    if (t < a.num_tokens) {
+      const float z = wave_sum_f32(acc[t]);
+      if (lane == 0) a.logits[(int64_t)t * a.num_experts + e] = z;
+    }
   }
 }
 
@@ -151,7 +163,9 @@ __device__ __forceinline__ TopK select_topk(const MoeArgs& a, int t, int lane) {
 // experts and passes the slot's expert to the others through LDS; the first
 // workgroup of each token also writes the token's top-k ids and weights.
 constexpr int kJW = 2;  // FFN rows per wave
+static_assert(kMoeMaxInter % (kMoeWaves * kJW) == 0, "whole FFN rows per wave");
 
+template <int CH>
 __global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -161,14 +175,12 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) 
   const int nslots = a.top_k + a.num_shared;
   __shared__ int sm_expert;
   // x does not wait for the selection
-  f32x4 x0[kMoeMaxChunks], x1[kMoeMaxChunks];
+  f32x4 x0[CH], x1[CH];
 #pragma unroll
-  for (int c = 0; c < kMoeMaxChunks; ++c) {
-    if (c * 512 < H) {
-      const float* xp = a.x + (int64_t)t * H + c * 512 + lane * 8;
-      x0[c] = *(const f32x4*)xp;
-      x1[c] = *(const f32x4*)(xp + 4);
-    }
+  for (int c = 0; c < CH; ++c) {
+    const float* xp = a.x + (int64_t)t * H + c * 512 + lane * 8;
+    x0[c] = *(const f32x4*)xp;
+    x1[c] = *(const f32x4*)(xp + 4);
   }
   int expert = a.num_experts + (slot - a.top_k);
   if (slot < a.top_k) {
@@ -196,30 +208,31 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) 
     __syncthreads();
     expert = sm_expert;
   }
-  for (int jj = 0; jj < kJW; ++jj) {
-    const int j = j0 + jj;
-    if (j >= I) break;
-    const uint16_t* wg = a.w_gate_up + ((int64_t)expert * 2 * I + j) * H + lane * 8;
-    const uint16_t* wu = wg + (int64_t)I * H;
-    u32x4 gv[kMoeMaxChunks], uv[kMoeMaxChunks];
+  // every row of the wave requested before any is used (I is a multiple of
+  // 4 * kJW, so all kJW rows exist)
+  u32x4 gv[kJW][CH], uv[kJW][CH];
 #pragma unroll
-    for (int c = 0; c < kMoeMaxChunks; ++c) {
-      if (c * 512 < H) {
-        gv[c] = __builtin_nontemporal_load((const u32x4*)(wg + c * 512));
-        uv[c] = __builtin_nontemporal_load((const u32x4*)(wu + c * 512));
-      }
+  for (int jj = 0; jj < kJW; ++jj) {
+    const uint16_t* wg = a.w_gate_up + ((int64_t)expert * 2 * I + j0 + jj) * H + lane * 8;
+    const uint16_t* wu = wg + (int64_t)I * H;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      gv[jj][c] = __builtin_nontemporal_load((const u32x4*)(wg + c * 512));
+      uv[jj][c] = __builtin_nontemporal_load((const u32x4*)(wu + c * 512));
     }
+  }
+#pragma unroll
+  for (int jj = 0; jj < kJW; ++jj) {
     float g = 0.f, u = 0.f;
 #pragma unroll
-    for (int c = 0; c < kMoeMaxChunks; ++c) {
-      if (c * 512 < H) {
-        g = dot8(gv[c], x0[c], x1[c], g);
-        u = dot8(uv[c], x0[c], x1[c], u);
-      }
+    for (int c = 0; c < CH; ++c) {
+      g = dot8(gv[jj][c], x0[c], x1[c], g);
+      u = dot8(uv[jj][c], x0[c], x1[c], u);
     }
     g = wave_sum_f32(g);
     u = wave_sum_f32(u);
-    if (lane == 0) a.h[((int64_t)t * nslots + slot) * I + j] = g / (1.f + __expf(-g)) * u;
+    if (lane == 0)
+      a.h[((int64_t)t * nslots + slot) * I + j0 + jj] = g / (1.f + __expf(-g)) * u;
   }
 }
 
@@ -269,18 +282,34 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_down_kernel(MoeArgs a) {
   if (lane == 0) a.out[(int64_t)t * H + r] = y;
 }
 
+template <int CH>
+hipError_t launch_moe_ch(const MoeArgs& a, hipStream_t s) {
+  const dim3 block(kMoeWaves * 64);
+  hipLaunchKernelGGL((moe_router_kernel<CH>), dim3(a.num_experts), dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows_per_wg = kMoeWaves * kJW;
+  const dim3 g2(a.inter / rows_per_wg, a.top_k + a.num_shared, a.num_tokens);
+  hipLaunchKernelGGL((moe_gate_up_kernel<CH>), g2, block, 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   const dim3 block(kMoeWaves * 64);
-  hipLaunchKernelGGL(moe_router_kernel, dim3(a.num_experts), dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int rows_per_wg = kMoeWaves * kJW;
-  const dim3 g2((a.inter + rows_per_wg - 1) / rows_per_wg, a.top_k + a.num_shared, a.num_tokens);
-  hipLaunchKernelGGL(moe_gate_up_kernel, g2, block, 0, s, a);
-  e = hipGetLastError();
+  hipError_t e;
+  switch (a.hidden / 512) {  // the API admits multiples of 512 up to kMoeMaxChunks * 512
+    case 1: e = launch_moe_ch<1>(a, s); break;
+    case 2: e = launch_moe_ch<2>(a, s); break;
+    case 3: e = launch_moe_ch<3>(a, s); break;
+    case 4: e = launch_moe_ch<4>(a, s); break;
+    case 5: e = launch_moe_ch<5>(a, s); break;
+    case 6: e = launch_moe_ch<6>(a, s); break;
+    case 7: e = launch_moe_ch<7>(a, s); break;
+    default: e = launch_moe_ch<8>(a, s); break;
+  }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moe_down_kernel, dim3((a.hidden + kMoeWaves - 1) / kMoeWaves, a.num_tokens),
                      block, 0, s, a);
