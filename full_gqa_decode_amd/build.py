@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libflint.so")
-SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip", "moe.hip"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip", "moe.hip", "moe_api.hip"]
 ARCH = "gfx950"
 
 

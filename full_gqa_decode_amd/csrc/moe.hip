@@ -27,7 +27,7 @@
 #include <climits>
 
 #include "device.h"
-#include "launch.h"
+#include "moe.h"
 
 namespace flint {
 
