@@ -278,7 +278,9 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int mt = 0; mt < kTiles; ++mt) {
           const float m_new = fmaxf(m_run[mt], pmax[mt]);
-          const float alpha = exp2_fast(m_run[mt] - m_new);
+          // a row that has seen no key yet holds zeros: nothing to rescale
+          // (and -inf - -inf would make the factor NaN)
+          const float alpha = m_run[mt] == -INFINITY ? 0.f : exp2_fast(m_run[mt] - m_new);
           l_part[mt] *= alpha;
           float al[4];
 #pragma unroll

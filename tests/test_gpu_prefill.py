@@ -99,6 +99,19 @@ def test_prefill_chunk_ragged_batch(window):
     assert max_err(got, case.expected()) <= TOL
 
 
+def test_windowed_prefill_with_chunk_starts_at_every_offset_mod_16():
+    # A chunk that starts at position base sees its window start at base - 512
+    # + row.  For base % 16 != 0 the first page pair a wave reads can hold
+    # keys of its first row's window while its later rows see none of them
+    # yet; those rows must come out finite and right.
+    reqs = [(513 + r + 96, 96) for r in range(16)]
+    case = PrefillCase(14, reqs, window=513)
+    got, _, _, _ = case.run_gpu()
+    bad = int((~np.isfinite(got)).sum())
+    assert bad == 0, f"{bad} non-finite outputs"
+    assert max_err(got, case.expected()) <= TOL
+
+
 def test_last_prefill_row_matches_decode_at_same_position():
     import torch
     import full_gqa_decode_amd as fl
