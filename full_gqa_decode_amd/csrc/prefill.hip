@@ -23,7 +23,7 @@
 // the two pages per dim row so that this operand is one 16-byte LDS read.  P
 // is split into bf16(p) and its bf16 remainder (two MFMAs) so the value
 // product is fp32-accurate.  Online softmax in log2 units with a lazy
-// reference max (moved only when a score exceeds it by 2^8), the sink joining
+// reference max (moved only when a probability would exceed 2^8), the sink joining
 // the denominator in the epilogue.  An fp8 E4M3 cache is widened to bf16
 // (exactly) as its pages are staged, with k_scale in the score scale and
 // v_scale applied to the output.
@@ -167,11 +167,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qop[mt][c]));
 
+  // m_run: the lazy reference max (log2 units).  It starts at the lowest
+  // finite float rather than -inf, so that a row's first visible key always
+  // moves it and a masked key (-inf) always gives exp2(-inf) = 0, never NaN.
   f32x4 acc[kTiles][8];
   float m_run[kTiles], l_part[kTiles];
 #pragma unroll
   for (int mt = 0; mt < kTiles; ++mt) {
-    m_run[mt] = -INFINITY;
+    m_run[mt] = -__FLT_MAX__;
     l_part[mt] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) acc[mt][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -260,27 +263,29 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
           }
         }
       }
-      // raw scores; the softmax runs on s * qscale (log2 units)
-      float pmax[kTiles];
+      // exponent arguments x = s * qscale - m_run (log2 units).  Lazy
+      // rescale: the reference max moves only when some x exceeds 8, so
+      // p = 2^x < 2^8 and the accumulators are rescaled a few times per row
+      // rather than every pair.  The exact row max is taken only then.
+      float xv[kTiles][8];
       bool grow = false;
 #pragma unroll
-      for (int mt = 0; mt < kTiles; ++mt) {
-        float x = sv[mt][0];
+      for (int mt = 0; mt < kTiles; ++mt)
 #pragma unroll
-        for (int j = 1; j < 8; ++j) x = fmaxf(x, sv[mt][j]);
-        pmax[mt] = max_xor32(max_xor16(x)) * a.qscale;
-        grow |= pmax[mt] > m_run[mt] + 8.f;
-      }
-      // lazy rescale: the reference max moves only when a score exceeds it
-      // by more than 8 (log2 units), so p < 2^8 and the accumulators are
-      // rescaled a few times per row rather than every pair
+        for (int j = 0; j < 8; ++j) {
+          xv[mt][j] = fmaf(sv[mt][j], a.qscale, -m_run[mt]);
+          grow |= xv[mt][j] > 8.f;
+        }
       if (__any(grow)) {
 #pragma unroll
         for (int mt = 0; mt < kTiles; ++mt) {
-          const float m_new = fmaxf(m_run[mt], pmax[mt]);
-          // a row that has seen no key yet holds zeros: nothing to rescale
-          // (and -inf - -inf would make the factor NaN)
-          const float alpha = m_run[mt] == -INFINITY ? 0.f : exp2_fast(m_run[mt] - m_new);
+          float x = sv[mt][0];
+#pragma unroll
+          for (int j = 1; j < 8; ++j) x = fmaxf(x, sv[mt][j]);
+          const float pmax = max_xor32(max_xor16(x)) * a.qscale;
+          const float m_new = fmaxf(m_run[mt], pmax);
+          // 0 for a row that had seen no key (its accumulators are zero)
+          const float alpha = exp2_fast(m_run[mt] - m_new);
           l_part[mt] *= alpha;
           float al[4];
 #pragma unroll
@@ -290,15 +295,15 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i2 = 0; i2 < 4; ++i2) acc[mt][nb][i2] *= al[i2];
           m_run[mt] = m_new;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv[mt][j] = fmaf(sv[mt][j], a.qscale, -m_new);
         }
       }
 #pragma unroll
       for (int mt = 0; mt < kTiles; ++mt) {
-        // a row that has seen no key yet keeps a finite reference
-        const float m_use = m_run[mt] == -INFINITY ? 0.f : m_run[mt];
         float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(fmaf(sv[mt][j], a.qscale, -m_use));
+        for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(xv[mt][j]);
         l_part[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
         bf16x8 ph, pl;
 #pragma unroll
