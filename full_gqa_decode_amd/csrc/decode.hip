@@ -311,18 +311,20 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
 
   // ---- loads that do not wait for seq_len -------------------------------
   constexpr int QPW = (kGroup + WAVES - 1) / WAVES;  // fused: q heads per wave
-  double x0[QPW], x1[QPW];    // fused: raw q of heads w, w+WAVES, ...
+  // fused: raw q of heads w, w+WAVES, ..., kept in fp32 until the norm
+  // widens them, so that nothing waits for these loads before the page
+  // loads below are issued
+  float x0[QPW], x1[QPW];
   f32x4 qraw[8];              // unfused: fp32 q of column n, dims c*32+gq*8..+7
   if (FUSED) {
 #pragma unroll
     for (int j = 0; j < QPW; ++j) {
-      const int hh = w + j * WAVES;
-      x0[j] = x1[j] = 0.0;
-      if (hh < kGroup) {
-        const float* x = a.q_in + ((int64_t)b * hq + g * kGroup + hh) * kHeadDim;
-        x0[j] = x[lane];
-        x1[j] = x[lane + 64];
-      }
+      // unconditional (a clamped head; only heads < kGroup are used): a load
+      // under a branch would be waited for at the branch's join
+      const int hh = min(w + j * WAVES, kGroup - 1);
+      const float* x = a.q_in + ((int64_t)b * hq + g * kGroup + hh) * kHeadDim;
+      x0[j] = x[lane];
+      x1[j] = x[lane + 64];
     }
   } else {
     const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim;
@@ -340,10 +342,6 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
   };
   int lo, p_begin, p_end;
   range(a.max_seq_len - 1, lo, p_begin, p_end);
-  // fused, rotating layers: this lane's RoPE angle for the speculated
-  // position, computed while the loads below are in flight
-  double cs = 1.0, sn = 0.0;
-  if (FUSED && a.use_rope) rope_cos_sin(a.max_seq_len - 1, lane, a.rope_theta, &cs, &sn);
   Raw r[NR];
   int bad = 0;
   auto issue = [&](int k) {  // page id and loads of this wave's k-th page
@@ -358,6 +356,12 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
   };
 #pragma unroll
   for (int k = 0; k < NR; ++k) issue(k);
+  // fused, rotating layers: this lane's RoPE angle for the speculated
+  // position (fp64), computed while the loads above are in flight.  q_in was
+  // requested before the pages, and loads complete in issue order, so
+  // waiting for q later never waits for a page.
+  double cs = 1.0, sn = 0.0;
+  if (FUSED && a.use_rope) rope_cos_sin(a.max_seq_len - 1, lane, a.rope_theta, &cs, &sn);
 
   // ---- the request's real length ------------------------------------------
   const int seq_len = a.seq_lens[b];

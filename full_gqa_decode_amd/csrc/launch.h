@@ -103,8 +103,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeWavesSingle = 8;
 constexpr int kSinglePages = 40;
-// kShortMinPages: least pages per split the plan gives a short range (the
-// 513-key window spreads over many CUs, then the merge kernel runs).
-constexpr int kShortMinPages = 2;
+// kShortMinPages: least pages per split the plan gives a short range.  The
+// 513-key window at batch 1 then takes 7 splits: 28 workgroups still spread
+// its 1 MB over enough CUs, and at 8 splits or fewer the merge runs the
+// one-pass small-merge kernel.  Measured per fused sliding step in a graph:
+// 8.4 us at 7 splits, 9.0 us at 17 (2 pages each), 9.4 at 4.
+constexpr int kShortMinPages = 5;
 
 }  // namespace flint
