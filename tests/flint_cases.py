@@ -31,27 +31,30 @@ def down16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def layers(window, fp8=None):
-    """(oracle layer, library layer); fp8 = (k_scale, v_scale) selects an fp8
-    E4M3 cache with those scales (fp32 values, passed to both sides)."""
+def layers(window, fp8=None, hkv=4):
+    """(oracle layer, library layer) with hkv KV heads (8 query heads each);
+    fp8 = (k_scale, v_scale) selects an fp8 E4M3 cache with those scales
+    (fp32 values, passed to both sides)."""
     import full_gqa_decode_amd as fl
     rope = 1 if window else 0
     # the library receives eps as fp32; the oracle uses that same value
     eps = float(np.float32(1e-6))
     if fp8 is None:
-        return (oracle.layer(window=window, use_rope=rope, eps=eps),
-                fl.layer(window=window, use_rope=rope, rms_eps=eps))
+        return (oracle.layer(window=window, use_rope=rope, eps=eps, hq=8 * hkv, hkv=hkv),
+                fl.layer(window=window, use_rope=rope, rms_eps=eps, num_q_heads=8 * hkv,
+                         num_kv_heads=hkv))
     ks, vs = (float(np.float32(x)) for x in fp8)
-    return (oracle.layer(window=window, use_rope=rope, eps=eps, kv_fp8=1, k_scale=ks, v_scale=vs),
+    return (oracle.layer(window=window, use_rope=rope, eps=eps, kv_fp8=1, k_scale=ks, v_scale=vs,
+                         hq=8 * hkv, hkv=hkv),
             fl.layer(window=window, use_rope=rope, rms_eps=eps, kv_dtype=fl.FLINT_KV_FP8_E4M3,
-                     k_scale=ks, v_scale=vs))
+                     k_scale=ks, v_scale=vs, num_q_heads=8 * hkv, num_kv_heads=hkv))
 
 
 def empty_caches(L, num_blocks, device=False):
     """K and V caches of num_blocks pages filled with the format's NaN
     sentinel, on the host (numpy) or the GPU (torch)."""
     fill = SENTINEL8 if L.kv_fp8 else SENTINEL
-    shapes = (oracle.k_cache_shape(num_blocks), oracle.v_cache_shape(num_blocks))
+    shapes = (oracle.k_cache_shape(num_blocks, hkv=L.hkv), oracle.v_cache_shape(num_blocks, hkv=L.hkv))
     if not device:
         return tuple(np.full(sh, fill, oracle.cache_dtype(L)) for sh in shapes)
     import torch
@@ -71,9 +74,10 @@ class DecodeCase:
     (both sides); the new token of request b is at position ctxs[b]-1."""
 
     def __init__(self, seed, ctxs, window=0, ring=False, weights_one=True, extra_pages=3,
-                 fp8=None):
+                 fp8=None, hkv=4):
         self.seed, self.ctxs, self.window = seed, list(ctxs), window
-        self.L, self.FL = layers(window, fp8)
+        self.L, self.FL = layers(window, fp8, hkv)
+        self.hkv, self.hq = hkv, 8 * hkv
         B = len(ctxs)
         self.B = B
         tag = (hash((tuple(ctxs), window, ring)) & 0xFFFF,)
@@ -89,7 +93,7 @@ class DecodeCase:
         self.num_blocks = nb + extra_pages
         self.qw = synth.norm_weight(seed, tag + (synth.QW,), 128, weights_one)
         self.kw = synth.norm_weight(seed, tag + (synth.KW,), 128, weights_one)
-        self.sinks = synth.normal(seed, tag + (synth.SINK,), 32)
+        self.sinks = synth.normal(seed, tag + (synth.SINK,), self.hq)
         # tokens to append: all of them, or (ring) only the pages the window can see
         toks, q_rows = [], []
         for b, c in enumerate(ctxs):
@@ -100,18 +104,18 @@ class DecodeCase:
         self.toks = toks
         T = sum(c - f for _, f, c in toks)
         self.T = T
-        self.q_in = np.zeros((T, 32, 128), np.float32)
-        self.k_in = np.empty((T, 4, 128), np.float32)
-        self.v_in = np.empty((T, 4, 128), np.float32)
+        self.q_in = np.zeros((T, self.hq, 128), np.float32)
+        self.k_in = np.empty((T, hkv, 128), np.float32)
+        self.v_in = np.empty((T, hkv, 128), np.float32)
         self.pos = np.empty(T, np.int32)
         self.slots = np.empty(T, np.int32)
         self.last_row = np.empty(B, np.int64)
         o = 0
         for b, f, c in toks:
             n = c - f
-            self.k_in[o:o + n] = synth.normal(seed, tag + (synth.K, b), (n, 4, 128))
-            self.v_in[o:o + n] = synth.normal(seed, tag + (synth.V, b), (n, 4, 128))
-            self.q_in[o + n - 1] = synth.normal(seed, tag + (synth.Q, b), (32, 128))
+            self.k_in[o:o + n] = synth.normal(seed, tag + (synth.K, b), (n, hkv, 128))
+            self.v_in[o:o + n] = synth.normal(seed, tag + (synth.V, b), (n, hkv, 128))
+            self.q_in[o + n - 1] = synth.normal(seed, tag + (synth.Q, b), (self.hq, 128))
             self.pos[o:o + n] = np.arange(f, c)
             for p in range(f, c):
                 self.slots[o + p - f] = oracle.slot(self.bt, b, p)
@@ -144,7 +148,7 @@ class DecodeCase:
         fl.flint_qk_norm_rope_append(self.FL, qd, up(self.k_in), up(self.v_in), up(self.qw),
                                      up(self.kw), up(self.pos), up(self.slots), qd, kd, vd)
         qdec = qd[torch.from_numpy(self.last_row).to(dev())].contiguous()
-        out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        out = torch.empty((self.B, self.hq, 128), dtype=torch.float32, device=dev())
         fl.flint_attn_decode(self.FL, qdec, kd, vd, up(self.bt), up(self.seq_lens),
                              max(self.ctxs), up(self.sinks), out, workspace=workspace,
                              pages_per_split=pages_per_split)
@@ -162,7 +166,7 @@ class DecodeCase:
         keep[self.last_row] = False
         pre = np.nonzero(keep)[0]
         if len(pre):
-            qs = torch.empty((len(pre), 32, 128), dtype=torch.float32, device=dev())
+            qs = torch.empty((len(pre), self.hq, 128), dtype=torch.float32, device=dev())
             fl.flint_qk_norm_rope_append(self.FL, up(self.q_in[pre]), up(self.k_in[pre]),
                                          up(self.v_in[pre]), up(self.qw), up(self.kw),
                                          up(self.pos[pre]), up(self.slots[pre]), qs, kd, vd)
@@ -170,8 +174,8 @@ class DecodeCase:
         slots = self.slots[r].copy()
         if slot_delta is not None:
             slots = slots + np.asarray(slot_delta, np.int32)
-        out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
-        qo = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        out = torch.empty((self.B, self.hq, 128), dtype=torch.float32, device=dev())
+        qo = torch.empty((self.B, self.hq, 128), dtype=torch.float32, device=dev())
         fl.flint_attn_decode_step(self.FL, up(self.q_in[r]), up(self.k_in[r]), up(self.v_in[r]),
                                   up(self.qw), up(self.kw), up(slots), kd, vd, up(self.bt),
                                   up(self.seq_lens), max(self.ctxs), up(self.sinks), out,
@@ -185,8 +189,9 @@ class CacheDecodeCase:
     so K2/K3 are tested on their own.  fp8 = (k_scale, v_scale): an fp8 cache
     of random codes (K magnitudes below 2, V below 30, before scaling)."""
 
-    def __init__(self, seed, ctxs, window=0, ring=False, q_scale=1.0, fp8=None):
-        self.L, self.FL = layers(window, fp8)
+    def __init__(self, seed, ctxs, window=0, ring=False, q_scale=1.0, fp8=None, hkv=4):
+        self.L, self.FL = layers(window, fp8, hkv)
+        self.hkv, self.hq = hkv, 8 * hkv
         self.ctxs = list(ctxs)
         B = len(ctxs)
         self.B = B
@@ -201,13 +206,17 @@ class CacheDecodeCase:
                                                      [-(-c // 16) for c in ctxs], self.bt_stride)
         self.num_blocks = nb
         if fp8 is None:
-            self.kc = synth.normal_bf16_bits(seed, tag + (synth.KC,), oracle.k_cache_shape(nb))
-            self.vc = synth.normal_bf16_bits(seed, tag + (synth.VC,), oracle.v_cache_shape(nb))
+            self.kc = synth.normal_bf16_bits(seed, tag + (synth.KC,),
+                                             oracle.k_cache_shape(nb, hkv=hkv))
+            self.vc = synth.normal_bf16_bits(seed, tag + (synth.VC,),
+                                             oracle.v_cache_shape(nb, hkv=hkv))
         else:
-            self.kc = synth.fp8_codes(seed, tag + (synth.KC,), oracle.k_cache_shape(nb), 0x3F)
-            self.vc = synth.fp8_codes(seed, tag + (synth.VC,), oracle.v_cache_shape(nb), 0x5F)
-        self.q = synth.normal(seed, tag + (synth.Q,), (B, 32, 128)) * np.float32(q_scale)
-        self.sinks = synth.normal(seed, tag + (synth.SINK,), 32)
+            self.kc = synth.fp8_codes(seed, tag + (synth.KC,), oracle.k_cache_shape(nb, hkv=hkv),
+                                      0x3F)
+            self.vc = synth.fp8_codes(seed, tag + (synth.VC,), oracle.v_cache_shape(nb, hkv=hkv),
+                                      0x5F)
+        self.q = synth.normal(seed, tag + (synth.Q,), (B, self.hq, 128)) * np.float32(q_scale)
+        self.sinks = synth.normal(seed, tag + (synth.SINK,), self.hq)
         self.seq_lens = np.array(ctxs, np.int32)
 
     def expected(self):
@@ -217,7 +226,7 @@ class CacheDecodeCase:
     def run_gpu(self, pages_per_split=0, sinks=None, seq_lens=None, bt=None, max_seq_len=None):
         import torch
         import full_gqa_decode_amd as fl
-        out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
+        out = torch.empty((self.B, self.hq, 128), dtype=torch.float32, device=dev())
         fl.flint_attn_decode(self.FL, up(self.q), up(self.kc), up(self.vc),
                              up(self.bt if bt is None else bt),
                              up(self.seq_lens if seq_lens is None else seq_lens),

@@ -14,8 +14,9 @@ class PrefillCase:
     """Requests with (seq_len, q_len): every token is appended; the last q_len
     rows of each request are the chunk's queries."""
 
-    def __init__(self, seed, reqs, window=0, fp8=None):
-        self.L, self.FL = layers(window, fp8)
+    def __init__(self, seed, reqs, window=0, fp8=None, hkv=4):
+        self.L, self.FL = layers(window, fp8, hkv)
+        self.hkv, self.hq = hkv, 8 * hkv
         self.reqs = reqs
         B = len(reqs)
         tag = (hash((tuple(reqs), window, 11)) & 0xFFFF,)
@@ -23,21 +24,21 @@ class PrefillCase:
         self.bt, nb = synth.shuffled_block_table(seed, tag + (synth.PERM,), B,
                                                  [-(-s // 16) for s, _ in reqs], self.bt_stride)
         self.num_blocks = nb + 2
-        self.sinks = synth.normal(seed, tag + (synth.SINK,), 32)
+        self.sinks = synth.normal(seed, tag + (synth.SINK,), self.hq)
         self.qw = synth.norm_weight(seed, tag + (synth.QW,), 128, False)
         self.kw = synth.norm_weight(seed, tag + (synth.KW,), 128, False)
         T = sum(s for s, _ in reqs)
-        self.k_in = np.empty((T, 4, 128), np.float32)
-        self.v_in = np.empty((T, 4, 128), np.float32)
-        self.q_in = np.empty((T, 32, 128), np.float32)
+        self.k_in = np.empty((T, hkv, 128), np.float32)
+        self.v_in = np.empty((T, hkv, 128), np.float32)
+        self.q_in = np.empty((T, self.hq, 128), np.float32)
         self.pos = np.empty(T, np.int32)
         self.slots = np.empty(T, np.int32)
         chunk_rows, cu = [], [0]
         o = 0
         for b, (s, ql) in enumerate(reqs):
-            self.k_in[o:o + s] = synth.normal(seed, tag + (synth.K, b), (s, 4, 128))
-            self.v_in[o:o + s] = synth.normal(seed, tag + (synth.V, b), (s, 4, 128))
-            self.q_in[o:o + s] = synth.normal(seed, tag + (synth.Q, b), (s, 32, 128))
+            self.k_in[o:o + s] = synth.normal(seed, tag + (synth.K, b), (s, hkv, 128))
+            self.v_in[o:o + s] = synth.normal(seed, tag + (synth.V, b), (s, hkv, 128))
+            self.q_in[o:o + s] = synth.normal(seed, tag + (synth.Q, b), (s, self.hq, 128))
             self.pos[o:o + s] = np.arange(s)
             self.slots[o:o + s] = [oracle.slot(self.bt, b, p) for p in range(s)]
             chunk_rows += list(range(o + s - ql, o + s))
@@ -60,7 +61,7 @@ class PrefillCase:
                            self.kw, self.pos[need], skip, kc, vc)
         qb = oracle.bf16_rne_f64(qh)
         qf = synth.bf16_bits_to_f32(qb).astype(np.float64)
-        full_q = np.zeros((len(self.chunk_rows), 32, 128))
+        full_q = np.zeros((len(self.chunk_rows), self.hq, 128))
         idx = np.arange(len(self.chunk_rows)) if rows is None else np.asarray(rows)
         full_q[idx] = qf
         return oracle.attn_prefill(self.L, full_q, self.cu, kc, vc, self.bt, self.seq_lens,
@@ -75,7 +76,8 @@ class PrefillCase:
                                      up(self.qw), up(self.kw), up(self.pos), up(self.slots), qb,
                                      kd, vd)
         qc = qb[torch.from_numpy(self.chunk_rows).to(dev())].contiguous()
-        out = torch.empty((len(self.chunk_rows), 32, 128), dtype=torch.float32, device=dev())
+        out = torch.empty((len(self.chunk_rows), self.hq, 128), dtype=torch.float32,
+                          device=dev())
         bt = self.bt if bt is None else bt
         sl = self.seq_lens if seq_lens is None else seq_lens
         fl.flint_attn_prefill(self.FL, qc, up(self.cu), self.max_q, kd, vd, up(bt), up(sl),

@@ -1,7 +1,8 @@
-"""GPU parity for sliding windows narrower than a page or a page pair
-(window w: position t sees keys t-w+1..t), against the fp64 oracle.  The
-513-key window of the model spans many pages; these widths put the window's
-start and end inside one page, one page pair, or one split."""
+"""GPU parity against the fp64 oracle for shapes the model's own layers do
+not reach: sliding windows narrower than a page or a page pair (window w:
+position t sees keys t-w+1..t, so the window's start and end fall inside one
+page, one page pair or one split), and KV head counts other than four (the
+C ABI admits 1..8, each with 8 query heads)."""
 import numpy as np
 import pytest
 
@@ -51,3 +52,35 @@ def test_fp8_decode_small_windows(window):
         out, _, _, _ = case.run_gpu(pages_per_split=pps)
         err = max_err(out.cpu().numpy(), ref)
         assert err <= TOL, (window, pps, err)
+
+
+# ---- KV head counts other than the model's 4 (the ABI admits 1..8) --------
+
+@pytest.mark.parametrize("hkv", [1, 2, 8])
+def test_decode_and_fused_step_other_kv_head_counts(hkv):
+    for window in (0, 33):
+        case = DecodeCase(44, [1, 17, 300, 2000], window=window, weights_one=False, hkv=hkv)
+        ref, _, _, _ = case.expected()
+        for pps in (0, 1, 4):
+            out, _, _, _ = case.run_gpu(pages_per_split=pps)
+            assert max_err(out.cpu().numpy(), ref) <= TOL, (hkv, window, pps)
+        out, _, _, _ = case.run_gpu_fused()
+        assert max_err(out.cpu().numpy(), ref) <= TOL, (hkv, window, "fused")
+
+
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_prefill_other_kv_head_counts(hkv):
+    from test_gpu_prefill import PrefillCase
+    for window in (0, 33):
+        case = PrefillCase(45, [(300, 300), (700, 90)], window=window, hkv=hkv)
+        got, _, _, _ = case.run_gpu()
+        assert max_err(got, case.expected()) <= TOL, (hkv, window)
+
+
+@pytest.mark.parametrize("hkv", [1, 8])
+def test_fp8_decode_other_kv_head_counts(hkv):
+    case = DecodeCase(46, [1, 40, 900], window=0, weights_one=False, fp8=(1.0 / 16, 0.5),
+                      hkv=hkv)
+    ref, _, _, _ = case.expected()
+    out, _, _, _ = case.run_gpu()
+    assert max_err(out.cpu().numpy(), ref) <= TOL
