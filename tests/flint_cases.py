@@ -31,23 +31,30 @@ def down16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def layers(window, fp8=None, hkv=4):
+def layers(window, fp8=None, hkv=4, rope=None, theta=10000.0, scale=None, eps=1e-6):
     """(oracle layer, library layer) with hkv KV heads (8 query heads each);
     fp8 = (k_scale, v_scale) selects an fp8 E4M3 cache with those scales
-    (fp32 values, passed to both sides)."""
+    (fp32 values, passed to both sides).  RoPE is on for sliding layers
+    unless `rope` says otherwise; theta, scale (default 1/sqrt(128)) and eps
+    go to both sides, rounded to fp32 where the library takes fp32."""
     import full_gqa_decode_amd as fl
-    rope = 1 if window else 0
-    # the library receives eps as fp32; the oracle uses that same value
-    eps = float(np.float32(1e-6))
-    if fp8 is None:
-        return (oracle.layer(window=window, use_rope=rope, eps=eps, hq=8 * hkv, hkv=hkv),
-                fl.layer(window=window, use_rope=rope, rms_eps=eps, num_q_heads=8 * hkv,
-                         num_kv_heads=hkv))
-    ks, vs = (float(np.float32(x)) for x in fp8)
-    return (oracle.layer(window=window, use_rope=rope, eps=eps, kv_fp8=1, k_scale=ks, v_scale=vs,
-                         hq=8 * hkv, hkv=hkv),
-            fl.layer(window=window, use_rope=rope, rms_eps=eps, kv_dtype=fl.FLINT_KV_FP8_E4M3,
-                     k_scale=ks, v_scale=vs, num_q_heads=8 * hkv, num_kv_heads=hkv))
+    rope = (1 if window else 0) if rope is None else int(rope)
+    # the library receives eps and the softmax scale as fp32; the oracle uses
+    # those same values
+    eps = float(np.float32(eps))
+    scale = float(np.float32(1.0 / np.sqrt(128) if scale is None else scale))
+    common = dict(window=window, use_rope=rope)
+    ks, vs, kvf = 1.0, 1.0, 0
+    if fp8 is not None:
+        ks, vs = (float(np.float32(x)) for x in fp8)
+        kvf = 1
+    Lo = oracle.layer(**common, eps=eps, hq=8 * hkv, hkv=hkv, theta=theta, scale=scale,
+                      kv_fp8=kvf, k_scale=ks, v_scale=vs)
+    Lf = fl.layer(**common, rms_eps=eps, num_q_heads=8 * hkv, num_kv_heads=hkv,
+                  rope_theta=theta, softmax_scale=scale,
+                  kv_dtype=fl.FLINT_KV_FP8_E4M3 if kvf else fl.FLINT_KV_BF16,
+                  k_scale=ks, v_scale=vs)
+    return Lo, Lf
 
 
 def empty_caches(L, num_blocks, device=False):
@@ -74,9 +81,9 @@ class DecodeCase:
     (both sides); the new token of request b is at position ctxs[b]-1."""
 
     def __init__(self, seed, ctxs, window=0, ring=False, weights_one=True, extra_pages=3,
-                 fp8=None, hkv=4):
+                 fp8=None, hkv=4, **layer_kw):
         self.seed, self.ctxs, self.window = seed, list(ctxs), window
-        self.L, self.FL = layers(window, fp8, hkv)
+        self.L, self.FL = layers(window, fp8, hkv, **layer_kw)
         self.hkv, self.hq = hkv, 8 * hkv
         B = len(ctxs)
         self.B = B

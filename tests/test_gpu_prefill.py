@@ -14,8 +14,8 @@ class PrefillCase:
     """Requests with (seq_len, q_len): every token is appended; the last q_len
     rows of each request are the chunk's queries."""
 
-    def __init__(self, seed, reqs, window=0, fp8=None, hkv=4):
-        self.L, self.FL = layers(window, fp8, hkv)
+    def __init__(self, seed, reqs, window=0, fp8=None, hkv=4, **layer_kw):
+        self.L, self.FL = layers(window, fp8, hkv, **layer_kw)
         self.hkv, self.hq = hkv, 8 * hkv
         self.reqs = reqs
         B = len(reqs)

@@ -84,3 +84,24 @@ def test_fp8_decode_other_kv_head_counts(hkv):
     ref, _, _, _ = case.expected()
     out, _, _, _ = case.run_gpu()
     assert max_err(out.cpu().numpy(), ref) <= TOL
+
+
+# ---- layer parameters other than the model's --------------------------------
+
+@pytest.mark.parametrize("window,rope,theta,scale,eps", [
+    (0, 1, 1e6, 0.05, 1e-5),         # full attention with RoPE, another base
+    (33, 1, 500000.0, 0.2, 1e-6),    # a short window, a large scale
+    (513, 0, 10000.0, 0.0625, 1e-6),  # a sliding window without RoPE
+])
+def test_other_rope_bases_scales_and_eps(window, rope, theta, scale, eps):
+    kw = dict(rope=rope, theta=theta, scale=scale, eps=eps)
+    case = DecodeCase(47, [1, 17, 700, 3000], window=window, weights_one=False, **kw)
+    ref, _, _, _ = case.expected()
+    out, _, _, _ = case.run_gpu()
+    assert max_err(out.cpu().numpy(), ref) <= TOL
+    out, _, _, _ = case.run_gpu_fused()
+    assert max_err(out.cpu().numpy(), ref) <= TOL
+    from test_gpu_prefill import PrefillCase
+    pc = PrefillCase(48, [(500, 500), (900, 130)], window=window, **kw)
+    got, _, _, _ = pc.run_gpu()
+    assert max_err(got, pc.expected()) <= TOL
