@@ -74,6 +74,18 @@ def test_moe_other_shape_two_shared_experts_top8():
     check(MoeCase(2, 3, dict(hidden=1024, experts=64, top_k=8, inter=512, shared=2)))
 
 
+@pytest.mark.parametrize("T,shape", [
+    (5, dict(hidden=1536, experts=100, top_k=4, inter=512, shared=1)),
+    (3, dict(hidden=4096, experts=256, top_k=6, inter=512, shared=1)),
+    (7, dict(hidden=3584, experts=37, top_k=2, inter=512, shared=2)),
+    (4, dict(hidden=2560, experts=9, top_k=8, inter=512, shared=0)),
+])
+def test_moe_other_hidden_sizes_and_expert_counts(T, shape):
+    # hidden/512 = 3, 8, 7, 5 (the kernels are specialised on it), expert
+    # counts that are not a multiple of the 64-lane selection width
+    check(MoeCase(7, T, shape))
+
+
 def test_moe_without_shared_expert():
     check(MoeCase(3, 2, dict(hidden=512, experts=256, top_k=1, inter=512, shared=0)))
 
