@@ -69,8 +69,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   double cs = 1.0, sn = 0.0;
   if (a.use_rope) rope_cos_sin(pos < 0 ? 0 : pos, lane, a.rope_theta, &cs, &sn);
   double y0, y1;
-  norm_rope_head(x[lane], x[lane + 64], is_q ? a.q_w : a.k_w, a.rms_eps, a.use_rope, cs, sn,
-                 lane, &y0, &y1);
+  const float* wp = is_q ? a.q_w : a.k_w;
+  norm_rope_head(x[lane], x[lane + 64], wp[lane], wp[lane + 64], a.rms_eps, a.use_rope, cs, sn,
+                 &y0, &y1);
 
   if (is_q) {
     if (bad) y0 = y1 = __builtin_nan("");

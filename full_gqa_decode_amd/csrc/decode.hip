@@ -313,8 +313,13 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
   constexpr int QPW = (kGroup + WAVES - 1) / WAVES;  // fused: q heads per wave
   // fused: raw q of heads w, w+WAVES, ..., kept in fp32 until the norm
   // widens them, so that nothing waits for these loads before the page
-  // loads below are issued
+  // loads below are issued.  With them, everything else the prologue reads:
+  // the norm weights and, for the split that will hold the new token, its
+  // raw K and V rows, its slot and the id of its page (for the speculated
+  // length).  Requested before the pages, these never wait for a page.
   float x0[QPW], x1[QPW];
+  float qw0 = 0.f, qw1 = 0.f, kw0 = 0.f, kw1 = 0.f, xk0 = 0.f, xk1 = 0.f, xv0 = 0.f, xv1 = 0.f;
+  int slot_pre = 0, pg_last_pre = -1;
   f32x4 qraw[8];              // unfused: fp32 q of column n, dims c*32+gq*8..+7
   if (FUSED) {
 #pragma unroll
@@ -326,6 +331,18 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
       x0[j] = x[lane];
       x1[j] = x[lane + 64];
     }
+    qw0 = a.q_w[lane];
+    qw1 = a.q_w[lane + 64];
+    const float* xk = a.k_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+    const float* xv = a.v_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+    kw0 = a.k_w[lane];
+    kw1 = a.k_w[lane + 64];
+    xk0 = xk[lane];
+    xk1 = xk[lane + 64];
+    xv0 = xv[lane];
+    xv1 = xv[lane + 64];
+    slot_pre = a.slots[b];
+    pg_last_pre = page_id(a, b, (a.max_seq_len - 1) / kPage);
   } else {
     const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim;
 #pragma unroll
@@ -400,7 +417,7 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
       const int hh = w + j * WAVES;
       if (hh < kGroup) {
         double y0, y1;
-        norm_rope_head(x0[j], x1[j], a.q_w, a.rms_eps, a.use_rope, cs, sn, lane, &y0, &y1);
+        norm_rope_head(x0[j], x1[j], qw0, qw1, a.rms_eps, a.use_rope, cs, sn, &y0, &y1);
         sm_q[hh][lane] = (float)y0;
         sm_q[hh][lane + 64] = (float)y1;
         if (s == 0 && a.q_out) {
@@ -412,14 +429,11 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
     }
     if (has_new && w < 2) {
       // the slot must be where the page table puts position t
-      const int pg = page_id(a, b, last_page);
-      const int slot = a.slots[b];
-      const bool ok = pg >= 0 && slot == pg * kPage + t % kPage;
+      const int pg = t == a.max_seq_len - 1 ? pg_last_pre : page_id(a, b, last_page);
+      const bool ok = pg >= 0 && slot_pre == pg * kPage + t % kPage;
       if (w == 0) {
-        const float* xk = a.k_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
         double y0, y1;
-        norm_rope_head(xk[lane], xk[lane + 64], a.k_w, a.rms_eps, a.use_rope, cs, sn, lane,
-                       &y0, &y1);
+        norm_rope_head(xk0, xk1, kw0, kw1, a.rms_eps, a.use_rope, cs, sn, &y0, &y1);
         const int64_t o = ((int64_t)pg * a.num_kv_heads + g) * (kPage * kHeadDim);
         if (KV8) {
           const uint32_t c0 = fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
@@ -443,11 +457,10 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
         }
         if (lane == 0) sm_fused_bad = !ok;
       } else {
-        const float* xv = a.v_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
         const int64_t o = ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage) + t % kPage;
         if (KV8) {
-          const uint32_t c0 = fp8_e4m3_rne_f64((double)xv[lane] / (double)a.v_scale);
-          const uint32_t c1 = fp8_e4m3_rne_f64((double)xv[lane + 64] / (double)a.v_scale);
+          const uint32_t c0 = fp8_e4m3_rne_f64((double)xv0 / (double)a.v_scale);
+          const uint32_t c1 = fp8_e4m3_rne_f64((double)xv1 / (double)a.v_scale);
           sm_vnew[lane] = (Elem)c0;
           sm_vnew[lane + 64] = (Elem)c1;
           if (ok) {
@@ -457,7 +470,7 @@ __global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void deco
             dst[fp8_v_off(t % kPage, lane + 64)] = (uint8_t)c1;
           }
         } else {
-          const uint16_t v0 = bf16_bits_rne(xv[lane]), v1 = bf16_bits_rne(xv[lane + 64]);
+          const uint16_t v0 = bf16_bits_rne(xv0), v1 = bf16_bits_rne(xv1);
           sm_vnew[lane] = (Elem)v0;
           sm_vnew[lane + 64] = (Elem)v1;
           if (ok) {

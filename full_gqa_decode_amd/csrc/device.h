@@ -217,16 +217,17 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int i, float theta, double
 
 // Per-head RMSNorm then (optionally) rotate-half RoPE of one 128-dim head,
 // one wave64: lane l holds dims l and l+64 (a RoPE pair) in x0, x1; on return
-// y0, y1 hold the result.  fp64 throughout; cs/sn are rope_cos_sin(pos, l).
-// Used by the stand-alone append and by the fused decode step, so both
-// produce bit-identical q, K and V.
-__device__ __forceinline__ void norm_rope_head(double x0, double x1, const float* w, float eps,
-                                               bool rope, double cs, double sn, int lane,
+// y0, y1 hold the result.  fp64 throughout; cs/sn are rope_cos_sin(pos, l);
+// w0, w1 are the norm weights of dims l and l+64 (passed as values so that a
+// caller can request them early).  Used by the stand-alone append and by the
+// fused decode step, so both produce bit-identical q, K and V.
+__device__ __forceinline__ void norm_rope_head(double x0, double x1, float w0, float w1,
+                                               float eps, bool rope, double cs, double sn,
                                                double* y0, double* y1) {
   const double ss = wave_sum_f64(x0 * x0 + x1 * x1);
   const double r = 1.0 / sqrt(ss / kHeadDim + (double)eps);
-  double a0 = x0 * r * (double)w[lane];
-  double a1 = x1 * r * (double)w[lane + 64];
+  double a0 = x0 * r * (double)w0;
+  double a1 = x1 * r * (double)w1;
   if (rope) {
     const double r0 = a0 * cs - a1 * sn;
     const double r1 = a1 * cs + a0 * sn;
