@@ -593,11 +593,32 @@ def cpu_baseline(layers, eps):
     for L in layers:
         worst = max(worst, float(np.max(np.abs(L["out"].cpu().numpy().astype(np.float64)
                                                - L["ref"]))))
-    log(f"bench: oracle step {secs:.2f} s on {nthreads} threads; max|gpu-oracle| {worst:.2e}")
+    # one thread: the attention of one full and one sliding layer (the append is
+    # negligible beside it), extrapolated to the step and labelled as such
+    one = {}
+    for full in (True, False):
+        L = next(L for L in layers if L["full"] == full)
+        h = L["host"]
+        Lo = Lf if full else Ls
+        qh = oracle.append(Lo, h["q"], h["k"], h["v"], ones, ones, np.array([t], np.int32),
+                           np.array([-1], np.int32), h["kc"], h["vc"])
+        t1 = time.perf_counter()
+        oracle.attn_decode(Lo, qh, h["kc"], h["vc"], h["bt"], np.array([CTX], np.int32),
+                           h["sinks"], nthreads=1)
+        one["full" if full else "sliding"] = (time.perf_counter() - t1) * 1e6
+    n_full = len(FULL_LAYERS)
+    single = {"us_full_layer": round(one["full"], 1), "us_sliding_layer": round(one["sliding"], 1),
+              "us_per_step_extrapolated": round(n_full * one["full"] +
+                                                (LAYERS - n_full) * one["sliding"], 1),
+              "threads": 1}
+    log(f"bench: oracle step {secs:.2f} s on {nthreads} threads; one thread: full layer "
+        f"{one['full'] / 1e6:.2f} s, sliding layer {one['sliding'] / 1e3:.1f} ms; "
+        f"max|gpu-oracle| {worst:.2e}")
     return ({"value": round(secs * 1e6, 1), "unit": "us/step", "cores": nthreads,
              "kind": "oracle",
              "sample": "the whole 49-layer step (append of the new token + attention for all "
-                       "32 heads of every layer), fp64, once"}, worst)
+                       "32 heads of every layer), fp64, once",
+             "single_thread": single}, worst)
 
 
 if __name__ == "__main__":
