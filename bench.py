@@ -119,6 +119,10 @@ def main():
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill leg (for counter runs of the prefill kernel)")
+    ap.add_argument("--batch-legs", action="store_true",
+                    help="only time batched decode: 64 ragged requests of 1024..131072 tokens "
+                         "(one full and one sliding layer) and batches of 2..16 requests at "
+                         "100K context (fused step), and print one JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times (the "
                          "known-size kernel that calibrates HBM byte counters) and exit")
@@ -137,6 +141,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.prefill_only:
         print(json.dumps(bench_prefill(fl, dev, None)), flush=True)
+        return
+    if args.batch_legs:
+        print(json.dumps(bench_batches(fl, dev)), flush=True)
         return
     eps = float(np.float32(1e-6))
     FULL = fl.layer(window=0, use_rope=0, rms_eps=eps)
@@ -477,6 +484,126 @@ def bench_moe(fl, dev, capture, stream):
     del layers
     torch.cuda.empty_cache()
     return res
+
+
+def _time_launches(fn, reps=10, warm=3):
+    """Mean µs per call of fn over reps calls after warm calls (HIP events on
+    the current stream)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bench_batches(fl, dev):
+    """Batched decode.  (1) 64 requests with lengths uniform in [1024, 131072]
+    (seeded), pages in one random physical order, one full and one sliding
+    layer, flint_attn_decode (K2 + K3) on a normalised q; algorithmic bytes
+    from the drawn lengths.  (2) B = 2, 4, 8, 16 requests at 100K context,
+    one fused step of a full and of a sliding layer each, in a graph of 6
+    (full) or 20 (sliding) distinct layers so that no layer's pages stay in
+    the caches between replays."""
+    import torch
+    eps = float(np.float32(1e-6))
+    FULL = fl.layer(window=0, use_rope=0, rms_eps=eps)
+    SLIDE = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps)
+    res = {}
+    # (1) config: 64 ragged requests
+    B = 64
+    lens = synth.uniform_ints(SEED, (3, 1), B, 1024, 131072).astype(np.int32)
+    maxlen = int(lens.max())
+    stride = -(-maxlen // PAGE)
+    q = torch.randn((B, HQ, D), device=dev, generator=torch.Generator(device=dev).manual_seed(3))
+    sinks = torch.randn(HQ, device=dev, generator=torch.Generator(device=dev).manual_seed(4))
+    out = torch.empty((B, HQ, D), device=dev)
+    sl = torch.from_numpy(lens).to(dev)
+    ragged = {"requests": B, "min_len": int(lens.min()), "max_len": maxlen,
+              "tokens": int(lens.sum())}
+    for kind, L in (("full", FULL), ("sliding", SLIDE)):
+        if kind == "full":
+            bt, nb = synth.shuffled_block_table(SEED, (3, 2), B, [-(-int(x) // PAGE) for x in lens],
+                                                stride)
+            kv_bytes = int(lens.sum()) * KV_BYTES_PER_TOKEN_LAYER
+        else:
+            bt, nb = synth.ring_block_table(SEED, (3, 2), B, stride, RING, stride)
+            kv_bytes = int(np.minimum(lens, WINDOW).sum()) * KV_BYTES_PER_TOKEN_LAYER
+        kc = synth.normal_bf16_bits_torch(SEED, (3, 3, kind == "full"), (nb, HKV, PAGE, D), dev)
+        vc = synth.normal_bf16_bits_torch(SEED, (3, 4, kind == "full"), (nb, HKV, D, PAGE), dev)
+        bt_d = torch.from_numpy(np.ascontiguousarray(bt)).to(dev)
+        ws = torch.zeros(max(fl.flint_attn_decode_workspace_size(L, B, maxlen), 256),
+                         dtype=torch.uint8, device=dev)
+        us = _time_launches(lambda: fl.flint_attn_decode(L, q, kc, vc, bt_d, sl, maxlen, sinks, out,
+                                                         workspace=ws))
+        assert torch.isfinite(out).all(), "non-finite output"
+        ragged[kind] = {"us": round(us, 1), "kv_bytes": kv_bytes,
+                        "gbps": round(kv_bytes / us / 1e3, 1),
+                        "frac": round(kv_bytes / us / 1e3 / HBM_PEAK_GBPS, 4),
+                        "plan": list(fl.flint_attn_decode_plan(L, B, maxlen))}
+        log(f"bench: 64 ragged requests, {kind} layer: {us:.1f} us, {kv_bytes / 1e9:.3f} GB, "
+            f"{kv_bytes / us / 1e3:.0f} GB/s")
+        del kc, vc
+    res["ragged_64"] = ragged
+    # (2) small batches at 100K context, fused step in a graph
+    ones = torch.ones(D, dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+    small = {}
+    pages = -(-CTX // PAGE)
+    t = CTX - 1
+    for Bs in (2, 4, 8, 16):
+        row = {}
+        for kind, L in (("full", FULL), ("sliding", SLIDE)):
+            nlay = 6 if kind == "full" else 20
+            lay = []
+            for l in range(nlay):
+                if kind == "full":
+                    bt, nb = synth.shuffled_block_table(SEED, (8, Bs, l), Bs, [pages] * Bs, pages)
+                else:
+                    bt, nb = synth.ring_block_table(SEED, (8, Bs, l), Bs, pages, RING, pages)
+                kc = synth.normal_bf16_bits_torch(SEED, (8, Bs, l, 1), (nb, HKV, PAGE, D), dev)
+                vc = synth.normal_bf16_bits_torch(SEED, (8, Bs, l, 2), (nb, HKV, D, PAGE), dev)
+                slots = np.array([int(bt[b, t // PAGE]) * PAGE + t % PAGE for b in range(Bs)],
+                                 np.int32)
+                lay.append((torch.from_numpy(np.ascontiguousarray(bt)).to(dev), kc, vc,
+                            torch.from_numpy(slots).to(dev)))
+            gen = torch.Generator(device=dev).manual_seed(5)
+            qi = torch.randn((Bs, HQ, D), device=dev, generator=gen)
+            ki = torch.randn((Bs, HKV, D), device=dev, generator=gen)
+            vi = torch.randn((Bs, HKV, D), device=dev, generator=gen)
+            sk = torch.randn(HQ, device=dev, generator=gen)
+            sl = torch.full((Bs,), CTX, dtype=torch.int32, device=dev)
+            o = torch.empty((Bs, HQ, D), device=dev)
+            ws = torch.zeros(max(fl.flint_attn_decode_workspace_size(L, Bs, CTX), 256),
+                             dtype=torch.uint8, device=dev)
+
+            def run_all():
+                for bt_d, kc, vc, slots in lay:
+                    fl.flint_attn_decode_step(L, qi, ki, vi, ones, ones, slots, kc, vc, bt_d, sl, CTX,
+                                              sk, o, workspace=ws)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(stream):
+                with torch.cuda.graph(g, stream=stream):
+                    run_all()
+            with torch.cuda.stream(stream):
+                us = _time_launches(g.replay, reps=20) / nlay
+            kv_bytes = Bs * (CTX if kind == "full" else WINDOW) * KV_BYTES_PER_TOKEN_LAYER
+            row[kind] = {"us_per_layer": round(us, 2), "gbps": round(kv_bytes / us / 1e3, 1),
+                         "plan": list(fl.flint_attn_decode_plan(L, Bs, CTX))}
+            del lay, g
+            torch.cuda.empty_cache()
+        small[f"B{Bs}"] = row
+        log(f"bench: B={Bs} at 100K: full layer {row['full']['us_per_layer']:.1f} us "
+            f"({row['full']['gbps']:.0f} GB/s), sliding layer {row['sliding']['us_per_layer']:.2f} us")
+    res["small_batches_100k"] = small
+    return {"workload": "batched decode: 64 ragged requests (1024..131072 tokens) on one full "
+                        "and one sliding layer; batches of 2..16 at 100K context (fused step)",
+            "unit": "us", "peak_gbps": HBM_PEAK_GBPS, **res}
 
 
 def copy_probe(dev):
