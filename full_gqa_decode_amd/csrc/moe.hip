@@ -17,7 +17,8 @@
 // 16-byte lane loads -- one 1 KiB contiguous load per instruction --, widens
 // bf16 to fp32 exactly (a shift) and accumulates fp32 FMAs against x; a
 // DPP/permlane reduction gives the dot product.  Three launches:
-//   K5a router logits (one single-wave workgroup per expert row, every token);
+//   K5a router logits (one workgroup per expert row, one wave per 512-element
+//       chunk of it, every token);
 //   K5b top-k -- recomputed by one wave of every workgroup from the token's
 //       logits, so no launch is spent on it -- then the gate and up rows and
 //       SwiGLU (each wave two FFN rows of one (slot, token));
@@ -67,40 +68,46 @@ __device__ __forceinline__ int wave_min_i32(int x) {
              min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
-// K5a: z[t][e] = <x_t, Wr_e> for every token; one single-wave workgroup per
-// expert row, so the 1 MB of router rows spreads over every CU.
-// CH = hidden / 512 (one 16-byte lane load per 512 elements of a row), a
-// template argument so that no register is held for
-// chunks a shape does not have.
-template <int CH>
-__global__ __launch_bounds__(64) void moe_router_kernel(MoeArgs a) {
+// K5a: z[t][e] = <x_t, Wr_e> for every token.  One workgroup per expert row
+// (the 1 MB of router rows spreads over every CU) and one wave per 512-element
+// chunk of it (hidden / 512 waves).  A wave requests its 1 KiB of the row and
+// the same chunk of every token's x at once -- unconditionally, with the token
+// index clamped, since a load under a branch is waited for at the join -- so
+// the launch costs one memory round trip; the chunks' partial dots meet in
+// LDS.  NT: token slots, 1, 2, 4 or 8 >= num_tokens.
+static_assert(kMoeMaxTokens == 8, "router token slots are 1, 2, 4 or 8");
+
+template <int NT>
+__global__ __launch_bounds__(kMoeMaxChunks * 64) void moe_router_kernel(MoeArgs a) {
   const int lane = threadIdx.x & 63;
+  const int c = threadIdx.x >> 6;
+  const int nch = blockDim.x >> 6;
   const int e = blockIdx.x;
   const int H = a.hidden;
-  const uint16_t* w = a.w_router + (int64_t)e * H + lane * 8;
-  u32x4 wv[CH];
+  __shared__ float sm_z[kMoeMaxChunks][NT];
+  const u32x4 wv =
+      __builtin_nontemporal_load((const u32x4*)(a.w_router + (int64_t)e * H + c * 512 + lane * 8));
+  f32x4 x0[NT], x1[NT];
 #pragma unroll
-  for (int c = 0; c < CH; ++c)
-    wv[c] = __builtin_nontemporal_load((const u32x4*)(w + c * 512));
-  // every token unrolled, so all of x is requested before any of it is used
-  float acc[kMoeMaxTokens];
-#pragma unroll
-  for (int t = 0; t < kMoeMaxTokens; ++t) {
-    acc[t] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (t < a.num_tokens) {
-        const float* xp = a.x + (int64_t)t * H + c * 512 + lane * 8;
-        acc[t] = dot8(wv[c], *(const f32x4*)xp, *(const f32x4*)(xp + 4), acc[t]);
-      }
-    }
+  for (int t = 0; t < NT; ++t) {
+    const int tt = min(t, a.num_tokens - 1);
+    const float* xp = a.x + (int64_t)tt * H + c * 512 + lane * 8;
+    x0[t] = *(const f32x4*)xp;
+    x1[t] = *(const f32x4*)(xp + 4);
   }
+  // every load above is in flight before the first dot product waits
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < kMoeMaxTokens; ++t) {
-    if (t < a.num_tokens) {
-      const float z = wave_sum_f32(acc[t]);
-      if (lane == 0) a.logits[(int64_t)t * a.num_experts + e] = z;
-    }
+  for (int t = 0; t < NT; ++t) {
+    const float z = wave_sum_f32(dot8(wv, x0[t], x1[t], 0.f));
+    if (lane == 0) sm_z[c][t] = z;
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < NT && t < a.num_tokens) {
+    float z = 0.f;
+    for (int i = 0; i < nch; ++i) z += sm_z[i][t];
+    a.logits[(int64_t)t * a.num_experts + e] = z;
   }
 }
 
@@ -118,7 +125,9 @@ __device__ __forceinline__ TopK select_topk(const MoeArgs& a, int t, int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    z[i] = e < E ? a.logits[(int64_t)t * E + e] : -INFINITY;
+    // unconditional (a clamped index), so the four loads are in flight at once
+    const float zl = a.logits[(int64_t)t * E + min(e, E - 1)];
+    z[i] = e < E ? zl : -INFINITY;
     if (z[i] != z[i]) z[i] = -INFINITY;  // a NaN logit ranks last
     zs[i] = z[i];
   }
@@ -238,56 +247,46 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) 
 
 // K5c: out[t][r] = sum_k w_k <Wd_{id_k}[r], h[t][k]> + sum_s <Wd_s[r], h[t][s]>.
 // One wave per (output row r, token t), every slot's row loaded up front.
+// NS = top_k + num_shared, a template argument so that the slot loop has no
+// branch: at a branch's join the compiler waits for the loads issued inside
+// it, which would cost one memory round trip per slot.
+template <int NS>
 __global__ __launch_bounds__(kMoeWaves * 64) void moe_down_kernel(MoeArgs a) {
+  static_assert(kMoeMaxInter == 512, "one 16-byte lane load per row");
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * kMoeWaves + (threadIdx.x >> 6);
   const int t = blockIdx.y;
   const int H = a.hidden, I = a.inter;
   if (r >= H) return;
-  const int nslots = a.top_k + a.num_shared;
-  constexpr int kSlots = kMoeMaxTopK + kMoeMaxShared;
-  constexpr int kIC = kMoeMaxInter / 512;
-  u32x4 wv[kSlots][kIC];
-  f32x4 h0[kSlots][kIC], h1[kSlots][kIC];
-  float wk[kSlots];
+  // the token's expert ids and weights in one vector load (lane k holds slot
+  // k's, the index clamped), so one wait precedes every row address
+  const int kl = t * a.top_k + min(lane, a.top_k - 1);
+  const int id_l = a.topk_ids[kl];
+  const float wt_l = a.topk_weights[kl];
+  u32x4 wv[NS];
+  f32x4 h0[NS], h1[NS];
+  float wk[NS];
 #pragma unroll
-  for (int k = 0; k < kSlots; ++k) {
-    if (k < nslots) {
-      const bool routed = k < a.top_k;
-      const int e = routed ? a.topk_ids[t * a.top_k + k] : a.num_experts + (k - a.top_k);
-      wk[k] = routed ? a.topk_weights[t * a.top_k + k] : 1.f;
-      const uint16_t* wd = a.w_down + ((int64_t)e * H + r) * I + lane * 8;
-      const float* hp = a.h + ((int64_t)t * nslots + k) * I + lane * 8;
-#pragma unroll
-      for (int c = 0; c < kIC; ++c) {
-        if (c * 512 < I) {
-          wv[k][c] = __builtin_nontemporal_load((const u32x4*)(wd + c * 512));
-          h0[k][c] = *(const f32x4*)(hp + c * 512);
-          h1[k][c] = *(const f32x4*)(hp + c * 512 + 4);
-        }
-      }
-    }
+  for (int k = 0; k < NS; ++k) {
+    const bool routed = k < a.top_k;
+    const int kr = min(k, kMoeMaxTopK - 1);
+    const int e = routed ? __builtin_amdgcn_readlane(id_l, kr) : a.num_experts + (k - a.top_k);
+    wk[k] = routed ? readlane_f32(wt_l, kr) : 1.f;
+    const uint16_t* wd = a.w_down + ((int64_t)e * H + r) * I + lane * 8;
+    const float* hp = a.h + ((int64_t)t * NS + k) * I + lane * 8;
+    wv[k] = __builtin_nontemporal_load((const u32x4*)wd);
+    h0[k] = *(const f32x4*)hp;
+    h1[k] = *(const f32x4*)(hp + 4);
   }
   float y = 0.f;
 #pragma unroll
-  for (int k = 0; k < kSlots; ++k) {
-    if (k < nslots) {
-      float d = 0.f;
-#pragma unroll
-      for (int c = 0; c < kIC; ++c)
-        if (c * 512 < I) d = dot8(wv[k][c], h0[k][c], h1[k][c], d);
-      y = fmaf(wk[k], wave_sum_f32(d), y);
-    }
-  }
+  for (int k = 0; k < NS; ++k) y = fmaf(wk[k], wave_sum_f32(dot8(wv[k], h0[k], h1[k], 0.f)), y);
   if (lane == 0) a.out[(int64_t)t * H + r] = y;
 }
 
 template <int CH>
 hipError_t launch_moe_ch(const MoeArgs& a, hipStream_t s) {
   const dim3 block(kMoeWaves * 64);
-  hipLaunchKernelGGL((moe_router_kernel<CH>), dim3(a.num_experts), dim3(64), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int rows_per_wg = kMoeWaves * kJW;
   const dim3 g2(a.inter / rows_per_wg, a.top_k + a.num_shared, a.num_tokens);
   hipLaunchKernelGGL((moe_gate_up_kernel<CH>), g2, block, 0, s, a);
@@ -299,7 +298,18 @@ hipError_t launch_moe_ch(const MoeArgs& a, hipStream_t s) {
 hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   const dim3 block(kMoeWaves * 64);
-  hipError_t e;
+  const dim3 rblock(a.hidden / 512 * 64);
+  const dim3 rgrid(a.num_experts);
+  if (a.num_tokens <= 1)
+    hipLaunchKernelGGL((moe_router_kernel<1>), rgrid, rblock, 0, s, a);
+  else if (a.num_tokens <= 2)
+    hipLaunchKernelGGL((moe_router_kernel<2>), rgrid, rblock, 0, s, a);
+  else if (a.num_tokens <= 4)
+    hipLaunchKernelGGL((moe_router_kernel<4>), rgrid, rblock, 0, s, a);
+  else
+    hipLaunchKernelGGL((moe_router_kernel<8>), rgrid, rblock, 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   switch (a.hidden / 512) {  // the API admits multiples of 512 up to kMoeMaxChunks * 512
     case 1: e = launch_moe_ch<1>(a, s); break;
     case 2: e = launch_moe_ch<2>(a, s); break;
@@ -311,8 +321,20 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
     default: e = launch_moe_ch<8>(a, s); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_down_kernel, dim3((a.hidden + kMoeWaves - 1) / kMoeWaves, a.num_tokens),
-                     block, 0, s, a);
+  const dim3 dgrid((a.hidden + kMoeWaves - 1) / kMoeWaves, a.num_tokens);
+  static_assert(kMoeMaxTopK + kMoeMaxShared == 10, "one case per slot count");
+  switch (a.top_k + a.num_shared) {  // the API admits 1..kMoeMaxTopK + kMoeMaxShared
+    case 1: hipLaunchKernelGGL((moe_down_kernel<1>), dgrid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((moe_down_kernel<2>), dgrid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((moe_down_kernel<3>), dgrid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((moe_down_kernel<4>), dgrid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((moe_down_kernel<5>), dgrid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((moe_down_kernel<6>), dgrid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((moe_down_kernel<7>), dgrid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((moe_down_kernel<8>), dgrid, block, 0, s, a); break;
+    case 9: hipLaunchKernelGGL((moe_down_kernel<9>), dgrid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((moe_down_kernel<10>), dgrid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
