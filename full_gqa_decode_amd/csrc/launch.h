@@ -107,8 +107,7 @@ constexpr int kSinglePages = 40;
 // 513-key window at batch 1 then takes 7 splits: 28 workgroups still spread
 // its 1 MB over enough CUs, and at 8 splits or fewer the merge runs the
 // one-pass small-merge kernel.  Measured per fused sliding step in a graph:
-// 8.4 us at 7 splits, 9.0 us at 17 (2 pages each), 9.4 at 4, 11.6 at one
-// (33 pages per workgroup, no merge launch: one CU's bandwidth bounds it).
+// 8.4 us at 7 splits, 9.0 us at 17 (2 pages each), 9.4 at 4.
 constexpr int kShortMinPages = 5;
 
 }  // namespace flint
