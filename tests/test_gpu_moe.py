@@ -38,12 +38,20 @@ class MoeCase:
     def host(self, t):
         return t.cpu().numpy().view(np.uint16)
 
-    def expected(self):
+    def topk_gap(self):
+        """Smallest distance, over the tokens, between the k-th and (k+1)-th
+        largest exact router logit (inf when every expert is selected)."""
+        if self.M.top_k >= self.M.experts:
+            return np.inf
         wr = self.host(self.wr)
         z = synth.bf16_bits_to_f32(wr).astype(np.float64) @ self.x.T.astype(np.float64)
         zs = -np.sort(-z, axis=0)
-        gap = (zs[self.M.top_k - 1] - zs[self.M.top_k]).min()
+        return float((zs[self.M.top_k - 1] - zs[self.M.top_k]).min())
+
+    def expected(self):
+        gap = self.topk_gap()
         assert gap > 1e-3, f"top-k boundary too close for a parity case ({gap:.2e})"
+        wr = self.host(self.wr)
         return oracle.moe_forward(self.M, self.x, wr, self.host(self.wgu), self.host(self.wd))
 
     def run_gpu(self):
@@ -84,6 +92,22 @@ def test_moe_other_hidden_sizes_and_expert_counts(T, shape):
     # hidden/512 = 3, 8, 7, 5 (the kernels are specialised on it), expert
     # counts that are not a multiple of the 64-lane selection width
     check(MoeCase(7, T, shape))
+
+
+@pytest.mark.parametrize("T,top_k,shared", [
+    (6, 1, 1), (1, 2, 1), (2, 5, 1), (3, 7, 2), (4, 8, 1), (8, 3, 0), (7, 6, 0), (5, 4, 2),
+])
+def test_moe_every_token_and_slot_count(T, top_k, shared):
+    # with the other tests, every token count 1..8 (the router's 1-, 2-, 4- and
+    # 8-token forms with clamped indices) and every slot count top_k + shared
+    # from 1 to 10 (one down-kernel form each) is run.  The first seed whose
+    # exact logits leave a clear top-k boundary is taken.
+    shape = dict(hidden=512, experts=24, top_k=top_k, inter=512, shared=shared)
+    for seed in range(100 + 10 * T + top_k, 140 + 10 * T + top_k):
+        case = MoeCase(seed, T, shape)
+        if case.topk_gap() > 1e-3:
+            break
+    check(case)
 
 
 def test_moe_without_shared_expert():
