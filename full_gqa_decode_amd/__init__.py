@@ -159,6 +159,26 @@ def _ptr(t, dtypes, name, cuda=True):
     return t.data_ptr()
 
 
+def _sizes(L, B=None, **tensors):
+    """Element counts the kernels assume, checked before any pointer crosses
+    the C ABI (which sees no sizes).  Each keyword is a tensor (or None) and
+    the count it must hold; block tables need at least B rows."""
+    for name, (t, n) in tensors.items():
+        if t is None:
+            continue
+        if name == "block_tables":
+            if t.dim() != 2 or (B is not None and t.shape[0] < B):
+                raise ValueError(f"block_tables must be 2-D with at least {B} rows, "
+                                 f"got shape {tuple(t.shape)}")
+            continue
+        if t.numel() != n:
+            raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+
+
+def _cache_elems(L, k_cache):
+    return k_cache.shape[0] * L.num_kv_heads * L.block_size * L.head_dim
+
+
 def _f32():
     return (_torch().float32,)
 
@@ -196,6 +216,11 @@ def flint_qk_norm_rope_append(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_n
     torch = _torch()
     T = k_in.shape[0]
     num_blocks = k_cache.shape[0]
+    Hq, Hkv, D = L.num_q_heads, L.num_kv_heads, L.head_dim
+    _sizes(L, q_in=(q_in, T * Hq * D), k_in=(k_in, T * Hkv * D), v_in=(v_in, T * Hkv * D),
+           q_norm_w=(q_norm_w, D), k_norm_w=(k_norm_w, D), positions=(positions, T),
+           slot_mapping=(slot_mapping, T), q_out=(q_out, T * Hq * D),
+           k_cache=(k_cache, _cache_elems(L, k_cache)), v_cache=(v_cache, _cache_elems(L, k_cache)))
     q_f32 = q_out if q_out is not None and q_out.dtype == torch.float32 else None
     q_b16 = q_out if q_out is not None and q_out.dtype != torch.float32 else None
     _check(lib().flint_qk_norm_rope_append(
@@ -231,6 +256,10 @@ def flint_attn_decode_partials(L: FlintAttnLayer, q, k_cache, v_cache, block_tab
     torch = _torch()
     B = q.shape[0]
     _, S = flint_attn_decode_plan(L, B, max_seq_len, pages_per_split)
+    Hq, D = L.num_q_heads, L.head_dim
+    _sizes(L, B, q=(q, B * Hq * D), k_cache=(k_cache, _cache_elems(L, k_cache)),
+           v_cache=(v_cache, _cache_elems(L, k_cache)), block_tables=(block_tables, 0),
+           seq_lens=(seq_lens, B), part_o=(part_o, B * S * Hq * D), part_lse=(part_lse, B * S * Hq))
     if part_o is None:
         part_o = torch.empty((B, S, L.num_q_heads, 128), dtype=torch.float32, device=q.device)
     if part_lse is None:
@@ -248,6 +277,9 @@ def flint_attn_merge(L: FlintAttnLayer, part_o, part_lse, sinks, out=None, strea
     """K3 alone: fold the partials [B,S,Hq,...] and the sinks into out [B,Hq,128]."""
     torch = _torch()
     B, S = part_lse.shape[0], part_lse.shape[1]
+    Hq, D = L.num_q_heads, L.head_dim
+    _sizes(L, part_o=(part_o, B * S * Hq * D), part_lse=(part_lse, B * S * Hq),
+           sinks=(sinks, Hq), out=(out, B * Hq * D))
     if out is None:
         out = torch.empty((B, L.num_q_heads, 128), dtype=torch.float32, device=part_o.device)
     _check(lib().flint_attn_merge(C.byref(L), B, S, _ptr(part_o, _f32(), "part_o"),
@@ -266,6 +298,10 @@ def flint_attn_decode(L: FlintAttnLayer, q, k_cache, v_cache, block_tables, seq_
     torch = _torch()
     B = q.shape[0]
     need = flint_attn_decode_workspace_size(L, B, max_seq_len, pages_per_split)
+    Hq, D = L.num_q_heads, L.head_dim
+    _sizes(L, B, q=(q, B * Hq * D), k_cache=(k_cache, _cache_elems(L, k_cache)),
+           v_cache=(v_cache, _cache_elems(L, k_cache)), block_tables=(block_tables, 0),
+           seq_lens=(seq_lens, B), sinks=(sinks, Hq), out=(out, B * Hq * D))
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -289,6 +325,12 @@ def flint_attn_decode_step(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_norm
     torch = _torch()
     B = q_in.shape[0]
     need = flint_attn_decode_workspace_size(L, B, max_seq_len, pages_per_split)
+    Hq, Hkv, D = L.num_q_heads, L.num_kv_heads, L.head_dim
+    _sizes(L, B, q_in=(q_in, B * Hq * D), k_in=(k_in, B * Hkv * D), v_in=(v_in, B * Hkv * D),
+           q_norm_w=(q_norm_w, D), k_norm_w=(k_norm_w, D), slot_mapping=(slot_mapping, B),
+           q_out=(q_out, B * Hq * D), k_cache=(k_cache, _cache_elems(L, k_cache)),
+           v_cache=(v_cache, _cache_elems(L, k_cache)), block_tables=(block_tables, 0),
+           seq_lens=(seq_lens, B), sinks=(sinks, Hq), out=(out, B * Hq * D))
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q_in.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -318,6 +360,10 @@ def flint_attn_prefill(L: FlintAttnLayer, q, cu_q_lens, max_q_len: int, k_cache,
     out fp32 [total_q, Hq, 128]."""
     torch = _torch()
     B = cu_q_lens.shape[0] - 1
+    Hq, D = L.num_q_heads, L.head_dim
+    _sizes(L, B, q=(q, q.shape[0] * Hq * D), out=(out, q.shape[0] * Hq * D),
+           k_cache=(k_cache, _cache_elems(L, k_cache)), v_cache=(v_cache, _cache_elems(L, k_cache)),
+           block_tables=(block_tables, 0), seq_lens=(seq_lens, B), sinks=(sinks, Hq))
     need = flint_attn_prefill_workspace_size(L, B, max_q_len, max_seq_len)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -344,6 +390,10 @@ def flint_moe_forward(M: FlintMoeLayer, x, w_router, w_gate_up, w_down, out=None
     torch = _torch()
     T = x.shape[0]
     dev = x.device
+    H, E, I, S, K = M.hidden, M.num_experts, M.inter, M.num_shared, M.top_k
+    _sizes(M, x=(x, T * H), w_router=(w_router, E * H), w_gate_up=(w_gate_up, (E + S) * 2 * I * H),
+           w_down=(w_down, (E + S) * H * I), out=(out, T * H), topk_ids=(topk_ids, T * K),
+           topk_weights=(topk_weights, T * K))
     if out is None:
         out = torch.empty((T, M.hidden), dtype=torch.float32, device=dev)
     if topk_ids is None:

@@ -261,3 +261,50 @@ def test_moe_zero_tokens_is_a_no_op_and_workspace_grows_with_tokens():
     # logits and the SwiGLU activations, fp32, each part 256-byte aligned
     assert w1 == 1024 + 7 * 512 * 4
     assert w8 == 8 * 256 * 4 + 8 * 7 * 512 * 4
+
+
+def _z(*shape, dtype="float32"):
+    import torch
+    return torch.zeros(shape, dtype=getattr(torch, dtype))
+
+
+def test_python_binding_checks_tensor_sizes_before_the_abi():
+    # The C ABI sees only pointers; the binding checks every tensor's element
+    # count against the layer and the batch first (host tensors reach no
+    # kernel: a size error is raised before the device checks).
+    L = fl.layer(window=0)
+    B, nb = 2, 3
+    kc, vc = _z(nb, 4, 16, 128, dtype="int16"), _z(nb, 4, 128, 16, dtype="int16")
+    bt, sl = _z(B, 8, dtype="int32"), _z(B, dtype="int32")
+    q, out, sinks = _z(B, 32, 128), _z(B, 32, 128), _z(32)
+    bad = [
+        dict(q=_z(B, 32, 127)),
+        dict(out=_z(B, 31, 128)),
+        dict(sinks=_z(31)),
+        dict(seq_lens=_z(B + 1, dtype="int32")),
+        dict(v_cache=_z(nb - 1, 4, 128, 16, dtype="int16")),
+        dict(block_tables=_z(B - 1, 8, dtype="int32")),
+    ]
+    for kw in bad:
+        args = dict(q=q, k_cache=kc, v_cache=vc, block_tables=bt, seq_lens=sl, sinks=sinks,
+                    out=out)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            fl.flint_attn_decode(L, args["q"], args["k_cache"], args["v_cache"],
+                                 args["block_tables"], args["seq_lens"], 100, args["sinks"],
+                                 args["out"])
+    with pytest.raises(ValueError, match="k_in"):
+        fl.flint_attn_decode_step(L, q, _z(B, 4, 64), _z(B, 4, 128), _z(128), _z(128),
+                                  _z(B, dtype="int32"), kc, vc, bt, sl, 100, sinks, out)
+    with pytest.raises(ValueError, match="positions"):
+        fl.flint_qk_norm_rope_append(L, q, _z(B, 4, 128), _z(B, 4, 128), _z(128), _z(128),
+                                     _z(B + 1, dtype="int32"), _z(B, dtype="int32"), q, kc, vc)
+    with pytest.raises(ValueError, match="out"):
+        fl.flint_attn_prefill(L, _z(5, 32, 128, dtype="int16"), _z(B + 1, dtype="int32"), 5,
+                              kc, vc, bt, sl, 100, sinks, _z(4, 32, 128))
+    with pytest.raises(ValueError, match="sinks"):
+        fl.flint_attn_merge(L, _z(B, 3, 32, 128), _z(B, 3, 32), _z(8), out)
+    M = fl.moe_layer(512, 16, 2, 512, 1)
+    with pytest.raises(ValueError, match="w_down"):
+        fl.flint_moe_forward(M, _z(1, 512), _z(16, 512, dtype="int16"),
+                             _z(17, 2, 512, 512, dtype="int16"), _z(16, 512, 512, dtype="int16"))
