@@ -282,12 +282,18 @@ __device__ __forceinline__ void substitute_new_token(PageRaw8& r, const uint8_t*
 // speculative page id is read inside the caller's block-table row and
 // validated before it addresses the cache.
 constexpr int kAhead8 = 2;
+// MI355X's compute units: a grid of at most this many workgroups runs as one
+// round at one workgroup per CU.
+constexpr int kComputeUnits = 256;
 
-// Launch bounds: the second figure is the least waves per SIMD.  fp8 split
-// kernels are held to 4 (128 VGPRs) so that two workgroups share a CU.
-template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED, bool KV8>
-__global__ __launch_bounds__(WAVES * 64, MAXP > 1 ? 1 : (KV8 ? 4 : 2)) void decode_split_kernel(
-    DecodeArgs a) {
+// Launch bounds: MINW, the least waves per SIMD.  fp8 split kernels are held
+// to 4 (128 VGPRs) by default so that two workgroups share a CU; a fused fp8
+// launch of at most one workgroup per CU takes MINW = 2 instead, which keeps
+// its fp64 prologue out of scratch (measured: the batch-1 fp8 step 687-693
+// -> 669-670 us).
+template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED, bool KV8,
+          int MINW = (MAXP > 1 ? 1 : (KV8 ? 4 : 2))>
+__global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeArgs a) {
   constexpr int kThreads = WAVES * 64;
   // page buffers per wave
   constexpr int NR = MAXP > 1 ? MAXP : (KV8 ? kAhead8 : 1);
@@ -866,21 +872,40 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   constexpr int W = kDecodeWaves;
+  // fused fp8 with at most one workgroup per CU: the looser register bound
+  constexpr int MW = (FUSED && KV8) ? 2 : (KV8 ? 4 : 2);
+  const bool loose = FUSED && KV8 && (int64_t)grid.x * grid.y * grid.z <= kComputeUnits;
   if (a.num_splits == 1) {  // one long split: pipelined loop, sink folded in
-    if (win)
+    if (loose) {
+      if (win)
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8, MW>), grid,
+                           dim3(W * 64), 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED, KV8, MW>), grid,
+                           dim3(W * 64), 0, st, a);
+    } else if (win) {
       hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8>), grid, dim3(W * 64), 0,
                          st, a);
-    else
+    } else {
       hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED, KV8>), grid, dim3(W * 64),
                          0, st, a);
+    }
     return hipGetLastError();
   }
-  if (win)
+  if (loose) {
+    if (win)
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8, MW>), grid,
+                         dim3(W * 64), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED, KV8, MW>), grid,
+                         dim3(W * 64), 0, st, a);
+  } else if (win) {
     hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8>), grid, dim3(W * 64), 0,
                        st, a);
-  else
+  } else {
     hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED, KV8>), grid, dim3(W * 64), 0,
                        st, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_merge_k(a, st);
