@@ -50,6 +50,11 @@ CASES = [
     (513, True, [1, 512, 513, 514, 2000], 0),
     (513, True, [32768], 0),
     (513, False, [2000, 33], 3),
+    # grids of more than 256 workgroups: the fused fp8 kernels at their
+    # two-workgroups-per-CU register bound (windowed multi-split; one long
+    # pipelined split per request)
+    (513, True, [600, 700, 800, 513, 514, 1000, 1200, 2000, 3000, 900], 0),
+    (0, False, [700 + 3 * i for i in range(65)], 60),
 ]
 
 
