@@ -507,8 +507,8 @@ def bench_batches(fl, dev):
     (seeded), pages in one random physical order, one full and one sliding
     layer, flint_attn_decode (K2 + K3) on a normalised q; algorithmic bytes
     from the drawn lengths.  (2) B = 2, 4, 8, 16 requests at 100K context,
-    one fused step of a full and of a sliding layer each, in a graph of 6
-    (full) or 20 (sliding) distinct layers so that no layer's pages stay in
+    one fused step of a full layer (bf16 and fp8 cache) and of a sliding
+    layer each, in a graph of 6 (full) or 20 (sliding) distinct layers so that no layer's pages stay in
     the caches between replays."""
     import torch
     eps = float(np.float32(1e-6))
@@ -556,12 +556,23 @@ def bench_batches(fl, dev):
     small = {}
     pages = -(-CTX // PAGE)
     t = CTX - 1
+    FULL8 = fl.layer(window=0, use_rope=0, rms_eps=eps, kv_dtype=fl.FLINT_KV_FP8_E4M3,
+                     k_scale=FP8_SCALES[0], v_scale=FP8_SCALES[1])
     for Bs in (2, 4, 8, 16):
         row = {}
-        for kind, L in (("full", FULL), ("sliding", SLIDE)):
-            nlay = 6 if kind == "full" else 20
+        for kind, L in (("full", FULL), ("sliding", SLIDE), ("full_fp8", FULL8)):
+            nlay = 20 if kind == "sliding" else 6
             lay = []
             for l in range(nlay):
+                if kind == "full_fp8":
+                    bt, nb = synth.shuffled_block_table(SEED, (9, Bs, l), Bs, [pages] * Bs, pages)
+                    kc = synth.fp8_codes_torch(SEED, (9, Bs, l, 1), (nb, HKV, PAGE, D), dev)
+                    vc = synth.fp8_codes_torch(SEED, (9, Bs, l, 2), (nb, HKV, D, PAGE), dev)
+                    slots = np.array([int(bt[b, t // PAGE]) * PAGE + t % PAGE for b in range(Bs)],
+                                     np.int32)
+                    lay.append((torch.from_numpy(np.ascontiguousarray(bt)).to(dev), kc, vc,
+                                torch.from_numpy(slots).to(dev)))
+                    continue
                 if kind == "full":
                     bt, nb = synth.shuffled_block_table(SEED, (8, Bs, l), Bs, [pages] * Bs, pages)
                 else:
@@ -592,17 +603,22 @@ def bench_batches(fl, dev):
                     run_all()
             with torch.cuda.stream(stream):
                 us = _time_launches(g.replay, reps=20) / nlay
-            kv_bytes = Bs * (CTX if kind == "full" else WINDOW) * KV_BYTES_PER_TOKEN_LAYER
+            kv_bytes = Bs * (WINDOW if kind == "sliding" else CTX) * KV_BYTES_PER_TOKEN_LAYER
+            if kind == "full_fp8":
+                kv_bytes //= 2
             row[kind] = {"us_per_layer": round(us, 2), "gbps": round(kv_bytes / us / 1e3, 1),
                          "plan": list(fl.flint_attn_decode_plan(L, Bs, CTX))}
             del lay, g
             torch.cuda.empty_cache()
         small[f"B{Bs}"] = row
         log(f"bench: B={Bs} at 100K: full layer {row['full']['us_per_layer']:.1f} us "
-            f"({row['full']['gbps']:.0f} GB/s), sliding layer {row['sliding']['us_per_layer']:.2f} us")
+            f"({row['full']['gbps']:.0f} GB/s), sliding layer {row['sliding']['us_per_layer']:.2f} us, "
+            f"fp8 full layer {row['full_fp8']['us_per_layer']:.1f} us "
+            f"({row['full_fp8']['gbps']:.0f} GB/s)")
     res["small_batches_100k"] = small
     return {"workload": "batched decode: 64 ragged requests (1024..131072 tokens) on one full "
-                        "and one sliding layer; batches of 2..16 at 100K context (fused step)",
+                        "and one sliding layer; batches of 2..16 at 100K context (fused step; "
+                        "full layers over a bf16 and an fp8 cache, sliding over bf16)",
             "unit": "us", "peak_gbps": HBM_PEAK_GBPS, **res}
 
 
