@@ -16,8 +16,9 @@
  *       small-batch MoE and dense GEMV kernels on the optimised decode path.
  * Readings where the pages are silent (each restated at its use):
  *   - router logits z_e = <x, w_e>, no bias; score s_e = 1 / (1 + e^{-z_e});
- *   - the top_k experts by score (the order of z), ties to the lower index,
- *     the comparison taken on z rounded to fp32 (the kernels' precision);
+ *   - the top_k experts by score, i.e. in the order of the exact (fp64) z,
+ *     ties to the lower index (the definition; a kernel that ranks rounded
+ *     logits agrees wherever the top-k boundary is not within its rounding);
  *   - routing weights s_sel / sum(s_sel) over the selected experts;
  *   - every expert, routed or shared, is a SwiGLU FFN of width `inter`:
  *     E(x) = W_down (silu(W_gate x) * (W_up x)), silu(g) = g / (1 + e^{-g});
@@ -43,22 +44,20 @@ int orc_moe_route(const orc_moe* M, const float* x, const uint16_t* w_router, in
                   double* weights) {
   if (M->top_k < 1 || M->top_k > M->experts) return -1;
   double* z = (double*)malloc(sizeof(double) * (size_t)M->experts);
-  float* z32 = (float*)malloc(sizeof(float) * (size_t)M->experts);
   char* taken = (char*)calloc((size_t)M->experts, 1);
   for (int e = 0; e < M->experts; ++e) {
     const uint16_t* w = w_router + (int64_t)e * M->hidden;
     double acc = 0.0;
     for (int i = 0; i < M->hidden; ++i) acc += (double)x[i] * bfv(w[i]);
     z[e] = acc;
-    z32[e] = (float)acc;
   }
-  /* top_k by repeated selection of the largest remaining logit; a strict
-   * comparison keeps the lower index on ties */
+  /* top_k by repeated selection of the largest remaining fp64 logit; a
+   * strict comparison keeps the lower index on ties */
   double ssum = 0.0;
   for (int k = 0; k < M->top_k; ++k) {
     int best = -1;
     for (int e = 0; e < M->experts; ++e)
-      if (!taken[e] && (best < 0 || z32[e] > z32[best])) best = e;
+      if (!taken[e] && (best < 0 || z[e] > z[best])) best = e;
     taken[best] = 1;
     ids[k] = best;
     weights[k] = 1.0 / (1.0 + exp(-z[best]));
@@ -66,7 +65,6 @@ int orc_moe_route(const orc_moe* M, const float* x, const uint16_t* w_router, in
   }
   for (int k = 0; k < M->top_k; ++k) weights[k] /= ssum;
   free(z);
-  free(z32);
   free(taken);
   return 0;
 }

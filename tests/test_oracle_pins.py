@@ -744,16 +744,33 @@ def test_moe_route_ties_go_to_the_lower_index():
     assert abs(w.sum() - 1.0) < 1e-15 and w[0] == w[1] and w[2] == w[5]
 
 
+def test_moe_route_ranks_the_exact_logits_not_their_fp32_rounding():
+    # experts 3 and 11 have logits 0.5 and 0.5 + 2^-30, equal once rounded to
+    # fp32: the definition (the exact logit) picks 11 first, a rounded
+    # comparison would pick 3 by the lower-index rule
+    M = oracle.moe(hidden=64, experts=16, top_k=2, inter=8, shared=1)
+    wr = np.zeros((16, 64), np.uint16)
+    wr[:, 0] = _bf16_exact(np.full(16, 0.25))[0]
+    wr[[3, 11], 0] = _bf16_exact([0.5, 0.5])[0]
+    wr[11, 1] = _bf16_exact([2.0 ** -10])[0][0]
+    x = np.zeros(64, np.float32)
+    x[0] = 1.0
+    x[1] = np.float32(2.0 ** -20)
+    assert np.float32(0.5 + 2.0 ** -30) == np.float32(0.5)
+    ids, _ = oracle.moe_route(M, x, wr)
+    assert ids.tolist() == [11, 3]
+
+
 def test_moe_route_matches_a_sort_of_the_logits():
     # random router: the selection is the stable descending order of the
-    # fp32-rounded logits, computed here by numpy's matmul and argsort
+    # exact (fp64) logits, computed here by numpy's matmul and argsort
     M = oracle.moe()
     wr = synth.normal_bf16_bits(51, (1,), (256, 2048))
     for t in range(4):
         x = synth.normal(51, (2, t), 2048) * np.float32(0.03)
         ids, w = oracle.moe_route(M, x, wr)
         z = synth.bf16_bits_to_f32(wr).astype(np.float64) @ x.astype(np.float64)
-        top = np.argsort(-z.astype(np.float32), kind="stable")[:6]
+        top = np.argsort(-z, kind="stable")[:6]
         assert ids.tolist() == top.tolist()
         s = 1.0 / (1.0 + np.exp(-z[top]))
         assert np.allclose(w, s / s.sum(), rtol=1e-12, atol=0)
