@@ -40,6 +40,7 @@ HQ, HKV, D, PAGE = 32, 4, 128, 16
 HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_TFLOPS = 2500.0
 SEED = 0
+PARITY_TOL = 4e-3   # max |GPU - oracle| of the fp32 outputs over the step
 KV_BYTES_PER_TOKEN_LAYER = 2 * HKV * D * 2   # K and V rows of one token, one layer
 COPY_PROBE_BYTES = 256 << 20
 
@@ -313,7 +314,11 @@ def main():
                                "shuffled), HIP graph",
                    "global_batch": 1, "seq_len": CTX, "layers": LAYERS,
                    "full_layers": len(FULL_LAYERS), "window": WINDOW, "parallelism": "none"},
+        # step-level rate over the algorithmic K/V bytes (not a counter
+        # reading; the counter-based figure of the dominant kernel is
+        # roofline.traffic)
         "hbm_gbps": round(gbps_step, 1),
+        "hbm_gbps_kind": "analytic: algorithmic K/V bytes of the step / step time",
         "hbm_frac_of_peak": round(gbps_step / HBM_PEAK_GBPS, 4),
         "kv_bytes_per_step": kv_step,
         "us_per_step_median": round(statistics.median(per), 2),
@@ -351,6 +356,10 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity_max_abs_err"] = cpu_baseline(layers, eps)
     print(json.dumps(result), flush=True)
+    err = result.get("parity_max_abs_err")
+    if err is not None and not err <= PARITY_TOL:
+        log(f"bench: FAILED parity: max|gpu-oracle| {err:.3e} above {PARITY_TOL}")
+        sys.exit(1)
 
 
 FP8_SCALES = (1.0 / 16, 0.5)

@@ -105,7 +105,7 @@ SIGNATURES = [
     ("flint_attn_merge", C.c_int, [_LP, _I, _I, _P, _P, _P, _P, _P]),
     ("flint_attn_prefill_workspace_size", _SZ, [_LP, _I, _I, _I]),
     ("flint_attn_prefill", C.c_int,
-     [_LP, _I, _P, _P, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
+     [_LP, _I, _P, _P, _I, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _P]),
     ("flint_moe_workspace_size", _SZ, [_MP, _I]),
     ("flint_moe_forward", C.c_int, [_MP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("flint_status_string", C.c_char_p, [C.c_int]),
@@ -369,7 +369,8 @@ def flint_attn_prefill(L: FlintAttnLayer, q, cu_q_lens, max_q_len: int, k_cache,
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().flint_attn_prefill(
-        C.byref(L), B, _ptr(q, _b16(), "q"), _ptr(cu_q_lens, _i32(), "cu_q_lens"), max_q_len,
+        C.byref(L), B, _ptr(q, _b16(), "q"), _ptr(cu_q_lens, _i32(), "cu_q_lens"), q.shape[0],
+        max_q_len,
         _ptr(k_cache, _kv(L), "k_cache"), _ptr(v_cache, _kv(L), "v_cache"), k_cache.shape[0],
         _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
         _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),

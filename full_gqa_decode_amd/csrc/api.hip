@@ -369,6 +369,10 @@ flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
   const size_t qbytes = (size_t)num_seqs * L->num_q_heads * 128 * sizeof(float);
   if (overlap(q_in, qbytes, out, qbytes) || (q_out && overlap(q_out, qbytes, out, qbytes)))
     return fail(FLINT_ERR_INVALID_ARGUMENT, "out must not alias q_in or q_out");
+  // every split workgroup reads the raw q_in while split 0 writes q_out, so a
+  // shared buffer would let later splits normalise an already normalised q
+  if (q_out && overlap(q_out, qbytes, q_in, qbytes))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "q_out must not alias q_in in the fused step");
   a.q_in = q_in;
   a.k_in = k_in;
   a.v_in = v_in;
@@ -475,7 +479,7 @@ size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_
 }
 
 flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* q,
-                                const int32_t* cu_q_lens, int32_t max_q_len,
+                                const int32_t* cu_q_lens, int32_t total_q, int32_t max_q_len,
                                 const void* k_cache, const void* v_cache,
                                 int32_t num_blocks, const int32_t* block_tables,
                                 int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
@@ -491,7 +495,8 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
                 kMaxContext);
   if (max_q_len < 0 || max_q_len > max_seq_len)
     return fail(FLINT_ERR_INVALID_ARGUMENT, "max_q_len %d outside [0, max_seq_len]", max_q_len);
-  if (num_seqs == 0 || max_q_len == 0) return ok();
+  if (total_q < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "total_q %d < 0", total_q);
+  if (num_seqs == 0 || max_q_len == 0 || total_q == 0) return ok();
   if (!q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !seq_lens || !sinks || !out)
     return fail(FLINT_ERR_INVALID_ARGUMENT, "a required pointer is NULL");
   if (num_blocks < 1) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_blocks %d < 1", num_blocks);
@@ -505,6 +510,7 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
   flint::PrefillArgs a;
   a.q = q;
   a.cu_q_lens = cu_q_lens;
+  a.total_q = total_q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.block_tables = block_tables;

@@ -75,6 +75,7 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s);
 struct PrefillArgs {
   const uint16_t* q;         // [total_q][Hq][128] bf16
   const int32_t* cu_q_lens;  // [B+1]
+  int32_t total_q;           // rows of q and out
   const void* k_cache;       // bf16 bits, or fp8 codes in the fp8 tile order (kv_fp8)
   const void* v_cache;
   const int32_t* block_tables;

@@ -137,6 +137,9 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int seq_len = a.seq_lens[b];
   const int wg_row0 = tile * kRows;
   if (q_len <= 0 || wg_row0 >= q_len) return;  // no rows in this workgroup
+  // rows outside q / out: a request whose cu_q_lens range leaves
+  // [0, total_q) is not touched at all (no row of it can be located safely)
+  if (q0 < 0 || (int64_t)q0 + q_len > a.total_q) return;
   const bool req_bad = q_len > a.max_q_len || seq_len > a.max_seq_len || q_len > seq_len;
   const int base = seq_len - q_len;  // position of row 0
 

@@ -51,6 +51,10 @@
  *   K load reads one 32-dim block of all 16 rows (1 KiB contiguous), and V
  *   is dim-major because the P.V contraction runs over tokens, so both
  *   operands load straight from HBM with full coalescing.
+ *   A conventional row-major paged cache ([page][head][16][128] K and V rows)
+ *   is NOT accepted by any call: the cache must be written by
+ *   flint_qk_norm_rope_append or flint_attn_decode_step, which place every
+ *   element in the tile order above.
  *
  * KV element formats (flint_attn_layer.kv_dtype)
  *   FLINT_KV_BF16: 2-byte bf16 elements (uint16 bit patterns), 4 KiB tiles.
@@ -81,7 +85,7 @@
 extern "C" {
 #endif
 
-#define FLINT_ABI_VERSION 2
+#define FLINT_ABI_VERSION 3
 
 typedef enum {
   FLINT_OK = 0,
@@ -141,7 +145,12 @@ flint_status flint_qk_norm_rope_append(const flint_attn_layer* L, int32_t num_to
 
 /*
  * Decode attention: one new query per request over its paged KV (bf16 or
- * fp8; for fp8, K_j and V_j below are the scaled code values).
+ * fp8; for fp8, K_j and V_j below are the scaled code values).  Sources:
+ * "Day-0 Support for Flint on vLLM" (hnkhoi.com), "Model architecture": GQA
+ * of 32 query over 4 KV heads, learned attention sinks, RoPE sliding layers
+ * and NoPE full layers; (newruntime.com), "What happened": a 513-token window
+ * on 35 layers, the full context on 14, and the batch-1 decode at a
+ * 100,000-token context this call serves.
  * Request b's query sits at position t = seq_lens[b] - 1 (seq_lens counts the
  * new token, which must already be appended) and attends to keys lo..t,
  * lo = 0 (window 0) or max(0, t - window + 1).  For query head h of KV group
@@ -196,7 +205,10 @@ flint_status flint_attn_decode_ex(const flint_attn_layer* L, int32_t num_seqs, c
  *   slot_mapping [B]: must equal the slot the page table gives position
  *     seq_lens[b]-1 (page * 16 + row); otherwise nothing is written and that
  *     request's output is NaN
- *   q_out: optional [B][num_q_heads][128] fp32 normalised (rotated) q, or NULL
+ *   q_out: optional [B][num_q_heads][128] fp32 normalised (rotated) q, or NULL;
+ *     unlike the stand-alone append it must not overlap q_in (every split
+ *     workgroup reads the raw q_in while one of them writes q_out), else
+ *     FLINT_ERR_INVALID_ARGUMENT
  *   pages_per_split: as for flint_attn_decode_ex (0 = the library's choice);
  *     size the workspace with flint_attn_decode_workspace_size_ex.
  */
@@ -260,22 +272,28 @@ flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32
 
 /*
  * Causal (optionally windowed) prefill attention over the paged cache, on
- * the matrix cores.  Request b owns query rows cu_q_lens[b] ..
+ * the matrix cores ("Day-0 Support for Flint on vLLM", newruntime.com, "What
+ * happened": the 8,192-token prefill of the optimised path; hnkhoi.com,
+ * "Model architecture": the same sink, window and GQA rules as decode).
+ * Request b owns query rows cu_q_lens[b] ..
  * cu_q_lens[b+1]-1 (cu_q_lens [B+1] int32 on device, cu_q_lens[0] = 0); row
  * i of it sits at position seq_lens[b] - q_len_b + i and attends to keys
  * lo..that position, whose K/V must already be appended.
  *   q   [total_q][num_q_heads][128] bf16 (normalised, rotated)
+ *   total_q    rows of q and of out (host side; 0 is a no-op)
  *   max_q_len  host-side bound of every q_len; max_seq_len as for decode
  *   out [total_q][num_q_heads][128] fp32
  * Same per-row result as decode; the sink joins every row's denominator.
  * Rows of a request with q_len > seq_len or seq_len > max_seq_len, or whose
- * pages include an id outside [0, num_blocks), are set to NaN.
+ * pages include an id outside [0, num_blocks), are set to NaN.  A request
+ * whose rows cu_q_lens[b] .. cu_q_lens[b+1]-1 do not lie inside
+ * [0, total_q) is skipped: none of q or out is touched for it.
  * An fp8 cache is widened to bf16 (exactly) as its pages are staged.
  */
 size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_seq_len);
 flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* q,
-                                const int32_t* cu_q_lens, int32_t max_q_len,
+                                const int32_t* cu_q_lens, int32_t total_q, int32_t max_q_len,
                                 const void* k_cache, const void* v_cache,
                                 int32_t num_blocks, const int32_t* block_tables,
                                 int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
@@ -288,8 +306,10 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
  * hnkhoi.com, "Model architecture": hidden size 2048, 256 experts, sigmoid
  * top-6, a shared expert; newruntime.com, "What happened": small-batch MoE and
  * dense GEMV kernels).  Readings where the pages are silent: router logits
- * z_e = <x, w_router[e]> with no bias; the top_k experts by z (fp32), ties to
- * the lower index; weights sigmoid(z_id) normalised over the selection; each
+ * z_e = <x, w_router[e]> with no bias; the top_k experts by z, ties to the
+ * lower index (the kernels rank their fp32 logits: the same experts as the
+ * exact ranking unless two logits at the top-k boundary lie within fp32
+ * rounding of each other); weights sigmoid(z_id) normalised over the selection; each
  * expert E(x) = W_down (silu(W_gate x) * (W_up x)) with silu(g) = g/(1+e^-g);
  * shared experts join with weight 1:
  *   out[t] = sum_k weight[t][k] E_{id[t][k]}(x[t]) + sum_s E_{experts+s}(x[t])

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = fl.lib()
-    assert lib.flint_abi_version() == 2
+    assert lib.flint_abi_version() == 3
     # 12 four-byte fields, in the header's order
     assert C.sizeof(fl.FlintAttnLayer) == 48
     assert [f[0] for f in fl.FlintAttnLayer._fields_][-3:] == ["kv_dtype", "k_scale", "v_scale"]
@@ -117,9 +117,25 @@ def test_fp8_layer_needs_positive_finite_scales(k_scale, v_scale):
 def test_prefill_checks_fp8_scales():
     lib = fl.lib()
     L = fl.full_layer(kv_dtype=fl.FLINT_KV_FP8_E4M3, k_scale=0.0, v_scale=2.0)
-    args = [C.byref(L), 1, P, P + 0x10000, 32, Q, Q + 0x10000, 4, P + 0x20000, 4, P + 0x30000,
-            64, P + 0x40000, P + 0x50000, None, 0, None]
+    args = [C.byref(L), 1, P, P + 0x10000, 32, 32, Q, Q + 0x10000, 4, P + 0x20000, 4,
+            P + 0x30000, 64, P + 0x40000, P + 0x50000, None, 0, None]
     assert lib.flint_attn_prefill(*args) == INVALID
+
+
+def test_fused_step_rejects_q_out_aliasing_q_in():
+    # every split workgroup of the fused step reads the raw q_in while one of
+    # them writes q_out: a shared buffer must be refused before any launch
+    lib = fl.lib()
+    L = fl.full_layer()
+    qi, qo = P + 0x80000, P + 0x90000
+    args = [C.byref(L), 1, qi, P + 0x10000, P + 0x20000, P + 0x30000, P + 0x40000, P + 0x50000,
+            qo, Q, Q + 0x10000, 4, P + 0x60000, 4, P + 0x70000, 64, P + 0xA0000, P + 0xB0000,
+            WS, 1 << 20, 0, None]
+    for alias in (qi, qi + 256):
+        bad = list(args)
+        bad[8] = alias
+        assert lib.flint_attn_decode_step(*bad) == INVALID
+        assert "q_out" in lib.flint_last_error().decode()
 
 
 def test_zero_requests_is_a_no_op():
@@ -154,12 +170,18 @@ def test_append_rejects_bad_arguments():
 def test_prefill_rejects_bad_arguments():
     lib = fl.lib()
     L = fl.full_layer()
-    base = [C.byref(L), 1, P, P + 0x10000, 32, Q, Q + 0x10000, 4, P + 0x20000, 4, P + 0x30000, 64,
-            P + 0x40000, P + 0x50000, None, 0, None]
-    for idx, val in ((4, 65), (11, 65), (11, 0), (2, None), (13, None), (7, 0), (2, P + 2)):
+    base = [C.byref(L), 1, P, P + 0x10000, 32, 32, Q, Q + 0x10000, 4, P + 0x20000, 4,
+            P + 0x30000, 64, P + 0x40000, P + 0x50000, None, 0, None]
+    for idx, val in ((5, 65), (12, 65), (12, 0), (2, None), (14, None), (8, 0), (2, P + 2),
+                     (4, -1)):
         bad = list(base)
         bad[idx] = val
         assert lib.flint_attn_prefill(*bad) == INVALID, (idx, val)
+    # no rows: nothing to do, whatever the pointers
+    empty = list(base)
+    empty[4] = 0
+    empty[2] = None
+    assert lib.flint_attn_prefill(*empty) == 0
 
 
 def test_decode_plan_covers_every_page():

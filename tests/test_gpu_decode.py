@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from flint_cases import (TOL, CacheDecodeCase, DecodeCase, bf16_ulp_diff, down16, max_err)
+from flint_cases import (TOL, assert_parity, check_err, CacheDecodeCase, DecodeCase, bf16_ulp_diff, down16, max_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,7 @@ def test_full_layer_end_to_end(ctx):
     case = DecodeCase(0, [ctx], window=0)
     ref, q, kc, vc = case.expected()
     out, qd, kd, vd = case.run_gpu()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
     _check_cache(case, kd, vd, kc, vc)
     qg = qd.cpu().numpy()[case.last_row]
     assert np.max(np.abs(qg - q)) < 1e-6
@@ -44,7 +44,7 @@ def test_sliding_layer_end_to_end_ring(ctx):
     case = DecodeCase(1, [ctx], window=513, ring=True)
     ref, q, kc, vc = case.expected()
     out, qd, kd, vd = case.run_gpu()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
     _check_cache(case, kd, vd, kc, vc)
 
 
@@ -54,7 +54,7 @@ def test_ragged_batch_end_to_end_nonunit_weights():
         case = DecodeCase(2, ctxs, window=window, ring=ring, weights_one=False)
         ref, q, kc, vc = case.expected()
         out, qd, kd, vd = case.run_gpu()
-        assert max_err(out.cpu().numpy(), ref) <= TOL
+        assert_parity(out.cpu().numpy(), ref)
         _check_cache(case, kd, vd, kc, vc)
 
 
@@ -63,7 +63,7 @@ def test_split_counts_agree(pps):
     case = CacheDecodeCase(3, [4096, 1, 700, 33], window=0)
     ref = case.expected()
     got = case.run_gpu(pages_per_split=pps)
-    assert max_err(got, ref) <= TOL
+    assert_parity(got, ref)
 
 
 def test_full_layer_bs1_ctx4096():
@@ -71,7 +71,7 @@ def test_full_layer_bs1_ctx4096():
     case = DecodeCase(0, [4096], window=0)
     ref, _, _, _ = case.expected()
     out, _, _, _ = case.run_gpu()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
 
 
 def test_sliding_layer_bs1_ctx32768():
@@ -79,7 +79,7 @@ def test_sliding_layer_bs1_ctx32768():
     case = DecodeCase(0, [32768], window=513, ring=False)
     ref, _, _, _ = case.expected()
     out, _, _, _ = case.run_gpu()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
 
 
 def test_sink_minus_inf_and_large_scores():
@@ -89,7 +89,7 @@ def test_sink_minus_inf_and_large_scores():
     ref = oracle.attn_decode(case.L, case.q.astype(np.float64), case.kc, case.vc, case.bt,
                              case.seq_lens, ninf)
     got = case.run_gpu(sinks=ninf)
-    assert max_err(got, ref) <= TOL
+    assert_parity(got, ref)
 
 
 def test_invalid_requests_give_nan_not_faults():
@@ -101,7 +101,7 @@ def test_invalid_requests_give_nan_not_faults():
     sl[2] = 0                             # empty request
     for pps in (0, 2):
         got = case.run_gpu(pages_per_split=pps, seq_lens=sl, bt=bt)
-        assert max_err(got[0], ref[0]) <= TOL
+        assert_parity(got[0], ref[0])
         assert np.all(np.isnan(got[1])) and np.all(np.isnan(got[2]))
 
 
@@ -119,7 +119,7 @@ def test_ragged_64_requests_scaled_lengths():
     lens = synth.uniform_ints(0, (3, 0, synth.LENS), 64, 1024, 8192)
     for window in (0, 513):
         case = CacheDecodeCase(7, lens, window=window)
-        assert max_err(case.run_gpu(), case.expected()) <= TOL
+        assert_parity(case.run_gpu(), case.expected())
 
 
 @pytest.mark.parametrize("window,ring,ctxs,pps", [
@@ -140,7 +140,7 @@ def test_fused_step_bitwise_equals_append_then_decode(window, ring, ctxs, pps):
     assert np.array_equal(down16(vd), down16(vd_ref))
     assert np.array_equal(qo.cpu().numpy(), qd.cpu().numpy()[case.last_row])
     ref, _, _, _ = case.expected()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
 
 
 def test_fused_step_rejects_a_slot_the_page_table_disagrees_with():
@@ -149,7 +149,7 @@ def test_fused_step_rejects_a_slot_the_page_table_disagrees_with():
     out, _, kd, vd = case.run_gpu_fused(slot_delta=[0, 1, 0])
     got = out.cpu().numpy()
     assert np.all(np.isnan(got[1]))
-    assert max_err(got[[0, 2]], ref[[0, 2]]) <= TOL
+    assert_parity(got[[0, 2]], ref[[0, 2]])
     # nothing was written for request 1: its new token's row is still the sentinel
     s = int(case.slots[case.last_row[1]])
     kg = down16(kd)
@@ -165,4 +165,4 @@ def test_every_request_shorter_than_the_host_bound(window):
     ref = case.expected()
     for pps in (0, 1, 3):
         got = case.run_gpu(pages_per_split=pps, max_seq_len=case.bt_stride * 16)
-        assert max_err(got, ref) <= TOL
+        assert_parity(got, ref)

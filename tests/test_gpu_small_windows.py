@@ -6,7 +6,7 @@ C ABI admits 1..8, each with 8 query heads)."""
 import numpy as np
 import pytest
 
-from flint_cases import TOL, DecodeCase, max_err
+from flint_cases import TOL, assert_parity, check_err, DecodeCase, max_err
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,7 @@ def test_decode_small_windows(window):
     for pps in (0, 1, 3):
         out, _, _, _ = case.run_gpu(pages_per_split=pps)
         err = max_err(out.cpu().numpy(), ref)
-        assert err <= TOL, (window, pps, err)
+        check_err(err, ref, (window, pps))
 
 
 @pytest.mark.parametrize("window", [1, 16, 17, 33])
@@ -31,7 +31,7 @@ def test_fused_step_small_windows(window):
     for pps in (0, 2):
         out, _, _, _ = case.run_gpu_fused(pages_per_split=pps)
         err = max_err(out.cpu().numpy(), ref)
-        assert err <= TOL, (window, pps, err)
+        check_err(err, ref, (window, pps))
 
 
 @pytest.mark.parametrize("window", [1, 2, 16, 17, 31, 33, 100])
@@ -41,7 +41,7 @@ def test_prefill_small_windows(window):
     got, _, _, _ = case.run_gpu()
     bad = int((~np.isfinite(got)).sum())
     assert bad == 0, f"{bad} non-finite outputs"
-    assert max_err(got, case.expected()) <= TOL
+    assert_parity(got, case.expected())
 
 
 @pytest.mark.parametrize("window", [1, 17, 33])
@@ -51,7 +51,7 @@ def test_fp8_decode_small_windows(window):
     for pps in (0, 1):
         out, _, _, _ = case.run_gpu(pages_per_split=pps)
         err = max_err(out.cpu().numpy(), ref)
-        assert err <= TOL, (window, pps, err)
+        check_err(err, ref, (window, pps))
 
 
 # ---- KV head counts other than the model's 4 (the ABI admits 1..8) --------
@@ -63,9 +63,9 @@ def test_decode_and_fused_step_other_kv_head_counts(hkv):
         ref, _, _, _ = case.expected()
         for pps in (0, 1, 4):
             out, _, _, _ = case.run_gpu(pages_per_split=pps)
-            assert max_err(out.cpu().numpy(), ref) <= TOL, (hkv, window, pps)
+            assert_parity(out.cpu().numpy(), ref, (hkv, window, pps))
         out, _, _, _ = case.run_gpu_fused()
-        assert max_err(out.cpu().numpy(), ref) <= TOL, (hkv, window, "fused")
+        assert_parity(out.cpu().numpy(), ref, (hkv, window, "fused"))
 
 
 @pytest.mark.parametrize("hkv", [1, 8])
@@ -74,7 +74,7 @@ def test_prefill_other_kv_head_counts(hkv):
     for window in (0, 33):
         case = PrefillCase(45, [(300, 300), (700, 90)], window=window, hkv=hkv)
         got, _, _, _ = case.run_gpu()
-        assert max_err(got, case.expected()) <= TOL, (hkv, window)
+        assert_parity(got, case.expected(), (hkv, window))
 
 
 @pytest.mark.parametrize("hkv", [1, 8])
@@ -83,7 +83,7 @@ def test_fp8_decode_other_kv_head_counts(hkv):
                       hkv=hkv)
     ref, _, _, _ = case.expected()
     out, _, _, _ = case.run_gpu()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
 
 
 # ---- layer parameters other than the model's --------------------------------
@@ -98,10 +98,10 @@ def test_other_rope_bases_scales_and_eps(window, rope, theta, scale, eps):
     case = DecodeCase(47, [1, 17, 700, 3000], window=window, weights_one=False, **kw)
     ref, _, _, _ = case.expected()
     out, _, _, _ = case.run_gpu()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
     out, _, _, _ = case.run_gpu_fused()
-    assert max_err(out.cpu().numpy(), ref) <= TOL
+    assert_parity(out.cpu().numpy(), ref)
     from test_gpu_prefill import PrefillCase
     pc = PrefillCase(48, [(500, 500), (900, 130)], window=window, **kw)
     got, _, _, _ = pc.run_gpu()
-    assert max_err(got, pc.expected()) <= TOL
+    assert_parity(got, pc.expected())

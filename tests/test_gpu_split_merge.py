@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from flint_cases import TOL, CacheDecodeCase, dev, up
+from flint_cases import TOL, CacheDecodeCase, assert_parity, dev, up
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def test_partials_match_oracle_ranges(window, ctxs, pps):
     assert np.array_equal(np.isneginf(lse_gpu), empty)
     assert np.abs(lse_gpu[~empty] - lse_ref[~empty]).max() <= LSE_TOL
     o_gpu = po.cpu().numpy().astype(np.float64)
-    assert np.abs(o_gpu[~empty] - o_ref[~empty]).max() <= TOL
+    assert_parity(o_gpu[~empty], o_ref[~empty])
 
 
 @pytest.mark.parametrize("window,ctxs,pps", CASES)
@@ -88,9 +88,9 @@ def test_merge_of_oracle_partials_matches_oracle(window, ctxs, pps):
             live = ~np.isinf(lse_ref[b, :, h])
             want[b, h] = oracle.merge(o_ref[b, live, h], lse_ref[b, live, h],
                                       float(case.sinks[h]))
-    assert np.abs(got - want).max() <= TOL
+    assert_parity(got, want)
     # and the whole chain against the direct definition
-    assert np.abs(got - case.expected()).max() <= TOL
+    assert_parity(got, case.expected())
 
 
 @pytest.mark.parametrize("ctx,pps", [(300, 5), (300, 1), (2000, 1)])
@@ -144,4 +144,4 @@ def test_merge_of_unaligned_buffers(ctx, pps):
     assert po1.data_ptr() % 16 != 0 and out1.data_ptr() % 16 != 0
     got, want = out1.cpu().numpy(), ref.cpu().numpy()
     assert np.abs(got - want).max() <= 1e-5
-    assert np.abs(got.astype(np.float64) - case.expected()).max() <= TOL
+    assert_parity(got, case.expected())
