@@ -118,6 +118,12 @@ def lib() -> C.CDLL:
     """Load libflint.so (built by `python -m full_gqa_decode_amd.build`)."""
     global _lib
     if _lib is None:
+        # torch ships its own copy of the HIP runtime under the same soname as
+        # ROCm's.  Loaded first, it is the copy libflint.so binds to, so one
+        # runtime owns the device memory, the streams and our launches;
+        # loading libflint.so first would bring in a second runtime, which
+        # torch's memory and streams do not belong to.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise FileNotFoundError(
                 f"{LIB_PATH} is missing: build it with `python -m full_gqa_decode_amd.build`")

@@ -114,6 +114,13 @@ Plan make_plan(const flint_attn_layer* L, int32_t num_seqs, int32_t max_seq_len,
   int64_t p = pps;
   if (p <= 0) {
     const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * L->num_kv_heads;
+    if (pages <= flint::kSinglePages && units * flint::kVSlices <= flint::kVSliceGrid) {
+      // a short range at small batch: one split, run by the slice kernel
+      Plan pl;
+      pl.pages_per_split = (int32_t)pages;
+      pl.num_splits = 1;
+      return pl;
+    }
     int64_t splits = (kTargetWorkgroups + units - 1) / units;
     p = (pages + splits - 1) / splits;
     if (p > kMaxSplitPages) {

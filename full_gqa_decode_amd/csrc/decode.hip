@@ -31,8 +31,11 @@
 // Latency: page ids are fetched one page ahead of the K/V loads; in a split
 // the next page's K is requested right after the score MFMAs consume this
 // page's K, and its V right after the value MFMAs.  A short key range (the
-// 513-key window) is one split per (request, KV head) whose waves issue every
-// page load up front and fold the sink in directly, so no merge launch runs.
+// 513-key window) at small batch runs in decode_vsplit_kernel: 8 workgroups
+// per (request, KV head), each reading every K page and a 16-dim slice of V,
+// issuing every page load up front and folding the sink in directly, so no
+// merge launch runs.  At larger batch one workgroup per (request, KV head)
+// does the same over all 128 dims.
 // Fused step: the workgroup normalises/rotates its own 8 query heads (one wave
 // per head, into LDS) and the split holding the new token writes its K/V row
 // into the cache and substitutes it in registers, so append and attention are
@@ -644,6 +647,420 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short key ranges at small batch -- the 513-key window, or any range of at
+// most kSinglePages pages -- in one launch with no merge.  kVSlices
+// workgroups per (request, KV head); workgroup js owns output dims
+// js*16 .. js*16+15 of the group's 8 query heads.  Each reads every K page of
+// the range, so it forms the complete softmax of its heads (sink included)
+// by itself, and only its 16-dim slice of V: one value MFMA per page instead
+// of eight.  The kVSlices workgroups of one (request, KV head) are given
+// workgroup ids that MI355X's round-robin dispatch sends to the same XCD
+// (vsplit_item), so the repeated K reads are served from that XCD's L2 after
+// the first.  Cutting the keys over workgroups instead needs a merge of their
+// partials: a second launch or a hand-off through memory, each a further
+// memory round trip on this latency-bound path.
+static_assert(kVSlices * 16 == kHeadDim, "16-dim slices cover the head");
+
+struct SliceRegs {
+  bf16x8 k[4];  // K rows: MFMA A operand, 32 dims per block
+  u32x2 v;      // V: 4 tokens of one dim of this workgroup's 16-dim slice
+};
+struct SliceRaw8 {
+  u32x4 k[2];   // fp8 K codes, dims gq*32 .. gq*32+31 of row n
+  uint32_t v;   // fp8 V codes: 4 tokens of one dim of the slice
+};
+
+// K of a page with ordinary loads (the other slices of this (request, KV
+// head) read the same lines and should find them in L2); the V slice is read
+// by this workgroup alone, so nontemporal.
+__device__ __forceinline__ void load_slice(const DecodeArgs& a, int pg, int g, int n, int gq,
+                                           int js, SliceRegs& r) {
+  const int64_t tile = ((int64_t)pg * a.num_kv_heads + g) * (kPage * kHeadDim);
+  const uint16_t* kp = (const uint16_t*)a.k_cache + tile + (gq * 16 + n) * 8;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.k[c] = *(const bf16x8*)(kp + c * 512);
+  const uint16_t* vp = (const uint16_t*)a.v_cache + tile + (js * 16 + n) * kPage + gq * 4;
+  r.v = __builtin_nontemporal_load((const u32x2*)vp);
+}
+
+__device__ __forceinline__ void load_slice(const DecodeArgs& a, int pg, int g, int n, int gq,
+                                           int js, SliceRaw8& r) {
+  const int64_t tile = ((int64_t)pg * a.num_kv_heads + g) * (kPage * kHeadDim);
+  const uint8_t* kp = (const uint8_t*)a.k_cache + tile + (gq * 16 + n) * 16;
+  r.k[0] = *(const u32x4*)kp;
+  r.k[1] = *(const u32x4*)(kp + 1024);
+  // fp8_v_off(gq*4 + i, js*16 + n) for i = 0..3: one dword
+  const uint8_t* vp =
+      (const uint8_t*)a.v_cache + tile + (js >> 2) * 1024 + (gq * 16 + n) * 16 + (js & 3) * 4;
+  r.v = __builtin_nontemporal_load((const uint32_t*)vp);
+}
+
+__device__ __forceinline__ bf16x8 k_operand(const SliceRegs& r, int c) { return r.k[c]; }
+__device__ __forceinline__ bf16x8 k_operand(const SliceRaw8& r, int c) {
+  const bf16x4 x0 = fp8x4_to_bf16x4(r.k[c >> 1][(c & 1) * 2]);
+  const bf16x4 x1 = fp8x4_to_bf16x4(r.k[c >> 1][(c & 1) * 2 + 1]);
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x4 v_operand(const SliceRegs& r) {
+  return __builtin_bit_cast(bf16x4, r.v);
+}
+__device__ __forceinline__ bf16x4 v_operand(const SliceRaw8& r) { return fp8x4_to_bf16x4(r.v); }
+
+__device__ __forceinline__ void mask_v(SliceRegs& r, const bool (&keep)[4]) {
+  r.v[0] &= (keep[0] ? 0xffffu : 0u) | (keep[1] ? 0xffff0000u : 0u);
+  r.v[1] &= (keep[2] ? 0xffffu : 0u) | (keep[3] ? 0xffff0000u : 0u);
+}
+__device__ __forceinline__ void mask_v(SliceRaw8& r, const bool (&keep)[4]) {
+  r.v &= (keep[0] ? 0xffu : 0u) | (keep[1] ? 0xff00u : 0u) | (keep[2] ? 0xff0000u : 0u) |
+         (keep[3] ? 0xff000000u : 0u);
+}
+
+// The new token's K row (all dims) and this slice's 16 V values (bf16 bits
+// or fp8 codes, as cached) replace what the loads returned for row tr.
+__device__ __forceinline__ void substitute_new_token(SliceRegs& r, const uint16_t* knew,
+                                                     const uint16_t* vslice, int tr, int n,
+                                                     int gq) {
+  if (n == tr) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.k[c] = *(const bf16x8*)(knew + kdim<false>(c, gq, 0));
+  }
+  if (gq == (tr >> 2)) {
+    const int e = tr & 3;
+    const uint32_t bits = vslice[n];
+    uint32_t wv = r.v[e >> 1];
+    wv = (e & 1) ? ((wv & 0xffffu) | (bits << 16)) : ((wv & 0xffff0000u) | bits);
+    r.v[e >> 1] = wv;
+  }
+}
+__device__ __forceinline__ void substitute_new_token(SliceRaw8& r, const uint8_t* knew,
+                                                     const uint8_t* vslice, int tr, int n,
+                                                     int gq) {
+  if (n == tr) {
+    r.k[0] = *(const u32x4*)(knew + gq * 32);
+    r.k[1] = *(const u32x4*)(knew + gq * 32 + 16);
+  }
+  if (gq == (tr >> 2)) {
+    const int sh = (tr & 3) * 8;
+    r.v = (r.v & ~(0xffu << sh)) | ((uint32_t)vslice[n] << sh);
+  }
+}
+
+// One page of a slice workgroup: the score MFMAs over the whole head, mask of
+// the ragged ends, online softmax, one value MFMA for the 16-dim slice.
+template <typename Regs>
+__device__ __forceinline__ void consume_slice(Regs& r, const bf16x8 (&qop)[4], int p, int lo,
+                                              int t, int n, int gq, f32x4& acc, float& m_run,
+                                              float& l_part) {
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(r, c), qop[c], sc, 0, 0, 0);
+  float sv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sv[i] = sc[i] + lane_xor8(sc[i]);
+  const int tok0 = p * kPage;
+  if (tok0 < lo || tok0 + kPage - 1 > t) {
+    bool keep[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = tok0 + gq * 4 + i;
+      keep[i] = tok >= lo && tok <= t;
+      if (!keep[i]) sv[i] = -INFINITY;
+    }
+    mask_v(r, keep);
+  }
+  float pmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  pmax = max_xor32(max_xor16(pmax));
+  const float m_new = fmaxf(m_run, pmax);
+  if (__any(m_new > m_run)) {
+    const float alpha = exp2_fast(m_run - m_new);
+    l_part *= alpha;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= __shfl(alpha, (gq * 4 + i) & 7);
+  }
+  m_run = m_new;
+  float pv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pv[i] = exp2_fast(sv[i] - m_new);
+  l_part += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+  const f32x2 p01 = {pv[0], pv[1]}, p23 = {pv[2], pv[3]};
+  const bf16x2 h01 = __builtin_convertvector(p01, bf16x2);
+  const bf16x2 h23 = __builtin_convertvector(p23, bf16x2);
+  const bf16x2 r01 = __builtin_convertvector(p01 - __builtin_convertvector(h01, f32x2), bf16x2);
+  const bf16x2 r23 = __builtin_convertvector(p23 - __builtin_convertvector(h23, f32x2), bf16x2);
+  const bf16x2 s01 = (n < 8) ? h01 : r01;
+  const bf16x2 s23 = (n < 8) ? h23 : r23;
+  const bf16x4 pop = {s01[0], s01[1], s23[0], s23[1]};
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, v_operand(r), acc, 0, 0, 0);
+}
+
+// Work item of slice workgroup L of a grid of units * kVSlices, units =
+// requests x KV heads.  Workgroups are dispatched to MI355X's 8 XCDs
+// round-robin (L to XCD L % 8), so XCD x runs L = x, x+8, x+16, ...: giving
+// it the items x*units .. x*units + units-1 of the unit-major order keeps the
+// slices of a unit together on one XCD (or two, when units < 8).
+__device__ __forceinline__ void vsplit_item(int L, int units, int& unit, int& js) {
+  const int i = (L & 7) * units + (L >> 3);
+  unit = i / kVSlices;
+  js = i % kVSlices;
+}
+
+// WAVES waves; each takes the pages w, w+WAVES, ... of the range and issues
+// all of its (at most MAXP) page loads up front.
+template <int WAVES, int MAXP, bool WINDOWED, bool FUSED, bool KV8>
+__global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs a) {
+  static_assert(WAVES >= kGroup, "one wave per query head of the group");
+  using Raw = typename std::conditional<KV8, SliceRaw8, SliceRegs>::type;
+  using Elem = typename std::conditional<KV8, uint8_t, uint16_t>::type;
+  int unit, js;
+  vsplit_item(blockIdx.x, a.num_seqs * a.num_kv_heads, unit, js);
+  const int b = unit / a.num_kv_heads, g = unit % a.num_kv_heads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, gq = lane >> 4;
+  const int hq = a.num_kv_heads * kGroup;
+  // fused: the new K row is normalised by wave kKw, the V row by wave kVw
+  constexpr int kKw = WAVES > kGroup ? kGroup : 0;
+  constexpr int kVw = WAVES > kGroup + 1 ? kGroup + 1 : 1;
+
+  __shared__ float sm_o[WAVES][kGroup][16];
+  __shared__ float sm_m[WAVES][kGroup];
+  __shared__ float sm_l[WAVES][kGroup];
+  __shared__ int sm_bad[WAVES];
+  __shared__ float sm_q[FUSED ? kGroup : 1][kHeadDim];
+  __shared__ __attribute__((aligned(16))) Elem sm_knew[FUSED ? kHeadDim : 16];
+  __shared__ __attribute__((aligned(16))) Elem sm_vnew[16];
+  __shared__ int sm_fused_bad;
+
+  // ---- loads that do not wait for seq_len (as in decode_split_kernel) ----
+  float x0 = 0.f, x1 = 0.f;
+  float qw0 = 0.f, qw1 = 0.f, kw0 = 0.f, kw1 = 0.f, xk0 = 0.f, xk1 = 0.f, xv0 = 0.f, xv1 = 0.f;
+  int slot_pre = 0, pg_last_pre = -1;
+  f32x4 qraw[8];
+  if (FUSED) {
+    const int hh = min(w, kGroup - 1);
+    const float* x = a.q_in + ((int64_t)b * hq + g * kGroup + hh) * kHeadDim;
+    x0 = x[lane];
+    x1 = x[lane + 64];
+    qw0 = a.q_w[lane];
+    qw1 = a.q_w[lane + 64];
+    const float* xk = a.k_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+    const float* xv = a.v_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
+    kw0 = a.k_w[lane];
+    kw1 = a.k_w[lane + 64];
+    xk0 = xk[lane];
+    xk1 = xk[lane + 64];
+    xv0 = xv[lane];
+    xv1 = xv[lane + 64];
+    slot_pre = a.slots[b];
+    pg_last_pre = page_id(a, b, (a.max_seq_len - 1) / kPage);
+  } else {
+    const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qraw[2 * c] = *(const f32x4*)(qh + kdim<KV8>(c, gq, 0));
+      qraw[2 * c + 1] = *(const f32x4*)(qh + kdim<KV8>(c, gq, 4));
+    }
+  }
+  auto range = [&](int tt, int& lo_, int& pb, int& pe) {
+    lo_ = WINDOWED ? max(0, tt - a.window + 1) : 0;
+    pb = lo_ / kPage;
+    pe = tt / kPage + 1;
+  };
+  int lo, p_begin, p_end;
+  range(a.max_seq_len - 1, lo, p_begin, p_end);
+  Raw r[MAXP];
+  int bad = 0;
+  auto issue = [&](int k) {
+    const int p = p_begin + w + k * WAVES;
+    if (p < p_end) {
+      int pg = page_id(a, b, p);
+      bad |= pg < 0;
+      pg = max(pg, 0);
+      load_slice(a, pg, g, n, gq, js, r[k]);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) issue(k);
+  double cs = 1.0, sn = 0.0;
+  if (FUSED && a.use_rope) rope_cos_sin(a.max_seq_len - 1, lane, a.rope_theta, &cs, &sn);
+
+  // ---- the request's real length ------------------------------------------
+  const int seq_len = a.seq_lens[b];
+  const bool len_bad = seq_len < 1 || seq_len > a.max_seq_len;
+  const int t = seq_len - 1;
+  if (!len_bad && seq_len != a.max_seq_len) {
+    range(t, lo, p_begin, p_end);
+    bad = 0;
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) issue(k);
+  }
+  if (len_bad) {
+    if (tid < kGroup * 16)
+      a.out[((int64_t)b * hq + g * kGroup + (tid >> 4)) * kHeadDim + js * 16 + (tid & 15)] =
+          __builtin_nanf("");
+    return;
+  }
+  const int last_page = t / kPage;
+  const int tr = t % kPage;
+
+  // ---- q operand (and, fused, the new token) ------------------------------
+  bf16x8 qop[4];
+  if (FUSED) {
+    if (a.use_rope && t != a.max_seq_len - 1) rope_cos_sin(t, lane, a.rope_theta, &cs, &sn);
+    if (w < kGroup) {
+      double y0, y1;
+      norm_rope_head(x0, x1, qw0, qw1, a.rms_eps, a.use_rope, cs, sn, &y0, &y1);
+      sm_q[w][lane] = (float)y0;
+      sm_q[w][lane + 64] = (float)y1;
+      if (js == 0 && a.q_out) {
+        float* qo = a.q_out + ((int64_t)b * hq + g * kGroup + w) * kHeadDim;
+        qo[lane] = (float)y0;
+        qo[lane + 64] = (float)y1;
+      }
+    }
+    // the slot must be where the page table puts position t; only slice 0
+    // writes the cache, every slice substitutes the new row in registers
+    const int pg = t == a.max_seq_len - 1 ? pg_last_pre : page_id(a, b, last_page);
+    const bool ok = pg >= 0 && slot_pre == pg * kPage + tr;
+    const bool write = ok && js == 0;
+    if (w == kKw) {
+      double y0, y1;
+      norm_rope_head(xk0, xk1, kw0, kw1, a.rms_eps, a.use_rope, cs, sn, &y0, &y1);
+      const int64_t o = ((int64_t)max(pg, 0) * a.num_kv_heads + g) * (kPage * kHeadDim);
+      if (KV8) {
+        const uint32_t c0 = fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
+        const uint32_t c1 = fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
+        sm_knew[lane] = (Elem)c0;
+        sm_knew[lane + 64] = (Elem)c1;
+        if (write) {
+          uint8_t* dst = (uint8_t*)a.k_cache + o;
+          dst[fp8_k_off(tr, lane)] = (uint8_t)c0;
+          dst[fp8_k_off(tr, lane + 64)] = (uint8_t)c1;
+        }
+      } else {
+        const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
+        sm_knew[lane] = (Elem)k0;
+        sm_knew[lane + 64] = (Elem)k1;
+        if (write) {
+          uint16_t* dst = (uint16_t*)a.k_cache + o;
+          dst[bf16_k_off(tr, lane)] = k0;
+          dst[bf16_k_off(tr, lane + 64)] = k1;
+        }
+      }
+      if (lane == 0) sm_fused_bad = !ok;
+    }
+    if (w == kVw) {
+      const int64_t o = ((int64_t)max(pg, 0) * a.num_kv_heads + g) * (kHeadDim * kPage);
+      uint32_t c0, c1;
+      if (KV8) {
+        c0 = fp8_e4m3_rne_f64((double)xv0 / (double)a.v_scale);
+        c1 = fp8_e4m3_rne_f64((double)xv1 / (double)a.v_scale);
+        if (write) {
+          uint8_t* dst = (uint8_t*)a.v_cache + o;
+          dst[fp8_v_off(tr, lane)] = (uint8_t)c0;
+          dst[fp8_v_off(tr, lane + 64)] = (uint8_t)c1;
+        }
+      } else {
+        c0 = bf16_bits_rne(xv0);
+        c1 = bf16_bits_rne(xv1);
+        if (write) {
+          uint16_t* dst = (uint16_t*)a.v_cache + o + tr;
+          dst[lane * kPage] = (uint16_t)c0;
+          dst[(lane + 64) * kPage] = (uint16_t)c1;
+        }
+      }
+      // this slice's dims js*16 .. js*16+15 sit in lanes (js&3)*16 .. +15 of
+      // the half (js >> 2)
+      const int d = lane - (js & 3) * 16;
+      if (d >= 0 && d < 16) sm_vnew[d] = (Elem)((js >> 2) ? c1 : c0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float* qh = &sm_q[n & 7][kdim<KV8>(c, gq, 0)];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f32x2 v = {qh[j] * a.qscale, qh[j + 1] * a.qscale};
+        const bf16x2 hi = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
+        const bf16x2 sel = (n < 8) ? hi : lo2;
+        qop[c][j] = sel[0];
+        qop[c][j + 1] = sel[1];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 q0 = qraw[2 * c], q1 = qraw[2 * c + 1];
+      const float xs[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f32x2 v = {xs[j] * a.qscale, xs[j + 1] * a.qscale};
+        const bf16x2 hi = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
+        const bf16x2 sel = (n < 8) ? hi : lo2;
+        qop[c][j] = sel[0];
+        qop[c][j + 1] = sel[1];
+      }
+    }
+  }
+
+  // ---- pages ---------------------------------------------------------------
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    const int p = p_begin + w + k * WAVES;
+    if (p < p_end) {
+      if (FUSED && p == last_page) substitute_new_token(r[k], sm_knew, sm_vnew, tr, n, gq);
+      consume_slice(r[k], qop, p, lo, t, n, gq, acc, m_run, l_part);
+    }
+  }
+
+  // ---- waves -> LDS -> this slice of the output ----------------------------
+  const float l_h = sum_xor32(sum_xor16(l_part));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = sum_xor32(acc[i]);
+  if (gq < 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[w][gq * 4 + i][n] = acc[i];
+  }
+  if (lane < kGroup) {
+    sm_m[w][lane] = m_run;
+    sm_l[w][lane] = l_h;
+  }
+  bad = __any(bad);
+  if (lane == 0) sm_bad[w] = bad;
+  __syncthreads();
+  if (tid < kGroup * 16) {
+    int any_bad = FUSED ? sm_fused_bad : 0;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) any_bad |= sm_bad[v];
+    const int h = tid >> 4, d = tid & 15;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sm_m[v][h]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) {
+      const float e = exp2_fast(sm_m[v][h] - M);
+      L += e * sm_l[v][h];
+      o += e * sm_o[v][h][d];
+    }
+    const int hg = g * kGroup + h;
+    const float sink = a.sinks[hg] * kLog2e;
+    const float M2 = fmaxf(M, sink);
+    const float scale_o = exp2_fast(M - M2);
+    const float den = exp2_fast(sink - M2) + L * scale_o;
+    float res = o * scale_o / den;
+    if (KV8) res *= a.v_scale;
+    if (any_bad) res = __builtin_nanf("");
+    a.out[((int64_t)b * hq + hg) * kHeadDim + js * 16 + d] = res;
+  }
+}
+
 // K3: out_h = sum_s w_s o_s / (e^{sink_h} + sum_s w_s), w_s = 2^{lse_s - M},
 // in log2 units.  Every split of the grid left an lse (-inf when it held no
 // key, NaN for a bad request or page), so no load here waits on seq_lens.
@@ -781,53 +1198,48 @@ __global__ __launch_bounds__(kSmallMergeThreads) void decode_merge_small_kernel(
   a.out[bh * kHeadDim + d] = nan ? __builtin_nanf("") : o / den;
 }
 
-// K3 for plans of kSmallMergeSplits+1 .. kMidMergeSplits splits (batch 1: the
-// 100K full layer's 64 splits, the window's 17): one wave per (request, query
-// head), with no LDS and no barrier.  Lane l holds split l's lse; the max, the
-// weights and the denominator come from wave reductions.  For the values,
-// lane (c, sg) = (l & 31, l >> 5) sums dims 4c..4c+3 over the splits of
-// parity sg; every load is issued before the max is known (one memory round
-// trip), and the two halves meet across lanes l and l^32.
+// K3 for plans of kSmallMergeSplits+1 .. kMidMergeSplits splits (batch 1:
+// the 100K full layer's 64 splits).
 constexpr int kMidMergeSplits = 64;
 
-__global__ __launch_bounds__(64) void decode_merge_mid_kernel(DecodeArgs a) {
+// K3 for plans of kSmallMergeSplits+1 .. kMidMergeSplits splits, spread
+// over (request, query head, 16-dim slice): one wave each, so that a batch-1
+// layer's 1 MB of partials is read by 256 workgroups at 4 KiB apiece rather
+// than by 32 at 32 KiB.  Lane l holds split l's lse and its 16 values of the
+// slice (four 16-byte loads), all requested before any is used; the max and
+// the weights come from wave reductions and every output dim is a wave sum.
+__global__ __launch_bounds__(64) void decode_merge_slice_kernel(DecodeArgs a) {
   const int hq = a.num_kv_heads * kGroup;
   const int ns = a.num_splits;
-  const int bh = blockIdx.x;  // b * hq + h
+  const int js = blockIdx.x % kVSlices;
+  const int bh = blockIdx.x / kVSlices;  // b * hq + h
   const int h = bh % hq, b = bh / hq;
-  const int l = threadIdx.x, c = l & 31, sg = l >> 5;
-  const int64_t base = (int64_t)b * ns * hq + h;  // split s: row base + s * hq
-  // loads past the last split re-read it (no branch between the loads); their
-  // weights are 0
-  float lse = a.part_lse[base + (int64_t)min(l, ns - 1) * hq];
-  if (l >= ns) lse = -INFINITY;
-  f32x4 ov[kMidMergeSplits / 2];
+  const int l = threadIdx.x;
+  const int64_t row = (int64_t)b * ns * hq + h + (int64_t)min(l, ns - 1) * hq;
+  // lanes past the last split re-read it (no branch between the loads);
+  // their weights are 0
+  float lse = a.part_lse[row];
+  const float* po = a.part_o + row * kHeadDim + js * 16;
+  f32x4 ov[4];
 #pragma unroll
-  for (int j = 0; j < kMidMergeSplits / 2; ++j) {
-    const int s = min(2 * j + sg, ns - 1);
-    ov[j] = *(const f32x4*)(a.part_o + (base + (int64_t)s * hq) * kHeadDim + 4 * c);
-  }
+  for (int i = 0; i < 4; ++i) ov[i] = *(const f32x4*)(po + 4 * i);
   __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the reductions
+  if (l >= ns) lse = -INFINITY;
   const bool nan = __any(lse != lse);
   const float sink = a.sinks[h] * kLog2e;
   const float M = fmaxf(sink, wave_max_f32(lse));
   // an empty split (lse -inf, output never written) contributes 0
   const float w = lse > -INFINITY ? exp2_fast(lse - M) : 0.f;
-  const float den = exp2_fast(sink - M) + wave_sum_f32(w);
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  const float inv = 1.f / (exp2_fast(sink - M) + wave_sum_f32(w));
+  float res = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMidMergeSplits / 2; ++j) {
-    const float w0 = readlane_f32(w, 2 * j), w1 = readlane_f32(w, 2 * j + 1);
-    const float ws = sg ? w1 : w0;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] += ws > 0.f ? ws * ov[j][i] : 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = sum_xor32(o[i]);
-  if (sg == 0) {
-    const f32x4 r = nan ? f32x4{NAN, NAN, NAN, NAN} : o / den;
-    *(f32x4*)(a.out + (int64_t)bh * kHeadDim + 4 * c) = r;
-  }
+    for (int j = 0; j < 4; ++j) {
+      const float s = wave_sum_f32(w > 0.f ? w * ov[i][j] : 0.f);
+      if (l == 4 * i + j) res = s;
+    }
+  if (l < 16) a.out[(int64_t)bh * kHeadDim + js * 16 + l] = nan ? __builtin_nanf("") : res * inv;
 }
 
 hipError_t launch_merge_k(const DecodeArgs& a, hipStream_t st) {
@@ -837,8 +1249,8 @@ hipError_t launch_merge_k(const DecodeArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)((n + kSmallMergeThreads - 1) / kSmallMergeThreads));
     hipLaunchKernelGGL(decode_merge_small_kernel, grid, dim3(kSmallMergeThreads), 0, st, a);
   } else if (a.num_splits <= kMidMergeSplits && al16) {
-    const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * kGroup));
-    hipLaunchKernelGGL(decode_merge_mid_kernel, grid, dim3(64), 0, st, a);
+    const dim3 grid((unsigned)(a.num_seqs * a.num_kv_heads * kGroup * kVSlices));
+    hipLaunchKernelGGL(decode_merge_slice_kernel, grid, dim3(64), 0, st, a);
   } else {
     const dim3 mgrid(a.num_kv_heads * kGroup, a.num_seqs, kHeadDim / kMergeDims);
     hipLaunchKernelGGL(decode_merge_kernel, mgrid, dim3(kMergeThreads), 0, st, a);
@@ -858,6 +1270,20 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     else
       hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false, KV8>), grid, dim3(W * 64),
                          0, st, a);
+    return hipGetLastError();
+  }
+  if (a.num_splits == 1 && a.pages_per_split <= kSinglePages &&
+      (int64_t)a.num_seqs * a.num_kv_heads * kVSlices <= kVSliceGrid) {
+    // one round of slice workgroups: one launch, no merge
+    constexpr int W = kVSliceWaves;
+    constexpr int P = (kSinglePages + W - 1) / W;
+    const dim3 vgrid((unsigned)(a.num_seqs * a.num_kv_heads * kVSlices));
+    if (win)
+      hipLaunchKernelGGL((decode_vsplit_kernel<W, P, true, FUSED, KV8>), vgrid, dim3(W * 64), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((decode_vsplit_kernel<W, P, false, FUSED, KV8>), vgrid, dim3(W * 64), 0,
+                         st, a);
     return hipGetLastError();
   }
   if (a.num_splits == 1 && a.pages_per_split <= kSinglePages) {

@@ -97,18 +97,28 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 
 // Waves per decode workgroup: kDecodeWaves when the key range is split (two
 // workgroups per CU), kDecodeWavesSingle when one workgroup covers a short
-// range by itself.  kSinglePages: ranges of at most this many pages use one
-// workgroup per (request, KV head), with every page load in flight at once
-// (kSinglePages / kDecodeWavesSingle pages of registers per wave) and no
-// merge launch.
+// range by itself.  kSinglePages: ranges of at most this many pages run in
+// one split with every page load in flight at once (kSinglePages /
+// waves pages of registers per wave) and no merge launch -- at small batch
+// in kVSlices slice workgroups per (request, KV head) (below), otherwise in
+// one workgroup per (request, KV head).
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeWavesSingle = 8;
 constexpr int kSinglePages = 40;
-// kShortMinPages: least pages per split the plan gives a short range.  The
-// 513-key window at batch 1 then takes 7 splits: 28 workgroups still spread
-// its 1 MB over enough CUs, and at 8 splits or fewer the merge runs the
-// one-pass small-merge kernel.  Measured per fused sliding step in a graph:
-// 8.4 us at 7 splits, 9.0 us at 17 (2 pages each), 9.4 at 4.
+// kShortMinPages: least pages per split the plan gives a short range it
+// splits (batches past the slice grid, or a caller's explicit split size).
+// The 513-key window then takes 7 splits: at 8 splits or fewer the merge
+// runs the one-pass small-merge kernel.  Measured per fused sliding step at
+// batch 1 in a graph: 8.4 us at 7 splits, 9.0 us at 17 (2 pages each), 9.4
+// at 4; the slice kernel (one launch) 8.1 us.
 constexpr int kShortMinPages = 5;
+// Short ranges (at most kSinglePages pages) at small batch: kVSlices
+// workgroups per (request, KV head), each owning 16 of the 128 output dims,
+// reading every K page of the range and its slice of V, with the sink folded
+// in -- one launch and no merge.  Used while the grid (requests x KV heads x
+// kVSlices) fits one round of kVSliceGrid workgroups.
+constexpr int kVSlices = 8;
+constexpr int kVSliceWaves = 8;
+constexpr int kVSliceGrid = 256;
 
 }  // namespace flint

@@ -64,14 +64,14 @@ class BigStep:
         self.pos = t.astype(np.int32)
         self.slots = np.array([oracle.slot(self.bt, b, int(t[b])) for b in range(B)], np.int32)
 
-    def run_gpu(self):
+    def run_gpu(self, pages_per_split=0):
         import torch
         import full_gqa_decode_amd as fl
         out = torch.empty((self.B, 32, 128), dtype=torch.float32, device=dev())
         fl.flint_attn_decode_step(self.FL, up(self.q_in), up(self.k_in), up(self.v_in),
                                   up(self.qw), up(self.kw), up(self.slots), self.kd, self.vd,
                                   up(self.bt), up(self.ctxs), int(self.ctxs.max()),
-                                  up(self.sinks), out)
+                                  up(self.sinks), out, pages_per_split=pages_per_split)
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
@@ -137,11 +137,14 @@ def test_bs1_100k_full_layer_step():
     assert np.array_equal(case.vd.cpu().numpy().view(np.uint16), case.vc)
 
 
-def test_bs1_100k_sliding_layer_step():
+@pytest.mark.parametrize("pps", [0, 5])
+def test_bs1_100k_sliding_layer_step(pps):
+    # the default plan (one launch of 16-dim slice workgroups) and the
+    # key-split plan (7 splits of 5 pages and a merge launch)
     import full_gqa_decode_amd as fl
     case = BigStep((11, 2), [100_000], window=513, full_table=False)
-    assert fl.flint_attn_decode_plan(case.FL, 1, 100_000) == (5, 7)
-    got = case.run_gpu()
+    assert fl.flint_attn_decode_plan(case.FL, 1, 100_000, pps) == ((33, 1) if pps == 0 else (5, 7))
+    got = case.run_gpu(pps)
     ref = case.oracle_step(np.arange(1))
     err = float(np.abs(got - ref).max())
     print(f"bs1 100K sliding layer: max err {err:.3e}", flush=True)
