@@ -99,6 +99,8 @@ SIGNATURES = [
      [_LP, _I, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _I, _P]),
     ("flint_attn_decode_step", C.c_int,
      [_LP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _P, _SZ, _I, _P]),
+    ("flint_attn_decode_step_noalloc", C.c_int,
+     [_LP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P]),
     ("flint_attn_decode_plan", C.c_int, [_LP, _I, _I, _I, C.POINTER(_I), C.POINTER(_I)]),
     ("flint_attn_decode_partials", C.c_int,
      [_LP, _I, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P, _P, _P]),
@@ -351,6 +353,34 @@ def flint_attn_decode_step(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_norm
         _ptr(out, _f32(), "out"), None if workspace is None else workspace.data_ptr(), ws_bytes,
         pages_per_split, _stream(stream)))
     return out
+
+
+def flint_attn_decode_step_noalloc(L: FlintAttnLayer, q_in, k_in, v_in, q_norm_w, k_norm_w,
+                                   slot_mapping, k_cache, v_cache, block_tables, seq_lens,
+                                   max_seq_len: int, sinks, out, q_out=None,
+                                   pages_per_split: int = 0, stream=None):
+    """flint_attn_decode_step with the split partials in the library's static
+    device scratch instead of a workspace: nothing is allocated."""
+    B = q_in.shape[0]
+    Hq, Hkv, D = L.num_q_heads, L.num_kv_heads, L.head_dim
+    _sizes(L, B, q_in=(q_in, B * Hq * D), k_in=(k_in, B * Hkv * D), v_in=(v_in, B * Hkv * D),
+           q_norm_w=(q_norm_w, D), k_norm_w=(k_norm_w, D), slot_mapping=(slot_mapping, B),
+           q_out=(q_out, B * Hq * D), k_cache=(k_cache, _cache_elems(L, k_cache)),
+           v_cache=(v_cache, _cache_elems(L, k_cache)), block_tables=(block_tables, 0),
+           seq_lens=(seq_lens, B), sinks=(sinks, Hq), out=(out, B * Hq * D))
+    _check(lib().flint_attn_decode_step_noalloc(
+        C.byref(L), B, _ptr(q_in, _f32(), "q_in"), _ptr(k_in, _f32(), "k_in"),
+        _ptr(v_in, _f32(), "v_in"), _ptr(q_norm_w, _f32(), "q_norm_w"),
+        _ptr(k_norm_w, _f32(), "k_norm_w"), _ptr(slot_mapping, _i32(), "slot_mapping"),
+        _ptr(q_out, _f32(), "q_out"), _ptr(k_cache, _kv(L), "k_cache"),
+        _ptr(v_cache, _kv(L), "v_cache"), k_cache.shape[0],
+        _ptr(block_tables, _i32(), "block_tables"), block_tables.shape[1],
+        _ptr(seq_lens, _i32(), "seq_lens"), max_seq_len, _ptr(sinks, _f32(), "sinks"),
+        _ptr(out, _f32(), "out"), pages_per_split, _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def flint_attn_prefill_workspace_size(L: FlintAttnLayer, num_seqs: int, max_q_len: int,

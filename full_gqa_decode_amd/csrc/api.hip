@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/flint.h"
 #include "launch.h"
@@ -158,6 +159,39 @@ WsLayout ws_layout(const flint_attn_layer* L, int32_t num_seqs, const Plan& pl) 
 
 size_t decode_ws_bytes(const flint_attn_layer* L, int32_t num_seqs, const Plan& pl) {
   return ws_layout(L, num_seqs, pl).total;
+}
+
+// Library-owned scratch for flint_attn_decode_step_noalloc: the split
+// partials of one call.  Every GPU the library runs on holds its own copy of
+// this array for the life of the process.  In host code `scratch` only names
+// the variable: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is ever handed to a kernel.
+constexpr size_t kScratchBytes = FLINT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use on that
+// device, with the device current).
+flint_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(FLINT_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(FLINT_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLINT_OK;
 }
 
 }  // namespace
@@ -388,6 +422,39 @@ flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
   a.slots = slot_mapping;
   a.q_out = q_out;
   return hip_status(flint::launch_decode(a, (hipStream_t)stream), "decode step launch");
+}
+
+flint_status flint_attn_decode_step_noalloc(
+    const flint_attn_layer* L, int32_t num_seqs, const float* q_in, const float* k_in,
+    const float* v_in, const float* q_norm_w, const float* k_norm_w,
+    const int32_t* slot_mapping, float* q_out, void* k_cache, void* v_cache, int32_t num_blocks,
+    const int32_t* block_tables, int32_t bt_stride, const int32_t* seq_lens,
+    int32_t max_seq_len, const float* sinks, float* out, int32_t pages_per_split, void* stream) {
+  flint_status st = check_layer(L);
+  if (st != FLINT_OK) return st;
+  if (num_seqs < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
+  if (pages_per_split < 0)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "pages_per_split %d < 0", pages_per_split);
+  if (max_seq_len < 1 || max_seq_len > kMaxContext)
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [1, %d]", max_seq_len,
+                kMaxContext);
+  if (num_seqs == 0) return ok();
+  const size_t need = decode_ws_bytes(L, num_seqs, make_plan(L, num_seqs, max_seq_len,
+                                                             pages_per_split));
+  if (need > kScratchBytes)
+    return fail(FLINT_ERR_WORKSPACE_TOO_SMALL,
+                "this batch needs %zu bytes of split partials, above the %zu-byte static "
+                "scratch of the allocation-free step (use flint_attn_decode_step with a "
+                "workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_current_device(&ws);
+    if (st != FLINT_OK) return st;
+  }
+  return flint_attn_decode_step(L, num_seqs, q_in, k_in, v_in, q_norm_w, k_norm_w, slot_mapping,
+                                q_out, k_cache, v_cache, num_blocks, block_tables, bt_stride,
+                                seq_lens, max_seq_len, sinks, out, ws, need, pages_per_split,
+                                stream);
 }
 
 flint_status flint_attn_decode(const flint_attn_layer* L, int32_t num_seqs, const float* q,

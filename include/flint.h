@@ -223,6 +223,31 @@ flint_status flint_attn_decode_step(const flint_attn_layer* L, int32_t num_seqs,
                                     size_t workspace_bytes, int32_t pages_per_split,
                                     void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * flint_attn_decode_step without the workspace arguments, same results bit for
+ * bit.  The split partials live in a static device array of
+ * FLINT_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call allocates nothing.  A batch whose plan
+ * needs more partials than that (flint_attn_decode_workspace_size_ex above
+ * the limit; e.g. more than ~16 requests at a 100,000-token context) returns
+ * FLINT_ERR_WORKSPACE_TOO_SMALL before any launch.  All calls on one GPU share
+ * the array: calls that may overlap on one GPU (several streams, several host
+ * threads) race on it and must be serialised by the caller.  Its contents
+ * need no initialisation: every call writes each partial before reading it.
+ */
+#define FLINT_NOALLOC_SCRATCH_BYTES (16u << 20)
+flint_status flint_attn_decode_step_noalloc(const flint_attn_layer* L, int32_t num_seqs,
+                                            const float* q_in, const float* k_in,
+                                            const float* v_in, const float* q_norm_w,
+                                            const float* k_norm_w, const int32_t* slot_mapping,
+                                            float* q_out, void* k_cache, void* v_cache,
+                                            int32_t num_blocks, const int32_t* block_tables,
+                                            int32_t bt_stride, const int32_t* seq_lens,
+                                            int32_t max_seq_len, const float* sinks, float* out,
+                                            int32_t pages_per_split, void* stream);
+
 /* The split plan flint_attn_decode_ex would use (host only, no HIP call):
  * writes the pages per split and the number of splits per request. */
 flint_status flint_attn_decode_plan(const flint_attn_layer* L, int32_t num_seqs,

@@ -169,9 +169,10 @@ class DecodeCase:
         return out, qd, kd, vd
 
 
-    def run_gpu_fused(self, pages_per_split=0, slot_delta=None):
+    def run_gpu_fused(self, pages_per_split=0, slot_delta=None, noalloc=False):
         """append every token except each request's new one, then the fused
-        step (append of the new token + decode in one launch)."""
+        step (append of the new token + decode in one launch); noalloc: through
+        flint_attn_decode_step_noalloc (the library's static scratch)."""
         import torch
         import full_gqa_decode_amd as fl
         kd, vd = empty_caches(self.L, self.num_blocks, device=True)
@@ -189,7 +190,8 @@ class DecodeCase:
             slots = slots + np.asarray(slot_delta, np.int32)
         out = torch.empty((self.B, self.hq, 128), dtype=torch.float32, device=dev())
         qo = torch.empty((self.B, self.hq, 128), dtype=torch.float32, device=dev())
-        fl.flint_attn_decode_step(self.FL, up(self.q_in[r]), up(self.k_in[r]), up(self.v_in[r]), up(self.qw),
+        step = fl.flint_attn_decode_step_noalloc if noalloc else fl.flint_attn_decode_step
+        step(self.FL, up(self.q_in[r]), up(self.k_in[r]), up(self.v_in[r]), up(self.qw),
              up(self.kw), up(slots), kd, vd, up(self.bt), up(self.seq_lens), max(self.ctxs),
              up(self.sinks), out, q_out=qo, pages_per_split=pages_per_split)
         torch.cuda.synchronize()

@@ -138,6 +138,25 @@ def test_fused_step_rejects_q_out_aliasing_q_in():
         assert "q_out" in lib.flint_last_error().decode()
 
 
+def test_noalloc_step_limit_is_checked_before_any_launch():
+    # a plan whose partials exceed the static scratch is refused on the host
+    lib = fl.lib()
+    L = fl.full_layer()
+    B, ctx = 64, 131072
+    assert fl.flint_attn_decode_workspace_size(L, B, ctx) > fl.NOALLOC_SCRATCH_BYTES
+    args = [C.byref(L), B, P, P + 0x10000, P + 0x20000, P + 0x30000, P + 0x40000, P + 0x50000,
+            None, Q, Q + 0x10000, 4, P + 0x60000, ctx // 16, P + 0x70000, ctx, P + 0xA0000,
+            P + 0xB0000, 0, None]
+    assert lib.flint_attn_decode_step_noalloc(*args) == WS_SMALL
+    assert "static scratch" in lib.flint_last_error().decode()
+    bad = list(args)
+    bad[1] = -1
+    assert lib.flint_attn_decode_step_noalloc(*bad) == INVALID
+    bad = list(args)
+    bad[1] = 0
+    assert lib.flint_attn_decode_step_noalloc(*bad) == 0
+
+
 def test_zero_requests_is_a_no_op():
     assert _decode(fl.full_layer(), num_seqs=0, q=None, out=None) == 0
 
