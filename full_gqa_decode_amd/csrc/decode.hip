@@ -795,6 +795,18 @@ __device__ __forceinline__ void consume_slice(Regs& r, const bf16x8 (&qop)[4], i
   acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, v_operand(r), acc, 0, 0, 0);
 }
 
+// An opaque zero that depends on three kernel arguments: adding it to the
+// address of the first table read makes the compiler read those arguments
+// before that load is issued, and not at their first use, where the wait for
+// them would also wait for every table load issued in between.  (Not
+// volatile: a volatile asm counts as a possible memory write and would turn
+// the table reads after it into vector loads.)
+__device__ __forceinline__ int zero_after(int x, float y, float z) {
+  int r;
+  asm("; zero_after %1 %2 %3" : "=s"(r) : "0"(0), "s"(x), "s"(y), "s"(z));
+  return r;
+}
+
 // Work item of slice workgroup L of a grid of units * kVSlices, units =
 // requests x KV heads.  Workgroups are dispatched to MI355X's 8 XCDs
 // round-robin (L to XCD L % 8), so XCD x runs L = x, x+8, x+16, ...: giving
@@ -808,6 +820,16 @@ __device__ __forceinline__ void vsplit_item(int L, int units, int& unit, int& js
 
 // WAVES waves; each takes the pages w, w+WAVES, ... of the range and issues
 // all of its (at most MAXP) page loads up front.
+//
+// Start-up order.  Every scalar load is issued first (this wave's page ids
+// for a request of the host-side bound max_seq_len, the request's length,
+// the slot) together with the vector loads of the small inputs.  Everything
+// that consumes those inputs -- the fp64 RoPE angle of the real position, the
+// norm of the wave's q head or of the new K row, the new V row, the q operand
+// -- runs before the wave issues its page loads: a wait for an input issued
+// before a variable number of page loads (pages are issued under per-page
+// conditions) would be compiled as a wait for every load, pages included.
+// Waves with no start-up work (kKw+2 and up) issue their pages at once.
 template <int WAVES, int MAXP, bool WINDOWED, bool FUSED, bool KV8>
 __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs a) {
   static_assert(WAVES >= kGroup, "one wave per query head of the group");
@@ -823,6 +845,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
   // fused: the new K row is normalised by wave kKw, the V row by wave kVw
   constexpr int kKw = WAVES > kGroup ? kGroup : 0;
   constexpr int kVw = WAVES > kGroup + 1 ? kGroup + 1 : 1;
+  // waves that rotate: the q heads and the K row
+  constexpr int kRotWaves = kKw + 1 > kGroup ? kKw + 1 : kGroup;
 
   __shared__ float sm_o[WAVES][kGroup][16];
   __shared__ float sm_m[WAVES][kGroup];
@@ -833,10 +857,34 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
   __shared__ __attribute__((aligned(16))) Elem sm_vnew[16];
   __shared__ int sm_fused_bad;
 
-  // ---- loads that do not wait for seq_len (as in decode_split_kernel) ----
-  float x0 = 0.f, x1 = 0.f;
-  float qw0 = 0.f, qw1 = 0.f, kw0 = 0.f, kw1 = 0.f, xk0 = 0.f, xk1 = 0.f, xv0 = 0.f, xv1 = 0.f;
-  int slot_pre = 0, pg_last_pre = -1;
+  const int use_rope = a.use_rope;
+  const float theta = a.rope_theta;
+  const float eps = a.rms_eps;
+  // ---- scalar loads: page ids, the length, the slot ----------------------
+  auto range = [&](int tt, int& lo_, int& pb, int& pe) {
+    lo_ = WINDOWED ? max(0, tt - a.window + 1) : 0;
+    pb = lo_ / kPage;
+    pe = tt / kPage + 1;
+  };
+  int lo, p_begin, p_end;
+  range(a.max_seq_len - 1, lo, p_begin, p_end);
+  const int* bt_row =
+      a.block_tables + (int64_t)b * a.bt_stride + zero_after(use_rope, theta, eps);
+  int ids[MAXP];
+  auto read_ids = [&] {  // unconditional reads, clamped into the range
+#pragma unroll
+    for (int k = 0; k < MAXP; ++k) ids[k] = bt_row[min(p_begin + w + k * WAVES, p_end - 1)];
+  };
+  read_ids();
+  const int seq_len = a.seq_lens[b];
+  int slot = 0, pg_last_raw = -1;
+  if (FUSED) {
+    slot = a.slots[b];
+    pg_last_raw = bt_row[(a.max_seq_len - 1) / kPage];
+  }
+  // ---- vector loads of the small inputs (unconditional, clamped head) -----
+  float x0 = 0.f, x1 = 0.f, qw0 = 0.f, qw1 = 0.f;
+  float xk0 = 0.f, xk1 = 0.f, kw0 = 0.f, kw1 = 0.f, xv0 = 0.f, xv1 = 0.f;
   f32x4 qraw[8];
   if (FUSED) {
     const int hh = min(w, kGroup - 1);
@@ -847,14 +895,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
     qw1 = a.q_w[lane + 64];
     const float* xk = a.k_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
     const float* xv = a.v_in + ((int64_t)b * a.num_kv_heads + g) * kHeadDim;
-    kw0 = a.k_w[lane];
-    kw1 = a.k_w[lane + 64];
     xk0 = xk[lane];
     xk1 = xk[lane + 64];
+    kw0 = a.k_w[lane];
+    kw1 = a.k_w[lane + 64];
     xv0 = xv[lane];
     xv1 = xv[lane + 64];
-    slot_pre = a.slots[b];
-    pg_last_pre = page_id(a, b, (a.max_seq_len - 1) / kPage);
   } else {
     const float* qh = a.q + ((int64_t)b * hq + g * kGroup + (n & 7)) * kHeadDim;
 #pragma unroll
@@ -863,93 +909,80 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
       qraw[2 * c + 1] = *(const f32x4*)(qh + kdim<KV8>(c, gq, 4));
     }
   }
-  auto range = [&](int tt, int& lo_, int& pb, int& pe) {
-    lo_ = WINDOWED ? max(0, tt - a.window + 1) : 0;
-    pb = lo_ / kPage;
-    pe = tt / kPage + 1;
-  };
-  int lo, p_begin, p_end;
-  range(a.max_seq_len - 1, lo, p_begin, p_end);
-  Raw r[MAXP];
-  int bad = 0;
-  auto issue = [&](int k) {
-    const int p = p_begin + w + k * WAVES;
-    if (p < p_end) {
-      int pg = page_id(a, b, p);
-      bad |= pg < 0;
-      pg = max(pg, 0);
-      load_slice(a, pg, g, n, gq, js, r[k]);
-    }
-  };
-#pragma unroll
-  for (int k = 0; k < MAXP; ++k) issue(k);
-  double cs = 1.0, sn = 0.0;
-  if (FUSED && a.use_rope) rope_cos_sin(a.max_seq_len - 1, lane, a.rope_theta, &cs, &sn);
 
-  // ---- the request's real length ------------------------------------------
-  const int seq_len = a.seq_lens[b];
-  const bool len_bad = seq_len < 1 || seq_len > a.max_seq_len;
-  const int t = seq_len - 1;
-  if (!len_bad && seq_len != a.max_seq_len) {
-    range(t, lo, p_begin, p_end);
-    bad = 0;
+  // fused, rotating layers: the angle of the speculated position, while the
+  // loads above are in flight (waves that rotate: the q heads and the K row)
+  double cs = 1.0, sn = 0.0;
+  __builtin_amdgcn_sched_barrier(0);
+  if (FUSED && use_rope && w < kRotWaves) rope_cos_sin(a.max_seq_len - 1, lane, theta, &cs, &sn);
+  __builtin_amdgcn_sched_barrier(0);
+  // one wait for every scalar value, before any branch on them (loads only
+  // one side of a branch needs would otherwise be moved past it and issued
+  // one round trip later)
+  asm volatile("" ::"s"(seq_len), "s"(slot), "s"(pg_last_raw));
 #pragma unroll
-    for (int k = 0; k < MAXP; ++k) issue(k);
-  }
-  if (len_bad) {
-    if (tid < kGroup * 16)
-      a.out[((int64_t)b * hq + g * kGroup + (tid >> 4)) * kHeadDim + js * 16 + (tid & 15)] =
-          __builtin_nanf("");
-    return;
+  for (int k = 0; k < MAXP; ++k) asm volatile("" ::"s"(ids[k]));
+
+  // ---- the request's length ------------------------------------------------
+  // A length outside [1, max_seq_len] runs the speculated range and writes
+  // NaN outputs and no cache row (no early exit: see above).
+  const bool len_bad = seq_len < 1 || seq_len > a.max_seq_len;
+  const int t = len_bad ? a.max_seq_len - 1 : seq_len - 1;
+  if (t != a.max_seq_len - 1) {  // shorter request: the real pages and angle
+    range(t, lo, p_begin, p_end);
+    read_ids();
+    if (FUSED) pg_last_raw = bt_row[t / kPage];
+    if (FUSED && use_rope && w < kRotWaves) rope_cos_sin(t, lane, theta, &cs, &sn);
   }
   const int last_page = t / kPage;
   const int tr = t % kPage;
 
-  // ---- q operand (and, fused, the new token) ------------------------------
+  // ---- start-up work: q operand and, fused, the new token ------------------
   bf16x8 qop[4];
   if (FUSED) {
-    if (a.use_rope && t != a.max_seq_len - 1) rope_cos_sin(t, lane, a.rope_theta, &cs, &sn);
-    if (w < kGroup) {
-      double y0, y1;
-      norm_rope_head(x0, x1, qw0, qw1, a.rms_eps, a.use_rope, cs, sn, &y0, &y1);
-      sm_q[w][lane] = (float)y0;
-      sm_q[w][lane + 64] = (float)y1;
-      if (js == 0 && a.q_out) {
-        float* qo = a.q_out + ((int64_t)b * hq + g * kGroup + w) * kHeadDim;
-        qo[lane] = (float)y0;
-        qo[lane + 64] = (float)y1;
-      }
-    }
+    const int pg = (pg_last_raw >= 0 && pg_last_raw < a.num_blocks) ? pg_last_raw : -1;
     // the slot must be where the page table puts position t; only slice 0
     // writes the cache, every slice substitutes the new row in registers
-    const int pg = t == a.max_seq_len - 1 ? pg_last_pre : page_id(a, b, last_page);
-    const bool ok = pg >= 0 && slot_pre == pg * kPage + tr;
+    const bool ok = pg >= 0 && slot == pg * kPage + tr && !len_bad;
     const bool write = ok && js == 0;
-    if (w == kKw) {
-      double y0, y1;
-      norm_rope_head(xk0, xk1, kw0, kw1, a.rms_eps, a.use_rope, cs, sn, &y0, &y1);
-      const int64_t o = ((int64_t)max(pg, 0) * a.num_kv_heads + g) * (kPage * kHeadDim);
-      if (KV8) {
-        const uint32_t c0 = fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
-        const uint32_t c1 = fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
-        sm_knew[lane] = (Elem)c0;
-        sm_knew[lane + 64] = (Elem)c1;
-        if (write) {
-          uint8_t* dst = (uint8_t*)a.k_cache + o;
-          dst[fp8_k_off(tr, lane)] = (uint8_t)c0;
-          dst[fp8_k_off(tr, lane + 64)] = (uint8_t)c1;
-        }
-      } else {
-        const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
-        sm_knew[lane] = (Elem)k0;
-        sm_knew[lane + 64] = (Elem)k1;
-        if (write) {
-          uint16_t* dst = (uint16_t*)a.k_cache + o;
-          dst[bf16_k_off(tr, lane)] = k0;
-          dst[bf16_k_off(tr, lane + 64)] = k1;
+    if (w < kRotWaves) {
+      if (w < kGroup) {
+        double y0, y1;
+        norm_rope_head(x0, x1, qw0, qw1, eps, use_rope, cs, sn, &y0, &y1);
+        sm_q[w][lane] = (float)y0;
+        sm_q[w][lane + 64] = (float)y1;
+        if (js == 0 && a.q_out) {
+          float* qo = a.q_out + ((int64_t)b * hq + g * kGroup + w) * kHeadDim;
+          qo[lane] = (float)y0;
+          qo[lane + 64] = (float)y1;
         }
       }
-      if (lane == 0) sm_fused_bad = !ok;
+      if (w == kKw) {
+        double y0, y1;
+        norm_rope_head(xk0, xk1, kw0, kw1, eps, use_rope, cs, sn, &y0, &y1);
+        const int64_t o = ((int64_t)max(pg, 0) * a.num_kv_heads + g) * (kPage * kHeadDim);
+        if (KV8) {
+          const uint32_t c0 = fp8_e4m3_rne_f64(y0 / (double)a.k_scale);
+          const uint32_t c1 = fp8_e4m3_rne_f64(y1 / (double)a.k_scale);
+          sm_knew[lane] = (Elem)c0;
+          sm_knew[lane + 64] = (Elem)c1;
+          if (write) {
+            uint8_t* dst = (uint8_t*)a.k_cache + o;
+            dst[fp8_k_off(tr, lane)] = (uint8_t)c0;
+            dst[fp8_k_off(tr, lane + 64)] = (uint8_t)c1;
+          }
+        } else {
+          const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
+          sm_knew[lane] = (Elem)k0;
+          sm_knew[lane + 64] = (Elem)k1;
+          if (write) {
+            uint16_t* dst = (uint16_t*)a.k_cache + o;
+            dst[bf16_k_off(tr, lane)] = k0;
+            dst[bf16_k_off(tr, lane + 64)] = k1;
+          }
+        }
+        if (lane == 0) sm_fused_bad = !ok;
+      }
     }
     if (w == kVw) {
       const int64_t o = ((int64_t)max(pg, 0) * a.num_kv_heads + g) * (kHeadDim * kPage);
@@ -976,20 +1009,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
       const int d = lane - (js & 3) * 16;
       if (d >= 0 && d < 16) sm_vnew[d] = (Elem)((js >> 2) ? c1 : c0);
     }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float* qh = &sm_q[n & 7][kdim<KV8>(c, gq, 0)];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const f32x2 v = {qh[j] * a.qscale, qh[j + 1] * a.qscale};
-        const bf16x2 hi = __builtin_convertvector(v, bf16x2);
-        const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
-        const bf16x2 sel = (n < 8) ? hi : lo2;
-        qop[c][j] = sel[0];
-        qop[c][j + 1] = sel[1];
-      }
-    }
   } else {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -998,6 +1017,34 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
         const f32x2 v = {xs[j] * a.qscale, xs[j + 1] * a.qscale};
+        const bf16x2 hi = __builtin_convertvector(v, bf16x2);
+        const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
+        const bf16x2 sel = (n < 8) ? hi : lo2;
+        qop[c][j] = sel[0];
+        qop[c][j + 1] = sel[1];
+      }
+    }
+  }
+
+  // ---- page loads ------------------------------------------------------------
+  Raw r[MAXP];
+  int bad = len_bad;
+#pragma unroll
+  for (int k = 0; k < MAXP; ++k) {
+    if (p_begin + w + k * WAVES < p_end) {
+      const bool ok = ids[k] >= 0 && ids[k] < a.num_blocks;
+      bad |= !ok;
+      load_slice(a, ok ? ids[k] : 0, g, n, gq, js, r[k]);
+    }
+  }
+  if (FUSED) {
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float* qh = &sm_q[n & 7][kdim<KV8>(c, gq, 0)];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const f32x2 v = {qh[j] * a.qscale, qh[j + 1] * a.qscale};
         const bf16x2 hi = __builtin_convertvector(v, bf16x2);
         const bf16x2 lo2 = __builtin_convertvector(v - __builtin_convertvector(hi, f32x2), bf16x2);
         const bf16x2 sel = (n < 8) ? hi : lo2;
