@@ -118,6 +118,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads' legs (single-layer latency of a full layer at "
+                         "4096 tokens and a sliding layer at 32768, 64 ragged requests, batches "
+                         "of 2..16 at 100K context)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only run the prefill leg (for counter runs of the prefill kernel)")
     ap.add_argument("--batch-legs", action="store_true",
@@ -350,6 +354,9 @@ def main():
     if not args.no_moe:
         result["moe"] = bench_moe(fl, dev, capture, stream)
 
+    if not args.no_configs:
+        result["configs"] = bench_configs(fl, dev)
+
     if not args.no_prefill:
         result["prefill"] = bench_prefill(fl, dev, stream)
 
@@ -512,19 +519,105 @@ def _time_launches(fn, reps=10, warm=3):
 
 
 def bench_batches(fl, dev):
-    """Batched decode.  (1) 64 requests with lengths uniform in [1024, 131072]
-    (seeded), pages in one random physical order, one full and one sliding
-    layer, flint_attn_decode (K2 + K3) on a normalised q; algorithmic bytes
-    from the drawn lengths.  (2) B = 2, 4, 8, 16 requests at 100K context,
-    one fused step of a full layer (bf16 and fp8 cache) and of a sliding
-    layer each, in a graph of 6 (full) or 20 (sliding) distinct layers so that no layer's pages stay in
-    the caches between replays."""
+    """Batched decode: the 64 ragged requests and the small batches at 100K
+    context (bench_ragged_64, bench_small_batches), as one JSON object."""
+    return {"workload": "batched decode: 64 ragged requests (1024..131072 tokens) on one full "
+                        "and one sliding layer; batches of 2..16 at 100K context (fused step; "
+                        "full layers over a bf16 and an fp8 cache, sliding over bf16)",
+            "unit": "us", "peak_gbps": HBM_PEAK_GBPS, "ragged_64": bench_ragged_64(fl, dev),
+            "small_batches_100k": bench_small_batches(fl, dev)}
+
+
+def bench_configs(fl, dev):
+    """The other workloads, each timed in its own graph or launch loop: one
+    full layer at 4096 tokens and one sliding layer at 32768 tokens (single-
+    layer latency), 64 ragged requests of 1024..131072 tokens, and batches of
+    2..16 requests at 100K context."""
+    out = bench_single_layers(fl, dev)
+    out["ragged_64"] = bench_ragged_64(fl, dev)
+    out["small_batches_100k"] = bench_small_batches(fl, dev, sizes=(2, 4, 8))
+    return out
+
+
+SINGLE_LAYER_ROTATION_BYTES = 512 << 20
+
+
+def bench_single_layers(fl, dev):
+    """One decode step of one layer at batch 1: a full (NoPE) layer over a
+    4096-token context and a sliding (RoPE, 513-key) layer at a 32768-token
+    context, each the fused step (norm/RoPE/append of the new token, then
+    attention).  A layer's pages (8.4 MB / 1.05 MB) fit the 256 MB last-level
+    cache, so each graph cycles through enough distinct copies -- their own
+    caches, page tables and token inputs -- to touch more than 512 MB per
+    replay: every step reads its pages from HBM."""
+    import torch
+    eps = float(np.float32(1e-6))
+    stream = torch.cuda.Stream()
+    res = {}
+    for name, ctx, window in (("full_layer_ctx4096", 4096, 0), ("sliding_layer_ctx32768", 32768,
+                                                                 WINDOW)):
+        L = fl.layer(window=window, use_rope=1 if window else 0, rms_eps=eps)
+        pages = ctx // PAGE
+        t = ctx - 1
+        kv_bytes = min(ctx, window or ctx) * KV_BYTES_PER_TOKEN_LAYER
+        copies = -(-SINGLE_LAYER_ROTATION_BYTES // kv_bytes)
+        tabs, nb0 = [], 0
+        for c in range(copies):
+            if window:
+                bt, nb = synth.ring_block_table(SEED, (5, ctx, c, synth.PERM), 1, pages, RING, pages)
+            else:
+                bt, nb = synth.shuffled_block_table(SEED, (5, ctx, c, synth.PERM), 1, [pages],
+                                                    pages)
+            tabs.append(np.where(bt >= 0, bt + c * nb, -1).astype(np.int32))
+            nb0 = nb
+        kc = synth.normal_bf16_bits_torch(SEED, (5, ctx, synth.KC), (copies * nb0, HKV, PAGE, D), dev)
+        vc = synth.normal_bf16_bits_torch(SEED, (5, ctx, synth.VC), (copies * nb0, HKV, D, PAGE), dev)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        bts = [up(b) for b in tabs]
+        slots = [up(np.array([int(b[0, t // PAGE]) * PAGE + t % PAGE], np.int32)) for b in tabs]
+        q = up(synth.normal(SEED, (5, ctx, synth.Q), (copies, 1, HQ, D)))
+        k = up(synth.normal(SEED, (5, ctx, synth.K), (copies, 1, HKV, D)))
+        v = up(synth.normal(SEED, (5, ctx, synth.V), (copies, 1, HKV, D)))
+        sinks = up(synth.normal(SEED, (5, ctx, synth.SINK), HQ))
+        ones = torch.ones(D, dtype=torch.float32, device=dev)
+        sl = torch.tensor([ctx], dtype=torch.int32, device=dev)
+        out = torch.empty((copies, 1, HQ, D), dtype=torch.float32, device=dev)
+        ws = torch.zeros(max(fl.flint_attn_decode_workspace_size(L, 1, ctx), 256), dtype=torch.uint8,
+                         device=dev)
+
+        def run():
+            for c in range(copies):
+                fl.flint_attn_decode_step(L, q[c], k[c], v[c], ones, ones, slots[c], kc, vc, bts[c],
+                                          sl, ctx, sinks, out[c], workspace=ws)
+        run()
+        torch.cuda.synchronize()
+        finite = bool(torch.isfinite(out).all())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                run()
+            us = _time_launches(g.replay, reps=10) / copies
+        nbytes = kv_bytes + HQ * D * 4 * 2 + HKV * D * 4 * 2 + HQ * 4 + (pages if not window
+                                                                         else RING) * 4
+        gbps = nbytes / us / 1e3
+        res[name] = {"us_per_step": round(us, 2), "bytes_per_step": nbytes,
+                     "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "copies_cycled": copies, "plan": list(fl.flint_attn_decode_plan(L, 1, ctx)),
+                     "finite": finite}
+        log(f"bench: one {name} step {us:.2f} us ({gbps:.0f} GB/s), {copies} copies cycled")
+        del kc, vc, g
+        torch.cuda.empty_cache()
+    return res
+
+
+def bench_ragged_64(fl, dev):
+    """64 requests with lengths uniform in [1024, 131072] (seeded), pages in one
+    random physical order, one full and one sliding layer, flint_attn_decode
+    on a normalised q; algorithmic bytes from the drawn lengths."""
     import torch
     eps = float(np.float32(1e-6))
     FULL = fl.layer(window=0, use_rope=0, rms_eps=eps)
     SLIDE = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps)
-    res = {}
-    # (1) config: 64 ragged requests
     B = 64
     lens = synth.uniform_ints(SEED, (3, 1), B, 1024, 131072).astype(np.int32)
     maxlen = int(lens.max())
@@ -558,8 +651,19 @@ def bench_batches(fl, dev):
         log(f"bench: 64 ragged requests, {kind} layer: {us:.1f} us, {kv_bytes / 1e9:.3f} GB, "
             f"{kv_bytes / us / 1e3:.0f} GB/s")
         del kc, vc
-    res["ragged_64"] = ragged
-    # (2) small batches at 100K context, fused step in a graph
+    torch.cuda.empty_cache()
+    return ragged
+
+
+def bench_small_batches(fl, dev, sizes=(2, 4, 8, 16)):
+    """B = 2, 4, 8, 16 (or `sizes`) requests at 100K context, one fused step of a full
+    layer (bf16 and fp8 cache) and of a sliding layer each, in a graph of 6
+    (full) or 20 (sliding) distinct layers so that no layer's pages stay in
+    the caches between replays."""
+    import torch
+    eps = float(np.float32(1e-6))
+    FULL = fl.layer(window=0, use_rope=0, rms_eps=eps)
+    SLIDE = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps)
     ones = torch.ones(D, dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
     small = {}
@@ -567,7 +671,7 @@ def bench_batches(fl, dev):
     t = CTX - 1
     FULL8 = fl.layer(window=0, use_rope=0, rms_eps=eps, kv_dtype=fl.FLINT_KV_FP8_E4M3,
                      k_scale=FP8_SCALES[0], v_scale=FP8_SCALES[1])
-    for Bs in (2, 4, 8, 16):
+    for Bs in sizes:
         row = {}
         for kind, L in (("full", FULL), ("sliding", SLIDE), ("full_fp8", FULL8)):
             nlay = 20 if kind == "sliding" else 6
@@ -624,11 +728,7 @@ def bench_batches(fl, dev):
             f"({row['full']['gbps']:.0f} GB/s), sliding layer {row['sliding']['us_per_layer']:.2f} us, "
             f"fp8 full layer {row['full_fp8']['us_per_layer']:.1f} us "
             f"({row['full_fp8']['gbps']:.0f} GB/s)")
-    res["small_batches_100k"] = small
-    return {"workload": "batched decode: 64 ragged requests (1024..131072 tokens) on one full "
-                        "and one sliding layer; batches of 2..16 at 100K context (fused step; "
-                        "full layers over a bf16 and an fp8 cache, sliding over bf16)",
-            "unit": "us", "peak_gbps": HBM_PEAK_GBPS, **res}
+    return small
 
 
 def copy_probe(dev):

@@ -21,14 +21,28 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library (always rebuilds)."""
-    tmp = SO + ".tmp"
+# The host half of the library built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (build(sanitize=True)): every flag reaches the
+# host compilation only, so the gfx950 code is built exactly as in the
+# product.  A process loads it with clang's ASan runtime preloaded.
+SO_SANITIZED = os.path.join(HERE, "libflint_san.so")
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host",
+                       "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every HIP source into one shared library (always rebuilds);
+    sanitize=True builds libflint_san.so with sanitized host code instead."""
+    so = SO_SANITIZED if sanitize else SO
+    tmp = so + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-result",
            # packed fp32 VALU ops stay off: ordinary float code only
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-o", tmp]
+    if sanitize:
+        cmd += HOST_SANITIZE_FLAGS
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     r = subprocess.run(cmd, cwd=HERE, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -37,9 +51,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, SO)
-    return SO
+    os.replace(tmp, so)
+    return so
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv))

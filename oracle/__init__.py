@@ -18,21 +18,29 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SO = os.path.join(HERE, "liboracle.so")
+# the same sources built with AddressSanitizer and UndefinedBehaviorSanitizer
+# (build(sanitize=True)); a process loads it with gcc's libasan preloaded
+SO_SANITIZED = os.path.join(HERE, "liboracle_san.so")
 SRC = os.path.join(HERE, "oracle.c")
 SRCS = [SRC, os.path.join(HERE, "moe.c")]
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
 
 
-def build(force: bool = True) -> str:
+def build(force: bool = True, sanitize: bool = False) -> str:
     """Compile oracle.c into liboracle.so with gcc (OpenMP for the
-    independent per-(query, head) work items)."""
-    if not force and os.path.exists(SO) and all(os.path.getmtime(SO) >= os.path.getmtime(f)
+    independent per-(query, head) work items); sanitize=True builds
+    liboracle_san.so with ASan and UBSan instead."""
+    so = SO_SANITIZED if sanitize else SO
+    if not force and os.path.exists(so) and all(os.path.getmtime(so) >= os.path.getmtime(f)
                                                  for f in SRCS):
-        return SO
-    tmp = SO + ".tmp"
+        return so
+    tmp = so + ".tmp"
+    extra = SANITIZE_FLAGS if sanitize else []
     subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
-                           "-Wall", "-Werror", "-o", tmp, *SRCS, "-lm"], cwd=HERE)
-    os.replace(tmp, SO)
-    return SO
+                           "-Wall", "-Werror", *extra, "-o", tmp, *SRCS, "-lm"], cwd=HERE)
+    os.replace(tmp, so)
+    return so
 
 
 class Layer(C.Structure):
