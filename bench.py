@@ -356,6 +356,7 @@ def main():
 
     if not args.no_configs:
         result["configs"] = bench_configs(fl, dev)
+        result["ceilings"] = bench_ceilings(dev)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(fl, dev, stream)
@@ -729,6 +730,40 @@ def bench_small_batches(fl, dev, sizes=(2, 4, 8, 16)):
             f"fp8 full layer {row['full_fp8']['us_per_layer']:.1f} us "
             f"({row['full_fp8']['gbps']:.0f} GB/s)")
     return small
+
+
+def bench_ceilings(dev):
+    """Reference rates of the box, measured with torch's own kernels (not the
+    library's): the cost of one kernel launch inside a HIP graph (one-element
+    adds back to back), and the rate of a plain device-to-device copy of
+    204.8 MB buffers (a full layer's K/V bytes), counted as bytes read plus
+    bytes written, 14 distinct buffers back to back."""
+    import torch
+    stream = torch.cuda.Stream()
+    x = torch.zeros(64, device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(35):
+                x[i:i + 1].add_(1.0)
+        us_launch = _time_launches(g.replay, reps=20) / 35
+    nbytes = CTX * KV_BYTES_PER_TOKEN_LAYER
+    src = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(14)]
+    dst = [torch.empty_like(x) for x in src]
+
+    def copy_all():
+        for a, b in zip(dst, src):
+            a.copy_(b)
+    us_copy = _time_launches(copy_all, reps=5) / len(src)
+    gbps = 2 * nbytes / us_copy / 1e3
+    log(f"bench: graph launch floor {us_launch:.2f} us; copy of 204.8 MB {us_copy:.1f} us "
+        f"({gbps:.0f} GB/s read + write)")
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"graph_launch_us": round(us_launch, 3),
+            "copy_204_8MB_us": round(us_copy, 2), "copy_gbps_read_plus_write": round(gbps, 1),
+            "copy_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "kernels": "torch one-element add in a graph (launch); torch copy_ (copy)"}
 
 
 def copy_probe(dev):
