@@ -290,16 +290,16 @@ constexpr int kAhead8 = 2;
 constexpr int kComputeUnits = 256;
 
 // Launch bounds: MINW, the least waves per SIMD.  fp8 split kernels are held
-// to 4 (128 VGPRs) by default so that two workgroups share a CU; a fused fp8
-// launch of at most one workgroup per CU takes MINW = 2 instead, which keeps
-// its fp64 prologue out of scratch (measured: the batch-1 fp8 step 687-693
-// -> 669-670 us).
+// to 4 (128 VGPRs) by default so that two workgroups share a CU; an fp8
+// launch of at most one workgroup per CU takes MINW = 2 instead, which holds
+// a two-page ring and keeps the fused fp64 prologue out of scratch.
 template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED, bool KV8,
           int MINW = (MAXP > 1 ? 1 : (KV8 ? 4 : 2))>
 __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeArgs a) {
   constexpr int kThreads = WAVES * 64;
-  // page buffers per wave
-  constexpr int NR = MAXP > 1 ? MAXP : (KV8 ? kAhead8 : 1);
+  // page buffers per wave (fp8 at two workgroups per CU: one, which fits the
+  // 128-VGPR bound without spilling; the CU then holds 16 waves of loads)
+  constexpr int NR = MAXP > 1 ? MAXP : ((KV8 && MINW < 4) ? kAhead8 : 1);
   using Raw = typename std::conditional<KV8, PageRaw8, PageRegs>::type;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -539,56 +539,54 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
         consume_page(r[k], qop, p, lo, t, n, gq, st, nothing);
       }
     }
-  } else if constexpr (KV8) {
-    // fp8: a ring of NR page buffers; buffer k is consumed and refilled with
-    // the page NR rounds later (K once the score MFMAs have read it, V after
-    // the value MFMAs).  Page ids run one more round ahead of those loads.
+  } else {
+    // The pipelined loop.  A ring of NR page buffers per wave (NR = 1 for
+    // bf16): buffer k is consumed and refilled with the page NR rounds later,
+    // K as soon as the score MFMAs have read it, V after the value MFMAs.
+    // Raw page ids are read one more round ahead, at an index clamped into
+    // the split, and checked when their loads are issued.
+    //
+    // Inside the main loop every load is unconditional: the pages that have
+    // no page NR rounds later are peeled off into the tail below.  A load
+    // under a branch would make the compiler's wait at the loop head count
+    // the path that skipped it, and so wait for the current page's V before
+    // its score MFMAs; the same holds for a page-id read that is checked
+    // right away.
+    const int64_t row = (int64_t)b * a.bt_stride;
+    const int last_in_split = p_end - 1;
+    int p = p_begin + w;
+    const int n_mine = p < p_end ? (p_end - 1 - p) / WAVES + 1 : 0;
     int ids[NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int pn = p_begin + w + (NR + k) * WAVES;
-      ids[k] = pn < p_end ? page_id(a, b, pn) : 0;
-    }
-    for (int p0 = p_begin + w; p0 < p_end; p0 += NR * WAVES) {
+    for (int k = 0; k < NR; ++k)
+      ids[k] = a.block_tables[row + min(p + (NR + k) * WAVES, last_in_split)];
+    auto step = [&](int k, int pp, bool load_next) {
+      const int raw = ids[k];
+      const bool ok = raw >= 0 && raw < a.num_blocks;
+      const int pg_next = ok ? raw : 0;
+      if (load_next) {
+        bad |= !ok;
+        ids[k] = a.block_tables[row + min(pp + 2 * NR * WAVES, last_in_split)];
+      }
+      if (FUSED && pp == last_page) substitute_new_token(r[k], sm_knew, sm_vnew, tr, n, gq);
+      consume_page(r[k], qop, pp, lo, t, n, gq, st, [&] {
+        if (load_next) load_k(a, pg_next, g, n, gq, r[k]);
+      });
+      if (load_next) load_v(a, pg_next, g, n, gq, r[k]);
+    };
+    int i = 0;
+    for (; i + 2 * NR <= n_mine; i += NR) {
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        const int p = p0 + k * WAVES;
-        if (p < p_end) {
-          const int pn = p + NR * WAVES;
-          const bool has_next = pn < p_end;
-          bad |= has_next && ids[k] < 0;
-          const int pg_next = max(ids[k], 0);
-          if (has_next) {
-            const int pa = pn + NR * WAVES;
-            ids[k] = pa < p_end ? page_id(a, b, pa) : 0;
-          }
-          if (FUSED && p == last_page) substitute_new_token(r[k], sm_knew, sm_vnew, tr, n, gq);
-          consume_page(r[k], qop, p, lo, t, n, gq, st, [&] {
-            if (has_next) load_k(a, pg_next, g, n, gq, r[k]);
-          });
-          if (has_next) load_v(a, pg_next, g, n, gq, r[k]);
-        }
-      }
+      for (int k = 0; k < NR; ++k) step(k, p + k * WAVES, true);
+      p += NR * WAVES;
     }
-  } else {
-    // page ids run one page ahead of the loads, the loads one page ahead of the
-    // math: K of the next page is requested as soon as the score MFMAs have
-    // consumed this page's K, V of the next page after the value MFMAs
-    int p = p_begin + w;
-    if (p < p_end) {
-      int pg_ahead = (p + WAVES < p_end) ? page_id(a, b, p + WAVES) : 0;
-      for (; p < p_end; p += WAVES) {
-        const bool has_next = p + WAVES < p_end;
-        bad |= pg_ahead < 0;
-        const int pg_next = max(pg_ahead, 0);
-        if (p + 2 * WAVES < p_end) pg_ahead = page_id(a, b, p + 2 * WAVES);
-        if (FUSED && p == last_page) substitute_new_token(r[0], sm_knew, sm_vnew, tr, n, gq);
-        consume_page(r[0], qop, p, lo, t, n, gq, st, [&] {
-          if (has_next) load_k(a, pg_next, g, n, gq, r[0]);
-        });
-        if (has_next) load_v(a, pg_next, g, n, gq, r[0]);
-      }
-    }
+    // tail: the last n_mine - i (< 2 NR) pages
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+      if (i + k < n_mine) step(k, p + k * WAVES, i + k + NR < n_mine);
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+      if (i + NR + k < n_mine) step(k, p + (NR + k) * WAVES, false);
   }
 
   // ---- per-wave state -> LDS -> this split's result -----------------------
@@ -1309,9 +1307,17 @@ template <bool FUSED, bool KV8>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
   const bool win = a.window > 0;
+  const bool one_round = (int64_t)grid.x * grid.y * grid.z <= kComputeUnits;
   if (!FUSED && a.partials_only) {  // every split's partial, whatever the count
     constexpr int W = kDecodeWaves;
-    if (win)
+    if (KV8 && one_round) {  // fp8, at most one workgroup per CU: the two-page ring
+      if (win)
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8, 2>), grid,
+                           dim3(W * 64), 0, st, a);
+      else
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false, KV8, 2>), grid,
+                           dim3(W * 64), 0, st, a);
+    } else if (win)
       hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8>), grid, dim3(W * 64),
                          0, st, a);
     else
@@ -1345,9 +1351,9 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   constexpr int W = kDecodeWaves;
-  // fused fp8 with at most one workgroup per CU: the looser register bound
-  constexpr int MW = (FUSED && KV8) ? 2 : (KV8 ? 4 : 2);
-  const bool loose = FUSED && KV8 && (int64_t)grid.x * grid.y * grid.z <= kComputeUnits;
+  // fp8 with at most one workgroup per CU: the looser register bound
+  constexpr int MW = 2;
+  const bool loose = KV8 && one_round;
   if (a.num_splits == 1) {  // one long split: pipelined loop, sink folded in
     if (loose) {
       if (win)
