@@ -274,9 +274,10 @@ __device__ __forceinline__ void substitute_new_token(PageRaw8& r, const uint8_t*
 // range, so the sink is folded in here and the output written directly.
 // FUSED: also the norm/RoPE of q and the append of the new token.  KV8: the
 // cache holds fp8 codes, widened to bf16 operand by operand (exact); k_scale
-// rides in qscale and v_scale multiplies the result, and a wave keeps kAhead8
-// pages of loads in flight (a 4 KiB page needs more pages in flight per wave
-// than an 8 KiB one for the same bytes in flight).
+// rides in qscale and v_scale multiplies the result.  In the pipelined loop a
+// wave keeps kAhead pages of loads in flight at one workgroup per CU, so that
+// its compute between a page's arrival and the next request does not leave
+// the load path idle.
 //
 // Start-up latency: the first loads (q, the first page ids and their K/V) are
 // issued before seq_lens[b] has arrived, for the key range of a request of
@@ -284,22 +285,25 @@ __device__ __forceinline__ void substitute_new_token(PageRaw8& r, const uint8_t*
 // known they are kept if it equals that bound and reissued otherwise.  Every
 // speculative page id is read inside the caller's block-table row and
 // validated before it addresses the cache.
-constexpr int kAhead8 = 2;
+constexpr int kAhead = 2;
 // MI355X's compute units: a grid of at most this many workgroups runs as one
 // round at one workgroup per CU.
 constexpr int kComputeUnits = 256;
 
-// Launch bounds: MINW, the least waves per SIMD.  fp8 split kernels are held
-// to 4 (128 VGPRs) by default so that two workgroups share a CU; an fp8
-// launch of at most one workgroup per CU takes MINW = 2 instead, which holds
-// a two-page ring and keeps the fused fp64 prologue out of scratch.
+// Launch bounds: MINW, the least waves per SIMD (fp8 kernels are held to 4,
+// 128 VGPRs, so that two workgroups share a CU).  RING: pages in flight per
+// wave in the pipelined loop.  A launch of at most one workgroup per CU takes
+// MINW = 2 and RING = kAhead: the loads alone stream at ~6.4 TB/s in this
+// shape, and one page per wave left the split kernel short of that, since
+// the wave's math between a page's arrival and its next request leaves the
+// load path idle.  Grids of several rounds keep RING = 1, whose smaller
+// register file lets workgroups share a CU.
 template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED, bool KV8,
-          int MINW = (MAXP > 1 ? 1 : (KV8 ? 4 : 2))>
+          int MINW = (MAXP > 1 ? 1 : (KV8 ? 4 : 2)), int RING = 1>
 __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeArgs a) {
   constexpr int kThreads = WAVES * 64;
-  // page buffers per wave (fp8 at two workgroups per CU: one, which fits the
-  // 128-VGPR bound without spilling; the CU then holds 16 waves of loads)
-  constexpr int NR = MAXP > 1 ? MAXP : ((KV8 && MINW < 4) ? kAhead8 : 1);
+  // page buffers per wave
+  constexpr int NR = MAXP > 1 ? MAXP : RING;
   using Raw = typename std::conditional<KV8, PageRaw8, PageRegs>::type;
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -540,8 +544,7 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
       }
     }
   } else {
-    // The pipelined loop.  A ring of NR page buffers per wave (NR = 1 for
-    // bf16): buffer k is consumed and refilled with the page NR rounds later,
+    // The pipelined loop.  A ring of NR page buffers per wave: buffer k is consumed and refilled with the page NR rounds later,
     // K as soon as the score MFMAs have read it, V after the value MFMAs.
     // Raw page ids are read one more round ahead, at an index clamped into
     // the split, and checked when their loads are issued.
@@ -574,19 +577,24 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
       });
       if (load_next) load_v(a, pg_next, g, n, gq, r[k]);
     };
-    int i = 0;
-    for (; i + 2 * NR <= n_mine; i += NR) {
+    if constexpr (NR == 1) {
+      for (int i = 1; i < n_mine; ++i, p += WAVES) step(0, p, true);
+      if (n_mine > 0) step(0, p, false);
+    } else {
+      int i = 0;
+      for (; i + 2 * NR <= n_mine; i += NR) {
 #pragma unroll
-      for (int k = 0; k < NR; ++k) step(k, p + k * WAVES, true);
-      p += NR * WAVES;
+        for (int k = 0; k < NR; ++k) step(k, p + k * WAVES, true);
+        p += NR * WAVES;
+      }
+      // tail: the last n_mine - i (< 2 NR) pages
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+        if (i + k < n_mine) step(k, p + k * WAVES, i + k + NR < n_mine);
+#pragma unroll
+      for (int k = 0; k < NR; ++k)
+        if (i + NR + k < n_mine) step(k, p + (NR + k) * WAVES, false);
     }
-    // tail: the last n_mine - i (< 2 NR) pages
-#pragma unroll
-    for (int k = 0; k < NR; ++k)
-      if (i + k < n_mine) step(k, p + k * WAVES, i + k + NR < n_mine);
-#pragma unroll
-    for (int k = 0; k < NR; ++k)
-      if (i + NR + k < n_mine) step(k, p + (NR + k) * WAVES, false);
   }
 
   // ---- per-wave state -> LDS -> this split's result -----------------------
@@ -1310,12 +1318,12 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const bool one_round = (int64_t)grid.x * grid.y * grid.z <= kComputeUnits;
   if (!FUSED && a.partials_only) {  // every split's partial, whatever the count
     constexpr int W = kDecodeWaves;
-    if (KV8 && one_round) {  // fp8, at most one workgroup per CU: the two-page ring
+    if (one_round) {  // at most one workgroup per CU: the page ring
       if (win)
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8, 2>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8, 2, kAhead>), grid,
                            dim3(W * 64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false, KV8, 2>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false, KV8, 2, kAhead>), grid,
                            dim3(W * 64), 0, st, a);
     } else if (win)
       hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8>), grid, dim3(W * 64),
@@ -1351,16 +1359,16 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   constexpr int W = kDecodeWaves;
-  // fp8 with at most one workgroup per CU: the looser register bound
+  // at most one workgroup per CU: the looser register bound
   constexpr int MW = 2;
-  const bool loose = KV8 && one_round;
+  const bool loose = one_round;
   if (a.num_splits == 1) {  // one long split: pipelined loop, sink folded in
     if (loose) {
       if (win)
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8, MW>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8, MW, kAhead>), grid,
                            dim3(W * 64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED, KV8, MW>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED, KV8, MW, kAhead>), grid,
                            dim3(W * 64), 0, st, a);
     } else if (win) {
       hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8>), grid, dim3(W * 64), 0,
@@ -1373,10 +1381,10 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   }
   if (loose) {
     if (win)
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8, MW>), grid,
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8, MW, kAhead>), grid,
                          dim3(W * 64), 0, st, a);
     else
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED, KV8, MW>), grid,
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED, KV8, MW, kAhead>), grid,
                          dim3(W * 64), 0, st, a);
   } else if (win) {
     hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8>), grid, dim3(W * 64), 0,
