@@ -128,6 +128,9 @@ def main():
                     help="only time batched decode: 64 ragged requests of 1024..131072 tokens "
                          "(one full and one sliding layer) and batches of 2..16 requests at "
                          "100K context (fused step), and print one JSON line")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only the machine-ceiling leg (launch, streaming reads, the split "
+                         "kernel's loads alone, atomics), as one JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times (the "
                          "known-size kernel that calibrates HBM byte counters) and exit")
@@ -138,6 +141,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.ceilings:
+        print(json.dumps({"ceilings": bench_ceilings(torch.device("cuda:0"))}), flush=True)
+        return
     if args.copy_probe:
         copy_probe(torch.device("cuda:0"))
         return
@@ -357,6 +363,9 @@ def main():
     if not args.no_configs:
         result["configs"] = bench_configs(fl, dev)
         result["ceilings"] = bench_ceilings(dev)
+        walk = result["ceilings"]["page_walk"]["us_per_launch"]
+        result["roofline"]["loads_alone_us"] = walk
+        result["roofline"]["frac_of_loads_alone"] = round(walk / us_k2, 4)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(fl, dev, stream)
@@ -732,23 +741,102 @@ def bench_small_batches(fl, dev, sizes=(2, 4, 8, 16)):
     return small
 
 
+def _ceiling_lib():
+    """libflint_ceiling.so: the measurement kernels of the ceilings leg."""
+    import ctypes as C
+
+    import full_gqa_decode_amd as fl
+    fl.lib()  # torch's HIP runtime first; raises if nothing was built
+    from full_gqa_decode_amd import build as fb
+    if not os.path.exists(fb.SO_CEILING):
+        raise RuntimeError(f"{fb.SO_CEILING} is missing: build it with "
+                           "`python -m full_gqa_decode_amd.build`")
+    L = C.CDLL(fb.SO_CEILING)
+    P, I = C.c_void_p, C.c_int
+    L.flint_ceiling_stream_bytes.restype = C.c_long
+    L.flint_ceiling_stream_read.argtypes = [I, I, P, P, P]
+    L.flint_ceiling_page_walk.argtypes = [P, P, P, I, I, I, P, P]
+    L.flint_ceiling_empty.argtypes = [P]
+    L.flint_ceiling_atomics.argtypes = [P, I, I, P]
+    return L
+
+
 def bench_ceilings(dev):
-    """Reference rates of the box, measured with torch's own kernels (not the
-    library's): the cost of one kernel launch inside a HIP graph (one-element
-    adds back to back), and the rate of a plain device-to-device copy of
-    204.8 MB buffers (a full layer's K/V bytes), counted as bytes read plus
-    bytes written, 14 distinct buffers back to back."""
+    """Machine ceilings the decode kernels are compared against, measured with
+    the kernels of libflint_ceiling.so (HIP graphs, events on the graph's
+    stream):
+      graph_launch_us  one empty kernel inside a graph (35 back to back);
+      stream_read      every byte of 14 distinct ~201 MB buffers, in 4 KiB
+                       chunks at pseudo-random offsets, nontemporal and
+                       ordinary loads (the access shape of a paged cache);
+      page_walk        the split-K kernel's loads alone in its own shape (64
+                       splits x 4 KV heads, 8 waves, a shuffled page table,
+                       6250 pages of 4 KiB K + 4 KiB V per head: one 100K
+                       full layer), 14 distinct layers;
+      atomics          agent-scope atomic adds on one hot counter per us;
+    plus torch's device-to-device copy of 204.8 MB (bytes read + written)."""
     import torch
+    L = _ceiling_lib()
     stream = torch.cuda.Stream()
-    x = torch.zeros(64, device=dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(g, stream=stream):
-            for i in range(35):
-                x[i:i + 1].add_(1.0)
-        us_launch = _time_launches(g.replay, reps=20) / 35
+
+    def graph_time(fn, n, reps=10):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                fn()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * n)
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("ceiling kernel launch failed")
+
+    sid = lambda: stream.cuda_stream
+    us_launch = graph_time(lambda: [ok(L.flint_ceiling_empty(sid())) for _ in range(35)], 35, 20)
+
+    nreg = 14
+    rb = L.flint_ceiling_stream_bytes()
+    buf = torch.empty(nreg * rb, dtype=torch.uint8, device=dev)
+    out = torch.empty(256 * 4 * 512, dtype=torch.int32, device=dev)
+    stream_read = {}
+    for nt in (1, 0):
+        us = graph_time(lambda: [ok(L.flint_ceiling_stream_read(4, nt, buf.data_ptr() + i * rb,
+                                                                out.data_ptr(), sid()))
+                                 for i in range(nreg)], nreg)
+        stream_read["nontemporal" if nt else "ordinary"] = {
+            "us_per_launch": round(us, 2), "gbps": round(rb / us / 1e3, 1),
+            "frac": round(rb / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    del buf
+
+    pages, heads, pps = -(-CTX // PAGE), HKV, 98
+    tb = pages * heads * 4096
+    k = [torch.empty(tb, dtype=torch.uint8, device=dev) for _ in range(nreg)]
+    v = [torch.empty(tb, dtype=torch.uint8, device=dev) for _ in range(nreg)]
+    gen = torch.Generator().manual_seed(SEED)
+    tables = [torch.randperm(pages, generator=gen).to(torch.int32).to(dev) for _ in range(nreg)]
+    us_walk = graph_time(lambda: [ok(L.flint_ceiling_page_walk(
+        k[i].data_ptr(), v[i].data_ptr(), tables[i].data_ptr(), pages, heads, pps,
+        out.data_ptr(), sid())) for i in range(nreg)], nreg)
+    walk_bytes = 2 * tb
+    del k, v
+
+    ctr = torch.zeros(1, dtype=torch.int32, device=dev)
+    wgs, per_wave = 1024, 16
+    us_atom = graph_time(lambda: ok(L.flint_ceiling_atomics(ctr.data_ptr(), wgs, per_wave, sid())),
+                         1, 5)
+    n_atom = wgs * 4 * per_wave
+    assert int(ctr.item()) == n_atom * (3 + 5), "atomic count"  # 3 warm-up + 5 timed replays
+
     nbytes = CTX * KV_BYTES_PER_TOKEN_LAYER
-    src = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(14)]
+    src = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(nreg)]
     dst = [torch.empty_like(x) for x in src]
 
     def copy_all():
@@ -756,14 +844,22 @@ def bench_ceilings(dev):
             a.copy_(b)
     us_copy = _time_launches(copy_all, reps=5) / len(src)
     gbps = 2 * nbytes / us_copy / 1e3
-    log(f"bench: graph launch floor {us_launch:.2f} us; copy of 204.8 MB {us_copy:.1f} us "
-        f"({gbps:.0f} GB/s read + write)")
     del src, dst
     torch.cuda.empty_cache()
-    return {"graph_launch_us": round(us_launch, 3),
-            "copy_204_8MB_us": round(us_copy, 2), "copy_gbps_read_plus_write": round(gbps, 1),
-            "copy_frac": round(gbps / HBM_PEAK_GBPS, 4),
-            "kernels": "torch one-element add in a graph (launch); torch copy_ (copy)"}
+    res = {"graph_launch_us": round(us_launch, 3),
+           "stream_read": dict(stream_read, bytes_per_launch=rb, chunk_kib=4),
+           "page_walk": {"us_per_launch": round(us_walk, 2), "bytes_per_launch": walk_bytes,
+                         "gbps": round(walk_bytes / us_walk / 1e3, 1),
+                         "frac": round(walk_bytes / us_walk / 1e3 / HBM_PEAK_GBPS, 4),
+                         "pages_per_split": pps, "splits": -(-pages // pps)},
+           "atomics_per_us": round(n_atom / us_atom, 1),
+           "copy_204_8MB_us": round(us_copy, 2), "copy_gbps_read_plus_write": round(gbps, 1)}
+    log(f"bench: ceilings: graph launch {us_launch:.2f} us; random 4 KiB chunks "
+        f"{stream_read['nontemporal']['gbps']:.0f} GB/s nontemporal, "
+        f"{stream_read['ordinary']['gbps']:.0f} GB/s ordinary; split-kernel loads alone "
+        f"{us_walk:.2f} us ({walk_bytes / us_walk / 1e3:.0f} GB/s); "
+        f"{n_atom / us_atom:.0f} atomics/us on one counter; copy {gbps:.0f} GB/s (read + write)")
+    return res
 
 
 def copy_probe(dev):

@@ -13,6 +13,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libflint.so")
 SOURCES = ["api.hip", "append.hip", "decode.hip", "prefill.hip", "moe.hip", "moe_api.hip"]
+# measurement kernels for the bench's machine ceilings, kept out of libflint
+SO_CEILING = os.path.join(HERE, "libflint_ceiling.so")
+SOURCES_CEILING = ["ceiling.hip"]
 ARCH = "gfx950"
 
 
@@ -32,18 +35,24 @@ HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsa
 
 
 def build(verbose: bool = False, sanitize: bool = False) -> str:
-    """Compile every HIP source into one shared library (always rebuilds);
-    sanitize=True builds libflint_san.so with sanitized host code instead."""
-    so = SO_SANITIZED if sanitize else SO
+    """Compile every HIP source into one shared library (always rebuilds),
+    and the ceiling kernels into libflint_ceiling.so; sanitize=True builds
+    libflint_san.so with sanitized host code instead."""
+    if sanitize:
+        return _hipcc(SO_SANITIZED, SOURCES, HOST_SANITIZE_FLAGS, verbose)
+    _hipcc(SO_CEILING, SOURCES_CEILING, [], verbose)
+    return _hipcc(SO, SOURCES, [], verbose)
+
+
+def _hipcc(so: str, sources: list, extra: list, verbose: bool) -> str:
     tmp = so + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-result",
            # packed fp32 VALU ops stay off: ordinary float code only
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-o", tmp]
-    if sanitize:
-        cmd += HOST_SANITIZE_FLAGS
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += extra
+    cmd += [os.path.join(CSRC, s) for s in sources]
     r = subprocess.run(cmd, cwd=HERE, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

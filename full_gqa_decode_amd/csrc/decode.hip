@@ -286,6 +286,7 @@ __device__ __forceinline__ void substitute_new_token(PageRaw8& r, const uint8_t*
 // speculative page id is read inside the caller's block-table row and
 // validated before it addresses the cache.
 constexpr int kAhead = 2;
+constexpr int kAhead8 = 2;  // the same for an fp8 cache
 // MI355X's compute units: a grid of at most this many workgroups runs as one
 // round at one workgroup per CU.
 constexpr int kComputeUnits = 256;
@@ -544,8 +545,9 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
       }
     }
   } else {
-    // The pipelined loop.  A ring of NR page buffers per wave: buffer k is consumed and refilled with the page NR rounds later,
-    // K as soon as the score MFMAs have read it, V after the value MFMAs.
+    // The pipelined loop.  A ring of NR page buffers per wave: buffer k is
+    // consumed and refilled with the page NR rounds later, K as soon as the
+    // score MFMAs have read it, V after the value MFMAs.
     // Raw page ids are read one more round ahead, at an index clamped into
     // the split, and checked when their loads are issued.
     //
@@ -1316,14 +1318,15 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
   const bool win = a.window > 0;
   const bool one_round = (int64_t)grid.x * grid.y * grid.z <= kComputeUnits;
+  constexpr int RG = KV8 ? kAhead8 : kAhead;  // page ring of one-round launches
   if (!FUSED && a.partials_only) {  // every split's partial, whatever the count
     constexpr int W = kDecodeWaves;
     if (one_round) {  // at most one workgroup per CU: the page ring
       if (win)
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8, 2, kAhead>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8, 2, RG>), grid,
                            dim3(W * 64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false, KV8, 2, kAhead>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, false, KV8, 2, RG>), grid,
                            dim3(W * 64), 0, st, a);
     } else if (win)
       hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, false, KV8>), grid, dim3(W * 64),
@@ -1365,10 +1368,10 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   if (a.num_splits == 1) {  // one long split: pipelined loop, sink folded in
     if (loose) {
       if (win)
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8, MW, kAhead>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8, MW, RG>), grid,
                            dim3(W * 64), 0, st, a);
       else
-        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED, KV8, MW, kAhead>), grid,
+        hipLaunchKernelGGL((decode_split_kernel<W, 1, true, false, FUSED, KV8, MW, RG>), grid,
                            dim3(W * 64), 0, st, a);
     } else if (win) {
       hipLaunchKernelGGL((decode_split_kernel<W, 1, true, true, FUSED, KV8>), grid, dim3(W * 64), 0,
@@ -1381,10 +1384,10 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   }
   if (loose) {
     if (win)
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8, MW, kAhead>), grid,
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8, MW, RG>), grid,
                          dim3(W * 64), 0, st, a);
     else
-      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED, KV8, MW, kAhead>), grid,
+      hipLaunchKernelGGL((decode_split_kernel<W, 1, false, false, FUSED, KV8, MW, RG>), grid,
                          dim3(W * 64), 0, st, a);
   } else if (win) {
     hipLaunchKernelGGL((decode_split_kernel<W, 1, false, true, FUSED, KV8>), grid, dim3(W * 64), 0,
@@ -1402,7 +1405,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
-  if (a.kv_fp8) return a.q_in ? launch_decode_t<true, true>(a, st) : launch_decode_t<false, true>(a, st);
+  if (a.kv_fp8)
+    return a.q_in ? launch_decode_t<true, true>(a, st) : launch_decode_t<false, true>(a, st);
   return a.q_in ? launch_decode_t<true, false>(a, st) : launch_decode_t<false, false>(a, st);
 }
 

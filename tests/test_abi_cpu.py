@@ -349,3 +349,23 @@ def test_python_binding_checks_tensor_sizes_before_the_abi():
     with pytest.raises(ValueError, match="w_down"):
         fl.flint_moe_forward(M, _z(1, 512), _z(16, 512, dtype="int16"),
                              _z(17, 2, 512, 512, dtype="int16"), _z(16, 512, 512, dtype="int16"))
+
+
+def test_ceiling_library_exports_its_kernels():
+    # the bench's measurement kernels live in a library of their own, which
+    # the product library neither links nor calls
+    from full_gqa_decode_amd import build as fb
+    fl.lib()
+    lib = C.CDLL(fb.SO_CEILING)
+    for name in ("flint_ceiling_stream_bytes", "flint_ceiling_stream_read",
+                 "flint_ceiling_page_walk", "flint_ceiling_empty", "flint_ceiling_atomics"):
+        assert hasattr(lib, name), name
+    lib.flint_ceiling_stream_bytes.restype = C.c_long
+    assert lib.flint_ceiling_stream_bytes() == 256 * 8 * 96 * 1024
+    # argument checks before any launch
+    lib.flint_ceiling_stream_read.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+    assert lib.flint_ceiling_stream_read(3, 1, None, None, None) == -1
+    lib.flint_ceiling_page_walk.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                            C.c_int, C.c_void_p, C.c_void_p]
+    assert lib.flint_ceiling_page_walk(None, None, None, 0, 4, 98, None, None) == -1
+    assert "ceiling" not in open(fb.SO, "rb").read().decode("latin-1")
