@@ -293,12 +293,13 @@ constexpr int kComputeUnits = 256;
 
 // Launch bounds: MINW, the least waves per SIMD (fp8 kernels are held to 4,
 // 128 VGPRs, so that two workgroups share a CU).  RING: pages in flight per
-// wave in the pipelined loop.  A launch of at most one workgroup per CU takes
-// MINW = 2 and RING = kAhead: the loads alone stream at ~6.4 TB/s in this
-// shape, and one page per wave left the split kernel short of that, since
-// the wave's math between a page's arrival and its next request leaves the
-// load path idle.  Grids of several rounds keep RING = 1, whose smaller
-// register file lets workgroups share a CU.
+// wave in the pipelined loop.  A launch of at most one workgroup per CU whose
+// waves walk at least 4 pages each takes MINW = 2 and RING = kAhead: the
+// loads alone stream at ~6.4 TB/s in this shape, and one page per wave left
+// the split kernel short of that, since the wave's math between a page's
+// arrival and its next request leaves the load path idle.  Grids of several
+// rounds keep RING = 1, whose smaller register file lets workgroups share a
+// CU, and so do short splits, where a ring has nothing to fill.
 template <int WAVES, int MAXP, bool SINGLE, bool WINDOWED, bool FUSED, bool KV8,
           int MINW = (MAXP > 1 ? 1 : (KV8 ? 4 : 2)), int RING = 1>
 __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeArgs a) {
@@ -1317,7 +1318,9 @@ template <bool FUSED, bool KV8>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_splits, a.num_kv_heads, a.num_seqs);
   const bool win = a.window > 0;
-  const bool one_round = (int64_t)grid.x * grid.y * grid.z <= kComputeUnits;
+  // one round of workgroups, each wave with at least 4 pages: the page ring
+  const bool one_round = (int64_t)grid.x * grid.y * grid.z <= kComputeUnits &&
+                         a.pages_per_split >= 4 * kDecodeWaves;
   constexpr int RG = KV8 ? kAhead8 : kAhead;  // page ring of one-round launches
   if (!FUSED && a.partials_only) {  // every split's partial, whatever the count
     constexpr int W = kDecodeWaves;
