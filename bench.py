@@ -49,10 +49,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_full_layer_ctx100k_hbm_cou
 DECODE_SOURCES = ["decode.hip", "device.h", "launch.h", "api.hip"]
 
 
-def measured_traffic():
-    """HBM bytes per full-layer launch pair from the committed rocprofv3
-    FETCH_SIZE/WRITE_SIZE summary, or None once the decode sources differ from
-    the ones those counters were taken on."""
+def measured_traffic(key="traffic_bytes_per_launch"):
+    """HBM bytes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary --
+    per launch of K2 alone (traffic_bytes_per_launch) or per 49-layer step
+    (step_traffic_bytes) -- or None once the decode sources differ from the
+    ones those counters were taken on."""
     import hashlib
     try:
         text = open(TRAFFIC_FILE).read()
@@ -60,16 +61,16 @@ def measured_traffic():
         return None
     vals = {}
     for line in text.splitlines():
-        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+        if ":" in line and line.split(":")[0] in (key, "source_sha256"):
             k, v = line.split(":", 1)
             vals[k] = v.strip()
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
         with open(os.path.join(ROOT, "full_gqa_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
-    if vals.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+    if vals.get("source_sha256") != h.hexdigest() or key not in vals:
         return None
-    return int(vals["traffic_bytes_per_launch"])
+    return int(vals[key])
 
 
 def log(msg):
@@ -304,6 +305,7 @@ def main():
                   for L in layers)
     gbps_step = kv_step / (us_step * 1e-6) / 1e9
 
+    step_traffic = measured_traffic("step_traffic_bytes")
     result = {
         "metric": METRIC,
         "value": round(us_step, 2),
@@ -330,6 +332,11 @@ def main():
         "hbm_gbps": round(gbps_step, 1),
         "hbm_gbps_kind": "analytic: algorithmic K/V bytes of the step / step time",
         "hbm_frac_of_peak": round(gbps_step / HBM_PEAK_GBPS, 4),
+        # the step's HBM bytes by counters (fetch + write of its kernels, from
+        # the committed summary while the sources match) over this run's time
+        "hbm_gbps_counters": (None if step_traffic is None
+                              else round(step_traffic / (us_step * 1e-6) / 1e9, 1)),
+        "step_traffic_bytes": step_traffic,
         "kv_bytes_per_step": kv_step,
         "us_per_step_median": round(statistics.median(per), 2),
         "us_per_step_p10": round(float(np.percentile(per, 10)), 2),
