@@ -1263,7 +1263,8 @@ constexpr int kMidMergeSplits = 64;
 // layer's 1 MB of partials is read by 256 workgroups at 4 KiB apiece rather
 // than by 32 at 32 KiB.  Lane l holds split l's lse and its 16 values of the
 // slice (four 16-byte loads), all requested before any is used; the max and
-// the weights come from wave reductions and every output dim is a wave sum.
+// the weights come from wave reductions, and the 16 output dims from one
+// reduce-scatter over the lanes.
 __global__ __launch_bounds__(64) void decode_merge_slice_kernel(DecodeArgs a) {
   const int hq = a.num_kv_heads * kGroup;
   const int ns = a.num_splits;
@@ -1287,15 +1288,42 @@ __global__ __launch_bounds__(64) void decode_merge_slice_kernel(DecodeArgs a) {
   // an empty split (lse -inf, output never written) contributes 0
   const float w = lse > -INFINITY ? exp2_fast(lse - M) : 0.f;
   const float inv = 1.f / (exp2_fast(sink - M) + wave_sum_f32(w));
-  float res = 0.f;
+  // The 16 sums over the 64 lanes, reduced and scattered at once: one
+  // lane-32 exchange of the pair (x[i], x[i+8]) leaves lanes 0-31 the sums
+  // of dims i and lanes 32-63 those of dims i+8 over their lane pair (8
+  // exchanges for 16 dims); one lane-16 exchange of (y[i], y[i+4]) halves
+  // them again; a row reduction finishes the 4 dims each row of 16 lanes
+  // holds: dims 8h + 4p .. +3, h = l >> 5, p = (l >> 4) & 1.
+  float x[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float s = wave_sum_f32(w > 0.f ? w * ov[i][j] : 0.f);
-      if (l == 4 * i + j) res = s;
-    }
-  if (l < 16) a.out[(int64_t)bh * kHeadDim + js * 16 + l] = nan ? __builtin_nanf("") : res * inv;
+    for (int j = 0; j < 4; ++j) x[4 * i + j] = w > 0.f ? w * ov[i][j] : 0.f;
+  float y[8], z[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x[i]),
+                                                    __builtin_bit_cast(unsigned, x[i + 8]),
+                                                    false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    y[i] = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, y[i]),
+                                                    __builtin_bit_cast(unsigned, y[i + 4]),
+                                                    false, false);
+    const unsigned r0 = r[0], r1 = r[1];
+    float t = __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+    t += row_ror<8>(t);
+    t += row_ror<4>(t);
+    t += row_ror<2>(t);
+    t += row_ror<1>(t);
+    z[i] = nan ? __builtin_nanf("") : t * inv;
+  }
+  if ((l & 15) == 0)
+    *(f32x4*)(a.out + (int64_t)bh * kHeadDim + js * 16 + 8 * (l >> 5) + 4 * ((l >> 4) & 1)) =
+        f32x4{z[0], z[1], z[2], z[3]};
 }
 
 hipError_t launch_merge_k(const DecodeArgs& a, hipStream_t st) {
