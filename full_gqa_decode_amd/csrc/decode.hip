@@ -419,6 +419,12 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
   }
   const bool has_new = FUSED && p_end == last_page + 1;  // this split holds token t
 
+  // fused, fp8: the new token's K or V codes of this lane and where they go,
+  // written after the page loop (below)
+  uint8_t* st8_dst = nullptr;
+  int st8_o0 = 0, st8_o1 = 0;
+  uint32_t st8_c0 = 0, st8_c1 = 0;
+
   // ---- q operand ----------------------------------------------------------
   // column n holds head n&7; n < 8 the bf16 part of q*c, n >= 8 the bf16
   // remainder.  Lane group gq holds dims c*32 + gq*8 .. +7 of block c.
@@ -456,9 +462,11 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
           sm_knew[lane] = (Elem)c0;
           sm_knew[lane + 64] = (Elem)c1;
           if (ok) {
-            uint8_t* dst = (uint8_t*)a.k_cache + o;
-            dst[fp8_k_off(t % kPage, lane)] = (uint8_t)c0;
-            dst[fp8_k_off(t % kPage, lane + 64)] = (uint8_t)c1;
+            st8_dst = (uint8_t*)a.k_cache + o;
+            st8_o0 = fp8_k_off(t % kPage, lane);
+            st8_o1 = fp8_k_off(t % kPage, lane + 64);
+            st8_c0 = c0;
+            st8_c1 = c1;
           }
         } else {
           const uint16_t k0 = bf16_bits_rne_f64(y0), k1 = bf16_bits_rne_f64(y1);
@@ -479,10 +487,11 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
           sm_vnew[lane] = (Elem)c0;
           sm_vnew[lane + 64] = (Elem)c1;
           if (ok) {
-            uint8_t* dst = (uint8_t*)a.v_cache +
-                           ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage);
-            dst[fp8_v_off(t % kPage, lane)] = (uint8_t)c0;
-            dst[fp8_v_off(t % kPage, lane + 64)] = (uint8_t)c1;
+            st8_dst = (uint8_t*)a.v_cache + ((int64_t)pg * a.num_kv_heads + g) * (kHeadDim * kPage);
+            st8_o0 = fp8_v_off(t % kPage, lane);
+            st8_o1 = fp8_v_off(t % kPage, lane + 64);
+            st8_c0 = c0;
+            st8_c1 = c1;
           }
         } else {
           const uint16_t v0 = bf16_bits_rne(xv0), v1 = bf16_bits_rne(xv1);
@@ -598,6 +607,16 @@ __global__ __launch_bounds__(WAVES * 64, MINW) void decode_split_kernel(DecodeAr
       for (int k = 0; k < NR; ++k)
         if (i + NR + k < n_mine) step(k, p + (NR + k) * WAVES, false);
     }
+  }
+
+  // fused, fp8: the cache row of the new token, written only now.  A byte
+  // store may alias any memory, so one issued before the loop would make the
+  // compiler read the page table through vector loads, each waited for with
+  // every page load in flight.  No workgroup reads this row from the cache
+  // in this launch: the split that holds it substitutes it in registers.
+  if (KV8 && FUSED && st8_dst) {
+    st8_dst[st8_o0] = (uint8_t)st8_c0;
+    st8_dst[st8_o1] = (uint8_t)st8_c1;
   }
 
   // ---- per-wave state -> LDS -> this split's result -----------------------
