@@ -373,6 +373,11 @@ def main():
         walk = result["ceilings"]["page_walk"]["us_per_launch"]
         result["roofline"]["loads_alone_us"] = walk
         result["roofline"]["frac_of_loads_alone"] = round(walk / us_k2, 4)
+        if "fp8" in result:
+            k8 = result["fp8"]["split_kernel"]
+            walk8 = result["ceilings"]["page_walk_fp8"]["us_per_launch"]
+            k8["loads_alone_us"] = walk8
+            k8["frac_of_loads_alone"] = round(walk8 / k8["us_per_launch"], 4)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(fl, dev, stream)
@@ -762,7 +767,7 @@ def _ceiling_lib():
     P, I = C.c_void_p, C.c_int
     L.flint_ceiling_stream_bytes.restype = C.c_long
     L.flint_ceiling_stream_read.argtypes = [I, I, P, P, P]
-    L.flint_ceiling_page_walk.argtypes = [P, P, P, I, I, I, P, P]
+    L.flint_ceiling_page_walk.argtypes = [P, P, P, I, I, I, I, P, P]
     L.flint_ceiling_empty.argtypes = [P]
     L.flint_ceiling_atomics.argtypes = [P, I, I, P]
     return L
@@ -779,7 +784,8 @@ def bench_ceilings(dev):
       page_walk        the split-K kernel's loads alone in its own shape (64
                        splits x 4 KV heads, 8 waves, a shuffled page table,
                        6250 pages of 4 KiB K + 4 KiB V per head: one 100K
-                       full layer), 14 distinct layers;
+                       full layer), 14 distinct layers; page_walk_fp8 the
+                       same over 2 KiB fp8 tiles;
       atomics          agent-scope atomic adds on one hot counter per us;
     plus torch's device-to-device copy of 204.8 MB (bytes read + written)."""
     import torch
@@ -830,9 +836,14 @@ def bench_ceilings(dev):
     gen = torch.Generator().manual_seed(SEED)
     tables = [torch.randperm(pages, generator=gen).to(torch.int32).to(dev) for _ in range(nreg)]
     us_walk = graph_time(lambda: [ok(L.flint_ceiling_page_walk(
-        k[i].data_ptr(), v[i].data_ptr(), tables[i].data_ptr(), pages, heads, pps,
+        k[i].data_ptr(), v[i].data_ptr(), tables[i].data_ptr(), pages, heads, pps, 0,
         out.data_ptr(), sid())) for i in range(nreg)], nreg)
     walk_bytes = 2 * tb
+    # the same walk over an fp8 cache's 2 KiB tiles (the first half of each buffer)
+    us_walk8 = graph_time(lambda: [ok(L.flint_ceiling_page_walk(
+        k[i].data_ptr(), v[i].data_ptr(), tables[i].data_ptr(), pages, heads, pps, 1,
+        out.data_ptr(), sid())) for i in range(nreg)], nreg)
+    walk8_bytes = tb
     del k, v
 
     ctr = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -859,12 +870,16 @@ def bench_ceilings(dev):
                          "gbps": round(walk_bytes / us_walk / 1e3, 1),
                          "frac": round(walk_bytes / us_walk / 1e3 / HBM_PEAK_GBPS, 4),
                          "pages_per_split": pps, "splits": -(-pages // pps)},
+           "page_walk_fp8": {"us_per_launch": round(us_walk8, 2), "bytes_per_launch": walk8_bytes,
+                             "gbps": round(walk8_bytes / us_walk8 / 1e3, 1),
+                             "frac": round(walk8_bytes / us_walk8 / 1e3 / HBM_PEAK_GBPS, 4)},
            "atomics_per_us": round(n_atom / us_atom, 1),
            "copy_204_8MB_us": round(us_copy, 2), "copy_gbps_read_plus_write": round(gbps, 1)}
     log(f"bench: ceilings: graph launch {us_launch:.2f} us; random 4 KiB chunks "
         f"{stream_read['nontemporal']['gbps']:.0f} GB/s nontemporal, "
         f"{stream_read['ordinary']['gbps']:.0f} GB/s ordinary; split-kernel loads alone "
-        f"{us_walk:.2f} us ({walk_bytes / us_walk / 1e3:.0f} GB/s); "
+        f"{us_walk:.2f} us ({walk_bytes / us_walk / 1e3:.0f} GB/s), over an fp8 cache "
+        f"{us_walk8:.2f} us ({walk8_bytes / us_walk8 / 1e3:.0f} GB/s); "
         f"{n_atom / us_atom:.0f} atomics/us on one counter; copy {gbps:.0f} GB/s (read + write)")
     return res
 

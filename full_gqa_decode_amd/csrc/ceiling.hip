@@ -11,11 +11,12 @@
 //                              in its shape: a workgroup per (split, KV head),
 //                              8 waves, wave w walks pages w, w+8, ... of its
 //                              split through a page table, one page of loads
-//                              ahead; 4 KiB of K (4 x 16-byte loads per lane)
-//                              and 4 KiB of V (8 x 8-byte loads) per page and
-//                              head, nontemporal.  Every loaded dword is
-//                              folded into one value per lane, so no load is
-//                              dropped.
+//                              ahead; per page and head 4 KiB of K (4 x
+//                              16-byte loads per lane) and 4 KiB of V (8 x
+//                              8-byte loads) for a bf16 cache, or 2 KiB of
+//                              each (2 x 16-byte loads) for an fp8 cache,
+//                              nontemporal.  Every loaded dword is folded into
+//                              one value per lane, so no load is dropped.
 //   flint_ceiling_empty        a kernel that does nothing (launch cost).
 //   flint_ceiling_atomics      count agent-scope atomic adds on one counter
 //                              (throughput of a hot counter; no thread ever
@@ -82,7 +83,9 @@ struct WalkArgs {
   uint32_t* out;
 };
 
+template <bool FP8>
 __global__ __launch_bounds__(kWaves * 64, 2) void page_walk_kernel(WalkArgs a) {
+  constexpr int kTile = FP8 ? 2048 : 4096;
   const int s = blockIdx.x, g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -90,23 +93,37 @@ __global__ __launch_bounds__(kWaves * 64, 2) void page_walk_kernel(WalkArgs a) {
   const int last = min(pb + a.pages_per_split, a.pages) - 1;
   int p = pb + w;
   const int n = p <= last ? (last - p) / kWaves + 1 : 0;
-  u32x4 k[4];
-  u32x2 v[8];
+  constexpr int KL = FP8 ? 2 : 4;  // 16-byte K loads per lane and page
+  constexpr int VL = FP8 ? 2 : 8;  // V loads per lane: 16 bytes (fp8) or 8 (bf16)
+  u32x4 k[KL];
+  u32x4 v4[FP8 ? VL : 1];
+  u32x2 v2[FP8 ? 1 : VL];
   uint32_t acc = 0;
   auto load = [&](int id) {
-    const int64_t tile = ((int64_t)id * a.heads + g) * 4096;
+    const int64_t tile = ((int64_t)id * a.heads + g) * kTile;
     const u32x4* kp = (const u32x4*)(a.k + tile + lane * 16);
-    const u32x2* vp = (const u32x2*)(a.v + tile + lane * 8);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) k[c] = __builtin_nontemporal_load(kp + c * 64);
+    for (int c = 0; c < KL; ++c) k[c] = __builtin_nontemporal_load(kp + c * 64);
+    if constexpr (FP8) {
+      const u32x4* vp = (const u32x4*)(a.v + tile + lane * 16);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = __builtin_nontemporal_load(vp + c * 64);
+      for (int c = 0; c < VL; ++c) v4[c] = __builtin_nontemporal_load(vp + c * 64);
+    } else {
+      const u32x2* vp = (const u32x2*)(a.v + tile + lane * 8);
+#pragma unroll
+      for (int c = 0; c < VL; ++c) v2[c] = __builtin_nontemporal_load(vp + c * 64);
+    }
   };
   auto fold = [&] {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc ^= k[c][0] ^ k[c][1] ^ k[c][2] ^ k[c][3];
+    for (int c = 0; c < KL; ++c) acc ^= k[c][0] ^ k[c][1] ^ k[c][2] ^ k[c][3];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc ^= v[c][0] ^ v[c][1];
+      for (int c = 0; c < VL; ++c) acc ^= v4[c][0] ^ v4[c][1] ^ v4[c][2] ^ v4[c][3];
+    } else {
+#pragma unroll
+      for (int c = 0; c < VL; ++c) acc ^= v2[c][0] ^ v2[c][1];
+    }
   };
   if (n > 0) {
     // ids are table entries inside [pb, last]; the host checks the table
@@ -166,14 +183,21 @@ int flint_ceiling_stream_read(int chunk_kb, int nontemporal, const void* base, u
   }
 }
 
-// k, v: pages * heads * 4096 bytes each; table: pages entries, each in
-// [0, pages) (checked by the caller); out: splits * heads * 512 uint32.
+// k, v: pages * heads * tile bytes each (4096 for a bf16 cache, 2048 for an
+// fp8 one: fp8 != 0); table: pages entries, each in [0, pages) (checked by
+// the caller); out: splits * heads * 512 uint32.
 int flint_ceiling_page_walk(const void* k, const void* v, const int* table, int pages,
-                            int heads, int pages_per_split, uint32_t* out, void* stream) {
+                            int heads, int pages_per_split, int fp8, uint32_t* out,
+                            void* stream) {
   if (pages < 1 || heads < 1 || pages_per_split < 1) return -1;
   const WalkArgs a{(const char*)k, (const char*)v, table, pages_per_split, pages, heads, out};
   const dim3 grid((pages + pages_per_split - 1) / pages_per_split, heads);
-  hipLaunchKernelGGL(page_walk_kernel, grid, dim3(kWaves * 64), 0, (hipStream_t)stream, a);
+  if (fp8)
+    hipLaunchKernelGGL(page_walk_kernel<true>, grid, dim3(kWaves * 64), 0, (hipStream_t)stream,
+                       a);
+  else
+    hipLaunchKernelGGL(page_walk_kernel<false>, grid, dim3(kWaves * 64), 0, (hipStream_t)stream,
+                       a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

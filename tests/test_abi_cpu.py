@@ -366,6 +366,6 @@ def test_ceiling_library_exports_its_kernels():
     lib.flint_ceiling_stream_read.argtypes = [C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
     assert lib.flint_ceiling_stream_read(3, 1, None, None, None) == -1
     lib.flint_ceiling_page_walk.argtypes = [C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
-                                            C.c_int, C.c_void_p, C.c_void_p]
-    assert lib.flint_ceiling_page_walk(None, None, None, 0, 4, 98, None, None) == -1
+                                            C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    assert lib.flint_ceiling_page_walk(None, None, None, 0, 4, 98, 0, None, None) == -1
     assert "ceiling" not in open(fb.SO, "rb").read().decode("latin-1")
