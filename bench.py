@@ -524,11 +524,17 @@ def bench_moe(fl, dev, capture, stream):
     return res
 
 
-def _time_launches(fn, reps=10, warm=3):
-    """Mean µs per call of fn over reps calls after warm calls (HIP events on
-    the current stream)."""
+def _time_launches(fn, reps=10, warm=3, warm_ms=30.0):
+    """Mean µs per call of fn over reps calls after warm calls and at least
+    warm_ms of calls (the core clock ramps up over tens of milliseconds of
+    sustained work), with HIP events on the current stream."""
     import torch
-    for _ in range(warm):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(max(warm, math.ceil(warm_ms / max(e0.elapsed_time(e1), 1e-3)))):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -908,6 +914,10 @@ def bench_prefill(fl, dev, stream):
     return full
 
 
+PREFILL_WARM_MS = 60.0
+PREFILL_TIMED_MS = 20.0
+
+
 def prefill_leg(fl, dev, window, fp8=False):
     import torch
     T = 32768
@@ -936,10 +946,20 @@ def prefill_leg(fl, dev, window, fp8=False):
     sl = up(np.array([T], np.int32))
     btd = up(bt)
     run = lambda: fl.flint_attn_prefill(L, qb, cu, T, kc, vc, btd, sl, T, sinks, out)
-    run()
-    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 3
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    first_ms = e0.elapsed_time(e1)
+    # The core clock ramps up over tens of milliseconds of sustained work: a
+    # single 0.6 ms sliding-layer launch after idle runs at ~1.9 GHz instead
+    # of ~2.35.  Warm up for PREFILL_WARM_MS of launches, then time at least
+    # PREFILL_TIMED_MS of them.
+    for _ in range(max(2, math.ceil(PREFILL_WARM_MS / first_ms))):
+        run()
+    reps = max(3, math.ceil(PREFILL_TIMED_MS / first_ms))
+    torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
         run()

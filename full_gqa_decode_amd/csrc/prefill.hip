@@ -8,12 +8,14 @@
 //
 // Design.  A query vector is one (row, head) pair; the eight heads of a KV
 // group share every key, so a 16-wide MFMA tile holds 2 rows x 8 heads.  A
-// wave owns kTiles such tiles (kWaveRows consecutive rows); a workgroup of
-// kPWaves waves owns kRows rows of one KV group.  The workgroup walks the key
-// pages of its rows in pairs (32 keys): every thread fetches 16 bytes of K and
-// 16 bytes of V of the pair two ahead while the waves compute on the current
-// one, and each pair is staged once in LDS (double-buffered, one barrier per
-// pair) for all waves -- HBM/L2 traffic per flop falls by the number of waves.
+// wave owns kTiles such tiles (kWaveRows consecutive rows); a work item is
+// kRows rows of one KV group, run by a workgroup of kPWaves waves (a
+// persistent grid of one workgroup per CU loops over the items).  The
+// workgroup walks the key pages of the item's rows in pairs (32 keys): every
+// thread fetches 16 bytes of K and 16 bytes of V of the pair two ahead while
+// the waves compute on the current one, and each pair is staged once in LDS
+// (double-buffered, one barrier per pair) for all waves -- HBM/L2 traffic per
+// flop falls by the number of waves.
 // Per pair and tile:
 //   S^T[32 keys x 16 qv] = K . Q^T     2 x 4 v_mfma_f32_16x16x32_bf16
 //   O[16 qv x 128]      += P . V        8 x 2 v_mfma_f32_16x16x32_bf16
@@ -43,7 +45,8 @@ constexpr int kSoftmaxValuFirst = 40, kValuPerMfma = 2;
 constexpr int kWaveRows = kTiles * 2;        // query rows per wave
 constexpr int kPWaves = 8;                   // waves per workgroup
 constexpr int kPThreads = kPWaves * 64;
-constexpr int kRows = kWaveRows * kPWaves;   // query rows per workgroup
+constexpr int kRows = kWaveRows * kPWaves;   // query rows per work item
+constexpr int kPrefillWorkgroups = 256;      // persistent grid: one workgroup per CU
 // LDS copy of one page pair, unpadded, with 16-byte slots permuted so that
 // every MFMA operand read is conflict-free.  gfx950's LDS serves a 16-byte
 // read 32 lanes at a time from 128 four-byte banks, so the 32 slots those
@@ -125,12 +128,13 @@ __device__ __forceinline__ void read_pair(const unsigned char* buf, int n, int g
     r.v[nb] = *(const u32x4*)(buf + v_slot(nb * 16 + n, gq));
 }
 
+// One work item: the kRows query rows of row block `tile` of request b, for
+// KV group g.  Every wave of the workgroup runs it (waves without rows still
+// stage pages and meet the barriers); items with no rows return at once.
 template <bool WINDOWED, bool KV8>
-__global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char sm[2][kBufBytes];
-  const int ntile = gridDim.x;
-  const int tile = ntile - 1 - blockIdx.x;  // longest key ranges first
-  const int g = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int g, int b,
+                                             unsigned char (&sm)[2][kBufBytes],
+                                             float (&sm_sink)[kGroup]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, gq = lane >> 4;
@@ -162,26 +166,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int p_first = wg_lo / kPage, p_last = wg_pos_last / kPage;
   const int npairs = req_bad ? 0 : (p_last - p_first) / 2 + 1;
 
-  // Q operands: tile mt, column n -> row row0 + 2*mt + (n>>3), head g*8 + (n&7)
-  bf16x8 qop[kTiles][4];
+  // Q operands (tile mt, column n -> row row0 + 2*mt + (n>>3), head
+  // g*8 + (n&7)), loaded at start-up, below
+  bf16x8 qop[kTiles][4] = {};
   int qpos[kTiles];
 #pragma unroll
-  for (int mt = 0; mt < kTiles; ++mt) {
-    const int r = min(row0 + 2 * mt + (n >> 3), q_len - 1);
-    qpos[mt] = base + row0 + 2 * mt + (n >> 3);
-    const uint16_t* qp = a.q + (((int64_t)(q0 + r) * hq) + g * kGroup + (n & 7)) * kHeadDim + gq * 8;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qop[mt][c] = (req_bad || !active) ? bf16x8{} : *(const bf16x8*)(qp + c * 32);
-  }
-
-  // wait for the Q operands here, once: inside the loop the compiler cannot
-  // tell them apart from the page loads in flight and would wait for all of
-  // those before every pair's first MFMA
-#pragma unroll
-  for (int mt = 0; mt < kTiles; ++mt)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qop[mt][c]));
+  for (int mt = 0; mt < kTiles; ++mt) qpos[mt] = base + row0 + 2 * mt + (n >> 3);
 
   // m_run: the lazy reference max (log2 units).  It starts at the lowest
   // finite float rather than -inf, so that a row's first visible key always
@@ -358,20 +348,50 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   // loads of pairs i+1 and i+2 in register sets (i+1)&1 and (i+2)&1, the ids
   // of pairs i+3 and i+4 in id sets (i+3)&1 and (i+4)&1 (loop unrolled by two
   // so every set is static).
+  //
+  // Start-up: the group's sinks and the first page ids, then the Q operands,
+  // then the first pair's pages once its ids are in.  Vector loads complete
+  // in issue order, so the wait for the ids does not wait for Q, and Q
+  // arrives under the id round trip instead of after it.  Every load here is
+  // unconditional (a row index clamped into the chunk: waves without rows
+  // load and ignore), so the compiler's counts of loads in flight are exact.
+  // The sinks go to LDS (read in the epilogue) rather than holding registers
+  // through the loop.
   u32x4 kr0, vr0, kr1, vr1;
   int ia0, ib0, ia1, ib1, ia2, ib2;
+  float sink_l2 = 0.f;
   if (npairs > 0) {
+    const float sink = a.sinks[g * kGroup + (lane & 7)];
     load_ids(0, ia0, ib0);
     load_ids(1, ia1, ib1);
     load_ids(2, ia2, ib2);
-    fetch(0, ia0, ib0, kr0, vr0);
+#pragma unroll
+    for (int mt = 0; mt < kTiles; ++mt) {
+      const int r = min(row0 + 2 * mt + (n >> 3), q_len - 1);
+      const uint16_t* qp =
+          a.q + (((int64_t)(q0 + r) * hq) + g * kGroup + (n & 7)) * kHeadDim + gq * 8;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qop[mt][c] = *(const bf16x8*)(qp + c * 32);
+    }
+    fetch(0, ia0, ib0, kr0, vr0);  // waits for the ids, hence for the sinks
+    sink_l2 = sink * kLog2e;
     stage_pair<KV8>(sm[0], tid, kr0, vr0);
+    // Q and the sinks were issued before pair 0, so they are in; pinning
+    // them here keeps the compiler from waiting for them inside the loop,
+    // where it could not tell them from the page loads in flight
+#pragma unroll
+    for (int mt = 0; mt < kTiles; ++mt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qop[mt][c]));
     fetch(1, ia1, ib1, kr1, vr1);
     fetch(2, ia2, ib2, kr0, vr0);
     load_ids(3, ia1, ib1);
     load_ids(4, ia0, ib0);
   }
   __syncthreads();
+  // every wave has left the previous item's epilogue (the last reader of
+  // sm_sink) by the barrier above; the loop's first barrier publishes this
+  if (npairs > 0 && tid < kGroup) sm_sink[tid] = sink_l2;
   for (int i = 0; i < npairs; i += 2) {
     compute(i);
     if (i + 1 < npairs) stage_pair<KV8>(sm[1], tid, kr1, vr1);
@@ -401,7 +421,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       const int r = row0 + 2 * mt + (v >> 3);
       if (r >= q_len) continue;
       const int h = g * kGroup + (v & 7);
-      const float sink = a.sinks[h] * kLog2e;
+      const float sink = sm_sink[v & 7];
       const float M2 = fmaxf(m, sink);
       const float so = exp2_fast(m - M2);
       const float inv = 1.f / (l * so + exp2_fast(sink - M2));
@@ -414,11 +434,39 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// Persistent grid: at most kPrefillWorkgroups workgroups (one per CU), each
+// looping over items.  Items are ordered longest key range first (row blocks
+// from the last down, then KV group, then request) and dealt out in rounds of
+// gridDim.x, every other round in reverse, so each workgroup's total is
+// balanced (for one causal request, exactly up to the last partial round).
+// Handing items to workgroups here rather than launching one workgroup per
+// item leaves no dispatch gaps: MI355X deals workgroups to its 8 XCDs in
+// turn, so with items of unequal length a CU that frees up waits until the
+// XCD whose turn it is has a free CU too.
+template <bool WINDOWED, bool KV8>
+__global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char sm[2][kBufBytes];
+  __shared__ float sm_sink[kGroup];  // log2-scaled sinks of the current item's heads
+  const int ntile = (a.max_q_len + kRows - 1) / kRows;
+  const int64_t per_tile = (int64_t)a.num_kv_heads * a.num_seqs;
+  const int64_t nitems = per_tile * ntile;
+  const int G = gridDim.x;
+  for (int64_t r = 0;; ++r) {
+    const int64_t slot = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (slot >= nitems) break;
+    const int tile = ntile - 1 - (int)(slot / per_tile);
+    const int rest = (int)(slot % per_tile);
+    prefill_item<WINDOWED, KV8>(a, tile, rest % a.num_kv_heads, rest / a.num_kv_heads, sm, sm_sink);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
-  const dim3 grid((a.max_q_len + kRows - 1) / kRows, a.num_kv_heads, a.num_seqs);
+  const int64_t items =
+      (int64_t)((a.max_q_len + kRows - 1) / kRows) * a.num_kv_heads * a.num_seqs;
+  const dim3 grid((unsigned)(items < kPrefillWorkgroups ? items : kPrefillWorkgroups));
   if (a.kv_fp8) {
     if (a.window > 0)
       hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kPThreads), 0, st, a);
