@@ -190,6 +190,43 @@ def test_prefill_invalid_requests_give_nan_and_spare_the_rest(window):
     assert_parity(got[:100], ok[:100])
 
 
+def _many_requests():
+    """24 requests with chunks of 1..119 rows on contexts up to 300 tokens
+    longer, request 0 the longest chunk (200 rows: 7 row blocks), request 5
+    an empty chunk."""
+    rng = np.random.default_rng(21)
+    reqs = []
+    for _ in range(24):
+        ql = int(rng.integers(1, 120))
+        reqs.append((ql + int(rng.integers(0, 300)), ql))
+    reqs[0] = (600, 200)
+    reqs[5] = (reqs[5][0], 0)
+    return reqs
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_prefill_many_requests_more_items_than_workgroups(window):
+    # 7 row blocks x 4 KV heads x 24 requests = 672 work items for the 256
+    # workgroups of the persistent grid, most of them past the end of a
+    # short chunk.  Request 9 holds a page id past num_blocks and request 14
+    # a chunk longer than its context: their rows come out NaN, and the
+    # workgroups that meet them go on to the next items unharmed.
+    reqs = _many_requests()
+    case = PrefillCase(7, reqs, window=window)
+    bt = case.bt.copy()
+    bt[9, 1] = case.num_blocks + 3
+    sl = case.seq_lens.copy()
+    sl[14] = reqs[14][1] - 1
+    got, _, _, _ = case.run_gpu(bt=bt, seq_lens=sl)
+    bad = np.zeros(len(case.chunk_rows), bool)
+    for b in (9, 14):
+        bad[case.cu[b]:case.cu[b + 1]] = True
+    assert bad.sum() > 0 and np.isnan(got[bad]).all()
+    good = np.flatnonzero(~bad)
+    want = case.expected(rows=good)
+    assert_parity(got[good], want[good])
+
+
 def test_prefill_graph_replays_match_eager():
     import torch
     import full_gqa_decode_amd as fl
