@@ -10,6 +10,8 @@ workgroups and the wide merge) and on a sliding layer whose RoPE angle is
 taken at position 262,143; and 64 requests with context lengths uniform in
 [1024, 131072] on a full layer (about 7.9 GB of KV, every request's output
 and cache write checked) and on a sliding layer (every request checked).
+Over an fp8 cache: the 100,000-token and the 262,144-token full layers, and
+the 64 requests on a full and on a sliding layer.
 
 The resident cache pages are N(0,1) bf16 drawn on the GPU by a seeded torch
 generator and copied to the host for the oracle; the new tokens' q/k/v come
@@ -249,5 +251,35 @@ def test_ragged_64_requests_sliding_layer_fp8():
     ref = case.oracle_step(np.arange(64))
     err = float(np.abs(got - ref).max())
     print(f"64 ragged requests, sliding layer, fp8 cache: max err {err:.3e}", flush=True)
+    check_err(err, ref)
+    case.check_written_rows()
+
+
+def test_bs1_max_context_full_layer_step_fp8():
+    # the fp8 cache at the maximum context: the same 128 x 128 plan, two
+    # rounds of workgroups (the fp8 kernel's one-page loop) and the wide merge
+    import full_gqa_decode_amd as fl
+    L = fl.layer(window=0, use_rope=0, kv_dtype=fl.FLINT_KV_FP8_E4M3, k_scale=1.0, v_scale=0.25)
+    assert fl.flint_attn_decode_plan(L, 1, MAX_CONTEXT) == (128, 128)
+    case = BigStep((11, 12), [MAX_CONTEXT], window=0, full_table=True, fp8=(1.0, 0.25))
+    got = case.run_gpu()
+    ref = case.oracle_step(np.arange(1))
+    err = float(np.abs(got - ref).max())
+    print(f"bs1 262,144-token full layer, fp8 cache: max err {err:.3e}", flush=True)
+    check_err(err, ref)
+    case.check_written_rows()
+
+
+def test_ragged_64_requests_full_layer_fp8():
+    # 64 requests of 1024..131072 tokens over an fp8 cache (about 4 GB of
+    # codes): a multi-round plan; every request's output and cache write checked
+    lens = ragged_lengths()
+    case = BigStep((11, 13), lens, window=0, full_table=True, fp8=(1.0 / 16, 0.25))
+    got = case.run_gpu()
+    assert np.isfinite(got).all()
+    ref = case.oracle_step(np.arange(64))
+    err = float(np.abs(got - ref).max())
+    print(f"64 ragged requests, full layer, fp8 cache: all 64 checked, max err {err:.3e}",
+          flush=True)
     check_err(err, ref)
     case.check_written_rows()
