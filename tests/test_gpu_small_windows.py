@@ -77,6 +77,20 @@ def test_prefill_other_kv_head_counts(hkv):
         assert_parity(got, case.expected(), (hkv, window))
 
 
+@pytest.mark.parametrize("hkv,reqs", [
+    (8, [(800, 800), (300, 60)]),                       # 25 row blocks x 8 x 2 = 400 items
+    (1, [(700 - 37 * i, 700 - 53 * i) for i in range(12)]),  # 22 x 1 x 12 = 264 items
+])
+def test_prefill_other_kv_head_counts_more_items_than_workgroups(hkv, reqs):
+    # more (row block, KV head, request) items than the 256 workgroups of the
+    # persistent prefill grid, so workgroups run several items each
+    from test_gpu_prefill import PrefillCase
+    for window in (0, 513):
+        case = PrefillCase(47, reqs, window=window, hkv=hkv)
+        got, _, _, _ = case.run_gpu()
+        assert_parity(got, case.expected(), (hkv, window))
+
+
 @pytest.mark.parametrize("hkv", [1, 8])
 def test_fp8_decode_other_kv_head_counts(hkv):
     case = DecodeCase(46, [1, 40, 900], window=0, weights_one=False, fp8=(1.0 / 16, 0.5),
