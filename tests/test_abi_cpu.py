@@ -369,3 +369,46 @@ def test_ceiling_library_exports_its_kernels():
                                             C.c_int, C.c_int, C.c_void_p, C.c_void_p]
     assert lib.flint_ceiling_page_walk(None, None, None, 0, 4, 98, 0, None, None) == -1
     assert "ceiling" not in open(fb.SO, "rb").read().decode("latin-1")
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include "flint.h"
+
+int main(void) {
+  flint_attn_layer L = {32, 4, 128, 16, 0, 0, 10000.0f, 1e-6f, 0.08838834764831845f,
+                        FLINT_KV_BF16, 1.0f, 1.0f};
+  int32_t pps = 0, splits = 0;
+  flint_status st = flint_attn_decode_plan(&L, 1, 100000, 0, &pps, &splits);
+  size_t ws = flint_attn_decode_workspace_size(&L, 1, 100000);
+  flint_status bad = flint_attn_decode_plan(NULL, 1, 100000, 0, &pps, &splits);
+  printf("%d %d %d %d %zu %d\n", (int)flint_abi_version(), (int)st, (int)pps, (int)splits, ws,
+         (int)bad);
+  return 0;
+}
+"""
+
+
+def test_header_is_c11_and_a_c_program_links_and_calls_the_library(tmp_path):
+    # The boundary from plain C: include/flint.h compiles as strict C11 and a
+    # program linked against libflint.so gets the same plan, workspace size
+    # and error status as the Python binding (host-only calls, no GPU).
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc is not installed")
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(fl.LIB_PATH)
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", libdir, "-lflint", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, check=True)
+    ver, st, pps, splits, ws, bad = (int(x) for x in out.stdout.split())
+    L = fl.full_layer()
+    assert ver == fl.lib().flint_abi_version()
+    assert st == fl.FLINT_OK and (pps, splits) == fl.flint_attn_decode_plan(L, 1, 100000)
+    assert ws == fl.flint_attn_decode_workspace_size(L, 1, 100000)
+    assert fl.STATUS_NAMES[bad] == "FLINT_ERR_INVALID_ARGUMENT"
