@@ -132,6 +132,10 @@ def main():
     ap.add_argument("--ceilings", action="store_true",
                     help="only the machine-ceiling leg (launch, streaming reads, the split "
                          "kernel's loads alone, atomics), as one JSON line")
+    ap.add_argument("--stamps", action="store_true",
+                    help="only the phase stamps of the prefill and slice kernels, from the "
+                         "instrumented libflint_stamps.so (python -m full_gqa_decode_amd.build "
+                         "--stamps), as one JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy three times (the "
                          "known-size kernel that calibrates HBM byte counters) and exit")
@@ -147,6 +151,9 @@ def main():
         return
     if args.copy_probe:
         copy_probe(torch.device("cuda:0"))
+        return
+    if args.stamps:
+        print(json.dumps({"stamps": bench_stamps(torch.device("cuda:0"))}), flush=True)
         return
     import full_gqa_decode_amd as fl
     fl.lib()
@@ -888,6 +895,92 @@ def bench_ceilings(dev):
         f"{us_walk8:.2f} us ({walk8_bytes / us_walk8 / 1e3:.0f} GB/s); "
         f"{n_atom / us_atom:.0f} atomics/us on one counter; copy {gbps:.0f} GB/s (read + write)")
     return res
+
+
+STAMP_NS = 10.0   # s_memrealtime counts at 100 MHz
+
+
+def bench_stamps(dev):
+    """Per-wave phase stamps (s_memrealtime) from the instrumented library:
+    the 32,768-token prefill of a sliding and of a full layer (per work item:
+    start-up, loop, epilogue, and the gaps between a workgroup's items) and one
+    fused sliding-layer decode step at batch 1 (per slice workgroup: scalar
+    inputs, start-up before the page loads, the pages, the epilogue)."""
+    import ctypes
+    import torch
+    import full_gqa_decode_amd as fl
+    path = os.path.join(ROOT, "full_gqa_decode_amd", "libflint_stamps.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: python -m full_gqa_decode_amd.build --stamps")
+    fl.LIB_PATH = path
+    lib = fl.lib()
+    lib.flint_stamps_prefill.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.flint_stamps_slice.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+
+    def read(fn, shape):
+        buf = np.zeros(int(np.prod(shape)), np.uint64)
+        assert fn(buf.ctypes.data, buf.nbytes) == 0
+        return buf.reshape(shape).astype(np.int64)
+
+    def stats(x):
+        return {"mean": round(float(np.mean(x)), 3), "median": round(float(np.median(x)), 3)}
+
+    out = {"clock": "s_memrealtime, 100 MHz; µs"}
+    items, waves = 4096, 8
+    for name, window in (("prefill_sliding_layer_32k", WINDOW), ("prefill_full_layer_32k", 0)):
+        prefill_leg(fl, dev, window=window)
+        torch.cuda.synchronize()
+        st = read(lib.flint_stamps_prefill, (8192, waves, 8))[:items]
+        t = (st[:, :, :6] - st[:, :, 0].min()) * STAMP_NS / 1e3
+        npairs = st[:, 0, 7]
+        ph = np.diff(t, axis=2).mean(1)   # per item, mean over waves
+        grid = 256
+        slot = np.arange(items)
+        wg = np.where((slot // grid) % 2 == 0, slot % grid, grid - 1 - slot % grid)
+        start, end = t[:, :, 0].min(1), t[:, :, 5].max(1)
+        gaps, ends = [], []
+        for g in range(grid):
+            idx = np.flatnonzero(wg == g)
+            o = idx[np.argsort(start[idx])]
+            gaps += list(start[o[1:]] - end[o[:-1]])
+            ends.append(end[idx].max())
+        out[name] = {
+            "items": items, "workgroups": grid,
+            "entry_to_lengths": stats(ph[:, 0]), "lengths_to_pair0_staged": stats(ph[:, 1]),
+            "pair0_to_loop": stats(ph[:, 2]), "loop": stats(ph[:, 3]),
+            "loop_per_pair": stats(ph[:, 3] / np.maximum(npairs, 1)),
+            "epilogue": stats(ph[:, 4]), "gap_between_items": stats(np.array(gaps)),
+            "workgroup_end_min_max": [round(float(min(ends)), 1), round(float(max(ends)), 1)]}
+    # one fused sliding-layer step at batch 1 (32 slice workgroups)
+    eps = float(np.float32(1e-6))
+    L = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps)
+    ctx = 32768
+    bt, nb = synth.ring_block_table(SEED, (6, ctx, synth.PERM), 1, ctx // PAGE, RING, ctx // PAGE)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    kc = synth.normal_bf16_bits_torch(SEED, (6, ctx, synth.KC), (nb, HKV, PAGE, D), dev)
+    vc = synth.normal_bf16_bits_torch(SEED, (6, ctx, synth.VC), (nb, HKV, D, PAGE), dev)
+    t_new = ctx - 1
+    slots = up(np.array([int(bt[0, t_new // PAGE]) * PAGE + t_new % PAGE], np.int32))
+    q = up(synth.normal(SEED, (6, ctx, synth.Q), (1, HQ, D)))
+    k = up(synth.normal(SEED, (6, ctx, synth.K), (1, HKV, D)))
+    v = up(synth.normal(SEED, (6, ctx, synth.V), (1, HKV, D)))
+    sinks = up(synth.normal(SEED, (6, ctx, synth.SINK), HQ))
+    ones = torch.ones(D, dtype=torch.float32, device=dev)
+    sl = torch.tensor([ctx], dtype=torch.int32, device=dev)
+    o = torch.empty((1, HQ, D), dtype=torch.float32, device=dev)
+    btd = up(bt)
+    for _ in range(3):   # the last call's stamps are read
+        fl.flint_attn_decode_step(L, q, k, v, ones, ones, slots, kc, vc, btd, sl, ctx, sinks, o)
+    torch.cuda.synchronize()
+    nwg = HKV * 8
+    st = read(lib.flint_stamps_slice, (1024, 16, 8))[:nwg, :8]
+    t = (st[:, :, :5] - st[:, :, 0].min()) * STAMP_NS / 1e3
+    ph = np.diff(t, axis=2).mean(1)
+    out["decode_sliding_layer_fused_bs1"] = {
+        "workgroups": nwg, "entry_to_scalars": stats(ph[:, 0]),
+        "scalars_to_page_issue": stats(ph[:, 1]), "pages": stats(ph[:, 2]),
+        "epilogue": stats(ph[:, 3]), "span": round(float(t[:, :, 4].max()), 3)}
+    return out
 
 
 def copy_probe(dev):

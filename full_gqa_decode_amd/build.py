@@ -34,12 +34,20 @@ HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsa
                        "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
 
 
-def build(verbose: bool = False, sanitize: bool = False) -> str:
+# The library with per-wave phase stamps in the prefill and slice kernels
+# (build(stamps=True), -DFLINT_STAMPS): read by `bench.py --stamps` only.
+SO_STAMPS = os.path.join(HERE, "libflint_stamps.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False, stamps: bool = False) -> str:
     """Compile every HIP source into one shared library (always rebuilds),
     and the ceiling kernels into libflint_ceiling.so; sanitize=True builds
-    libflint_san.so with sanitized host code instead."""
+    libflint_san.so with sanitized host code instead, stamps=True the
+    instrumented libflint_stamps.so."""
     if sanitize:
         return _hipcc(SO_SANITIZED, SOURCES, HOST_SANITIZE_FLAGS, verbose)
+    if stamps:
+        return _hipcc(SO_STAMPS, SOURCES, ["-DFLINT_STAMPS"], verbose)
     _hipcc(SO_CEILING, SOURCES_CEILING, [], verbose)
     return _hipcc(SO, SOURCES, [], verbose)
 
@@ -65,4 +73,4 @@ def _hipcc(so: str, sources: list, extra: list, verbose: bool) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True, sanitize="--sanitize" in sys.argv))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv, stamps="--stamps" in sys.argv))

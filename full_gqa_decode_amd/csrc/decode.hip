@@ -858,6 +858,37 @@ __device__ __forceinline__ void vsplit_item(int L, int units, int& unit, int& js
 // before a variable number of page loads (pages are issued under per-page
 // conditions) would be compiled as a wait for every load, pages included.
 // Waves with no start-up work (kKw+2 and up) issue their pages at once.
+// Phase stamps of the slice kernel (the instrumented build only,
+// -DFLINT_STAMPS, which bench.py --stamps loads): per workgroup and wave,
+// s_memrealtime at entry (0), once the scalar inputs are in (1), before the
+// page loads are issued (2), after the pages are consumed (3) and after the
+// output is written (4); slot 6 holds the CU (__smid).  The product build
+// compiles every stamp to nothing.
+#ifdef FLINT_STAMPS
+constexpr int kStampWorkgroups = 1024;
+__device__ unsigned long long g_slice_stamps[kStampWorkgroups * 16 * 8];
+#define SL_STAMP(k)                                                                       \
+  do {                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    const unsigned long long t_ = __builtin_amdgcn_s_memrealtime();                       \
+    if (lane == 0 && blockIdx.x < kStampWorkgroups && w < 16)                             \
+      g_slice_stamps[(blockIdx.x * 16 + w) * 8 + (k)] = t_;                               \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+  } while (0)
+#define SL_STAMP_VALUE(k, v)                                                              \
+  do {                                                                                    \
+    if (lane == 0 && blockIdx.x < kStampWorkgroups && w < 16)                             \
+      g_slice_stamps[(blockIdx.x * 16 + w) * 8 + (k)] = (v);                              \
+  } while (0)
+#else
+#define SL_STAMP(k) \
+  do {              \
+  } while (0)
+#define SL_STAMP_VALUE(k, v) \
+  do {                       \
+  } while (0)
+#endif
+
 template <int WAVES, int MAXP, bool WINDOWED, bool FUSED, bool KV8>
 __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs a) {
   static_assert(WAVES >= kGroup, "one wave per query head of the group");
@@ -870,6 +901,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, gq = lane >> 4;
   const int hq = a.num_kv_heads * kGroup;
+  SL_STAMP(0);
+  SL_STAMP_VALUE(6, __smid());
   // fused: the new K row is normalised by wave kKw, the V row by wave kVw
   constexpr int kKw = WAVES > kGroup ? kGroup : 0;
   constexpr int kVw = WAVES > kGroup + 1 ? kGroup + 1 : 1;
@@ -950,6 +983,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
   asm volatile("" ::"s"(seq_len), "s"(slot), "s"(pg_last_raw));
 #pragma unroll
   for (int k = 0; k < MAXP; ++k) asm volatile("" ::"s"(ids[k]));
+  SL_STAMP(1);
 
   // ---- the request's length ------------------------------------------------
   // A length outside [1, max_seq_len] runs the speculated range and writes
@@ -1055,6 +1089,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
   }
 
   // ---- page loads ------------------------------------------------------------
+  SL_STAMP(2);
   Raw r[MAXP];
   int bad = len_bad;
 #pragma unroll
@@ -1094,6 +1129,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
     }
   }
 
+  SL_STAMP(3);
   // ---- waves -> LDS -> this slice of the output ----------------------------
   const float l_h = sum_xor32(sum_xor16(l_part));
 #pragma unroll
@@ -1134,6 +1170,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void decode_vsplit_kernel(DecodeArgs
     if (any_bad) res = __builtin_nanf("");
     a.out[((int64_t)b * hq + hg) * kHeadDim + js * 16 + d] = res;
   }
+  SL_STAMP(4);
 }
 
 // K3: out_h = sum_s w_s o_s / (e^{sink_h} + sum_s w_s), w_s = 2^{lse_s - M},
@@ -1452,6 +1489,18 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+#ifdef FLINT_STAMPS
+// The last slice-kernel launch's stamps (instrumented build only): copies
+// min(bytes, their size) bytes to host memory at dst.
+extern "C" int flint_stamps_slice(void* dst, size_t bytes) {
+  const size_t n = bytes < sizeof(g_slice_stamps) ? bytes : sizeof(g_slice_stamps);
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_slice_stamps), n, 0, hipMemcpyDeviceToHost) ==
+                 hipSuccess
+             ? 0
+             : -1;
+}
+#endif
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;

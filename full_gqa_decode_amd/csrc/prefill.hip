@@ -128,17 +128,50 @@ __device__ __forceinline__ void read_pair(const unsigned char* buf, int n, int g
     r.v[nb] = *(const u32x4*)(buf + v_slot(nb * 16 + n, gq));
 }
 
+// Phase stamps (the instrumented build only, -DFLINT_STAMPS, which
+// bench.py --stamps loads): per work item (its slot in the item order) and
+// wave, s_memrealtime at item entry (0), once the request's lengths are in
+// (1), once pair 0 is staged (2), after the barrier before the loop (3), at
+// the loop's end (4) and after the output stores (5); slot 6 holds the CU
+// (__smid) and slot 7 the item's page pairs.  The product build compiles
+// every stamp to nothing.
+#ifdef FLINT_STAMPS
+constexpr int kStampItems = 8192;
+__device__ unsigned long long g_prefill_stamps[kStampItems * kPWaves * 8];
+#define PF_STAMP(k)                                                                    \
+  do {                                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+    const unsigned long long t_ = __builtin_amdgcn_s_memrealtime();                    \
+    if (lane == 0 && item < kStampItems) g_prefill_stamps[(item * kPWaves + w) * 8 + (k)] = t_; \
+    __builtin_amdgcn_sched_barrier(0);                                                 \
+  } while (0)
+#define PF_STAMP_VALUE(k, v)                                                           \
+  do {                                                                                 \
+    if (lane == 0 && item < kStampItems) g_prefill_stamps[(item * kPWaves + w) * 8 + (k)] = (v); \
+  } while (0)
+#else
+#define PF_STAMP(k) \
+  do {              \
+  } while (0)
+#define PF_STAMP_VALUE(k, v) \
+  do {                       \
+  } while (0)
+#endif
+
 // One work item: the kRows query rows of row block `tile` of request b, for
 // KV group g.  Every wave of the workgroup runs it (waves without rows still
 // stage pages and meet the barriers); items with no rows return at once.
+// `item` is the item's slot in the item order (it only labels the stamps).
 template <bool WINDOWED, bool KV8>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int g, int b,
-                                             unsigned char (&sm)[2][kBufBytes],
+                                             int64_t item, unsigned char (&sm)[2][kBufBytes],
                                              float (&sm_sink)[kGroup]) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, gq = lane >> 4;
   const int hkv = a.num_kv_heads, hq = hkv * kGroup;
+  PF_STAMP(0);
+  PF_STAMP_VALUE(6, __smid());
 
   const int q0 = a.cu_q_lens[b];
   const int q_len = a.cu_q_lens[b + 1] - q0;
@@ -165,6 +198,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
   const int wg_lo = WINDOWED ? max(0, base + wg_row0 - a.window + 1) : 0;
   const int p_first = wg_lo / kPage, p_last = wg_pos_last / kPage;
   const int npairs = req_bad ? 0 : (p_last - p_first) / 2 + 1;
+#ifdef FLINT_STAMPS
+  asm volatile("" ::"s"(npairs));  // stamp 1 after the lengths have arrived
+#endif
+  PF_STAMP(1);
+  PF_STAMP_VALUE(7, npairs);
 
   // Q operands (tile mt, column n -> row row0 + 2*mt + (n>>3), head
   // g*8 + (n&7)), loaded at start-up, below
@@ -383,12 +421,14 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
     for (int mt = 0; mt < kTiles; ++mt)
 #pragma unroll
       for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(qop[mt][c]));
+    PF_STAMP(2);
     fetch(1, ia1, ib1, kr1, vr1);
     fetch(2, ia2, ib2, kr0, vr0);
     load_ids(3, ia1, ib1);
     load_ids(4, ia0, ib0);
   }
   __syncthreads();
+  PF_STAMP(3);
   // every wave has left the previous item's epilogue (the last reader of
   // sm_sink) by the barrier above; the loop's first barrier publishes this
   if (npairs > 0 && tid < kGroup) sm_sink[tid] = sink_l2;
@@ -405,6 +445,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
     load_ids(i + 6, ia0, ib0);
     __syncthreads();
   }
+  PF_STAMP(4);
   if (!active) return;
 
   bad = __any(bad);
@@ -432,6 +473,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
         dst[nb * 16] = bad ? __builtin_nanf("") : acc[mt][nb][i] * so * inv * vs;
     }
   }
+  PF_STAMP(5);
 }
 
 // Persistent grid: at most kPrefillWorkgroups workgroups (one per CU), each
@@ -456,11 +498,24 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     if (slot >= nitems) break;
     const int tile = ntile - 1 - (int)(slot / per_tile);
     const int rest = (int)(slot % per_tile);
-    prefill_item<WINDOWED, KV8>(a, tile, rest % a.num_kv_heads, rest / a.num_kv_heads, sm, sm_sink);
+    prefill_item<WINDOWED, KV8>(a, tile, rest % a.num_kv_heads, rest / a.num_kv_heads, slot, sm,
+                                sm_sink);
   }
 }
 
 }  // namespace
+
+#ifdef FLINT_STAMPS
+// The last launch's prefill stamps (instrumented build only): copies
+// min(bytes, their size) bytes to host memory at dst.
+extern "C" int flint_stamps_prefill(void* dst, size_t bytes) {
+  const size_t n = bytes < sizeof(g_prefill_stamps) ? bytes : sizeof(g_prefill_stamps);
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_prefill_stamps), n, 0, hipMemcpyDeviceToHost) ==
+                 hipSuccess
+             ? 0
+             : -1;
+}
+#endif
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
