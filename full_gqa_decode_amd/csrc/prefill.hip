@@ -158,14 +158,53 @@ __device__ unsigned long long g_prefill_stamps[kStampItems * kPWaves * 8];
   } while (0)
 #endif
 
-// One work item: the kRows query rows of row block `tile` of request b, for
-// KV group g.  Every wave of the workgroup runs it (waves without rows still
-// stage pages and meet the barriers); items with no rows return at once.
-// `item` is the item's slot in the item order (it only labels the stamps).
+// A request's lengths as the kernel last read them (items of one request
+// reuse them), and the page range of one of its row blocks.
+struct ReqLens {
+  int b, q0, q_len, seq_len;
+};
+
+// The page range [pf, pl] of row block `tile` of a request with lengths rl;
+// false when the block has no page pairs to walk (no rows, a request outside
+// q/out or an invalid one).  The same range prefill_item walks.
+template <bool WINDOWED>
+__device__ __forceinline__ bool item_pages(const PrefillArgs& a, int tile, const ReqLens& rl,
+                                           int& pf, int& pl) {
+  const int wg_row0 = tile * kRows;
+  if (rl.q_len <= 0 || wg_row0 >= rl.q_len || rl.q0 < 0 ||
+      (int64_t)rl.q0 + rl.q_len > a.total_q)
+    return false;
+  if (rl.q_len > a.max_q_len || rl.seq_len > a.max_seq_len || rl.q_len > rl.seq_len) return false;
+  const int base = rl.seq_len - rl.q_len;
+  const int wg_pos_last = base + min(wg_row0 + kRows, rl.q_len) - 1;
+  const int wg_lo = WINDOWED ? max(0, base + wg_row0 - a.window + 1) : 0;
+  pf = wg_lo / kPage;
+  pl = wg_pos_last / kPage;
+  return true;
+}
+
+// Page ids handed from one item to the next of the same request: pairs 0..2
+// of the next item, requested after the current item's last pair (ids[2j],
+// ids[2j+1] = the table entries of pair j's two pages).
+struct IdCarry {
+  int ids[6];
+  bool valid;
+};
+
+// One work item: the kRows query rows of row block `tile` of request rl.b,
+// for KV group g.  Every wave of the workgroup runs it (waves without rows
+// still stage pages and meet the barriers); items with no rows return at
+// once.  `item` is the item's slot in the item order (it only labels the
+// stamps).  carry: in, the ids of this item's first three pairs if valid; out,
+// those of the next item (next_ok: it belongs to the same request and walks
+// [next_pf, next_pl]).
 template <bool WINDOWED, bool KV8>
-__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int g, int b,
-                                             int64_t item, unsigned char (&sm)[2][kBufBytes],
-                                             float (&sm_sink)[kGroup]) {
+__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int g,
+                                             const ReqLens& rl, int64_t item,
+                                             unsigned char (&sm)[2][kBufBytes],
+                                             float (&sm_sink)[kGroup], IdCarry& carry,
+                                             bool next_ok, int next_pf, int next_pl) {
+  const int b = rl.b;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, gq = lane >> 4;
@@ -173,9 +212,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
   PF_STAMP(0);
   PF_STAMP_VALUE(6, __smid());
 
-  const int q0 = a.cu_q_lens[b];
-  const int q_len = a.cu_q_lens[b + 1] - q0;
-  const int seq_len = a.seq_lens[b];
+  const int q0 = rl.q0, q_len = rl.q_len, seq_len = rl.seq_len;
+  const bool carried = carry.valid;
+  carry.valid = false;
   const int wg_row0 = tile * kRows;
   if (q_len <= 0 || wg_row0 >= q_len) return;  // no rows in this workgroup
   // rows outside q / out: a request whose cu_q_lens range leaves
@@ -400,9 +439,15 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
   float sink_l2 = 0.f;
   if (npairs > 0) {
     const float sink = a.sinks[g * kGroup + (lane & 7)];
-    load_ids(0, ia0, ib0);
-    load_ids(1, ia1, ib1);
-    load_ids(2, ia2, ib2);
+    if (carried) {  // requested by the previous item, after its last pair
+      ia0 = carry.ids[0], ib0 = carry.ids[1];
+      ia1 = carry.ids[2], ib1 = carry.ids[3];
+      ia2 = carry.ids[4], ib2 = carry.ids[5];
+    } else {
+      load_ids(0, ia0, ib0);
+      load_ids(1, ia1, ib1);
+      load_ids(2, ia2, ib2);
+    }
 #pragma unroll
     for (int mt = 0; mt < kTiles; ++mt) {
       const int r = min(row0 + 2 * mt + (n >> 3), q_len - 1);
@@ -446,6 +491,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
     __syncthreads();
   }
   PF_STAMP(4);
+  // the next item's first page ids, before this item's output stores (the
+  // id registers are free: the last pair has been fetched)
+  if (next_ok) {
+    const int* nrow = a.block_tables + (int64_t)b * a.bt_stride;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int p = min(next_pf + 2 * j, next_pl);
+      carry.ids[2 * j] = nrow[p];
+      carry.ids[2 * j + 1] = nrow[min(p + 1, next_pl)];
+    }
+    carry.valid = true;
+  }
   if (!active) return;
 
   bad = __any(bad);
@@ -493,13 +550,36 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int64_t per_tile = (int64_t)a.num_kv_heads * a.num_seqs;
   const int64_t nitems = per_tile * ntile;
   const int G = gridDim.x;
+  auto slot_of = [&](int64_t r) {
+    return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+  };
+  ReqLens rl = {-1, 0, 0, 0};
+  IdCarry carry;
+  carry.valid = false;
   for (int64_t r = 0;; ++r) {
-    const int64_t slot = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    const int64_t slot = slot_of(r);
     if (slot >= nitems) break;
     const int tile = ntile - 1 - (int)(slot / per_tile);
     const int rest = (int)(slot % per_tile);
-    prefill_item<WINDOWED, KV8>(a, tile, rest % a.num_kv_heads, rest / a.num_kv_heads, slot, sm,
-                                sm_sink);
+    const int b = rest / a.num_kv_heads;
+    if (b != rl.b) {
+      rl.b = b;
+      rl.q0 = a.cu_q_lens[b];
+      rl.q_len = a.cu_q_lens[b + 1] - rl.q0;
+      rl.seq_len = a.seq_lens[b];
+    }
+    // the next item, if it belongs to the same request: its page range
+    const int64_t nslot = slot_of(r + 1);
+    bool next_ok = false;
+    int next_pf = 0, next_pl = 0;
+    if (nslot < nitems) {
+      const int nrest = (int)(nslot % per_tile);
+      if (nrest / a.num_kv_heads == b)
+        next_ok = item_pages<WINDOWED>(a, ntile - 1 - (int)(nslot / per_tile), rl, next_pf,
+                                       next_pl);
+    }
+    prefill_item<WINDOWED, KV8>(a, tile, rest % a.num_kv_heads, rl, slot, sm, sm_sink, carry,
+                                next_ok, next_pf, next_pl);
   }
 }
 
