@@ -935,8 +935,7 @@ def bench_stamps(dev):
         npairs = st[:, 0, 7]
         ph = np.diff(t, axis=2).mean(1)   # per item, mean over waves
         grid = 256
-        slot = np.arange(items)
-        wg = np.where((slot // grid) % 2 == 0, slot % grid, grid - 1 - slot % grid)
+        wg = st[:, 0, 6] >> 16            # the workgroup that ran the item
         start, end = t[:, :, 0].min(1), t[:, :, 5].max(1)
         gaps, ends = [], []
         for g in range(grid):
@@ -950,7 +949,10 @@ def bench_stamps(dev):
             "pair0_to_loop": stats(ph[:, 2]), "loop": stats(ph[:, 3]),
             "loop_per_pair": stats(ph[:, 3] / np.maximum(npairs, 1)),
             "epilogue": stats(ph[:, 4]), "gap_between_items": stats(np.array(gaps)),
-            "workgroup_end_min_max": [round(float(min(ends)), 1), round(float(max(ends)), 1)]}
+            "workgroup_end_min_max": [round(float(min(ends)), 1), round(float(max(ends)), 1)],
+            "workgroup_end_mean": round(float(np.mean(ends)), 1),
+            "items_per_workgroup_min_max": [int(np.bincount(wg, minlength=grid).min()),
+                                            int(np.bincount(wg, minlength=grid).max())]}
     # one fused sliding-layer step at batch 1 (32 slice workgroups)
     eps = float(np.float32(1e-6))
     L = fl.layer(window=WINDOW, use_rope=1, rms_eps=eps)
@@ -1038,7 +1040,9 @@ def prefill_leg(fl, dev, window, fp8=False):
     cu = up(np.array([0, T], np.int32))
     sl = up(np.array([T], np.int32))
     btd = up(bt)
-    run = lambda: fl.flint_attn_prefill(L, qb, cu, T, kc, vc, btd, sl, T, sinks, out)
+    ws = torch.zeros(max(8, fl.flint_attn_prefill_workspace_size(L, 1, T, T)), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: fl.flint_attn_prefill(L, qb, cu, T, kc, vc, btd, sl, T, sinks, out, ws)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     run()

@@ -393,7 +393,9 @@ def flint_attn_prefill(L: FlintAttnLayer, q, cu_q_lens, max_q_len: int, k_cache,
                        block_tables, seq_lens, max_seq_len: int, sinks, out, workspace=None,
                        stream=None):
     """Causal prefill for the rows in cu_q_lens; q bf16 bits [total_q, Hq, 128],
-    out fp32 [total_q, Hq, 128]."""
+    out fp32 [total_q, Hq, 128].  workspace: a device tensor of at least
+    flint_attn_prefill_workspace_size bytes holding zeros (each call leaves it
+    so), or None for a fresh zero-filled one."""
     torch = _torch()
     B = cu_q_lens.shape[0] - 1
     Hq, D = L.num_q_heads, L.head_dim
@@ -401,8 +403,8 @@ def flint_attn_prefill(L: FlintAttnLayer, q, cu_q_lens, max_q_len: int, k_cache,
            k_cache=(k_cache, _cache_elems(L, k_cache)), v_cache=(v_cache, _cache_elems(L, k_cache)),
            block_tables=(block_tables, 0), seq_lens=(seq_lens, B), sinks=(sinks, Hq))
     need = flint_attn_prefill_workspace_size(L, B, max_q_len, max_seq_len)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None and need > 0:  # zero-filled; every call leaves it zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().flint_attn_prefill(
         C.byref(L), B, _ptr(q, _b16(), "q"), _ptr(cu_q_lens, _i32(), "cu_q_lens"), q.shape[0],

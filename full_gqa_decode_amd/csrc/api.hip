@@ -545,11 +545,9 @@ flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32
 
 size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_seq_len) {
-  (void)L;
-  (void)num_seqs;
-  (void)max_q_len;
   (void)max_seq_len;
-  return 0;
+  if (!L) return 0;
+  return flint::prefill_workspace_bytes(num_seqs, L->num_kv_heads, max_q_len);
 }
 
 flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, const uint16_t* q,
@@ -559,8 +557,6 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
                                 int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len,
                                 const float* sinks, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   flint_status st = check_layer(L);
   if (st != FLINT_OK) return st;
   if (num_seqs < 0) return fail(FLINT_ERR_INVALID_ARGUMENT, "num_seqs %d < 0", num_seqs);
@@ -601,6 +597,13 @@ flint_status flint_attn_prefill(const flint_attn_layer* L, int32_t num_seqs, con
   a.kv_fp8 = L->kv_dtype == FLINT_KV_FP8_E4M3;
   a.qscale = L->softmax_scale * 1.4426950408889634f * (a.kv_fp8 ? L->k_scale : 1.f);
   a.v_scale = a.kv_fp8 ? L->v_scale : 1.f;
+  const size_t need = flint::prefill_workspace_bytes(num_seqs, L->num_kv_heads, max_q_len);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FLINT_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                need);
+  if (need > 0 && !aligned(workspace, 8))
+    return fail(FLINT_ERR_INVALID_ARGUMENT, "workspace must be 8-byte aligned");
+  a.claims = need > 0 ? (unsigned long long*)workspace : nullptr;
   return hip_status(flint::launch_prefill(a, (hipStream_t)stream), "prefill launch");
 }
 

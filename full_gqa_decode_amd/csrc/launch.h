@@ -92,8 +92,12 @@ struct PrefillArgs {
   float qscale;              // softmax_scale * log2(e) (* k_scale for an fp8 cache)
   int32_t kv_fp8;
   float v_scale;             // multiplies the output (1 for bf16)
+  unsigned long long* claims;  // item counter (prefill_workspace_bytes > 0), else null
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+// Workspace of a prefill launch: one item counter when the items outnumber
+// the persistent grid, else none.
+size_t prefill_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t max_q_len);
 
 // Waves per decode workgroup: kDecodeWaves when the key range is split (two
 // workgroups per CU), kDecodeWavesSingle when one workgroup covers a short

@@ -132,8 +132,9 @@ __device__ __forceinline__ void read_pair(const unsigned char* buf, int n, int g
 // bench.py --stamps loads): per work item (its slot in the item order) and
 // wave, s_memrealtime at item entry (0), once the request's lengths are in
 // (1), once pair 0 is staged (2), after the barrier before the loop (3), at
-// the loop's end (4) and after the output stores (5); slot 6 holds the CU
-// (__smid) and slot 7 the item's page pairs.  The product build compiles
+// the loop's end (4) and after the output stores (5); slot 6 holds the
+// workgroup (bits 16 up) and the CU (__smid, the low 16 bits) and slot 7 the
+// item's page pairs.  The product build compiles
 // every stamp to nothing.
 #ifdef FLINT_STAMPS
 constexpr int kStampItems = 8192;
@@ -191,35 +192,86 @@ struct IdCarry {
   bool valid;
 };
 
+// The item order: row blocks from the last down (longest key range first),
+// then KV group, then request.  The first nfixed items are dealt out in
+// rounds of gridDim.x, every other round in reverse; the rest are claimed one
+// at a time from a counter in the workspace by whichever workgroup frees up
+// first, so CUs that run faster take more of them.  With more items than
+// workgroups the last third of the rounds is claimed (for one causal request
+// ~11% of the work, for equal items a third); with no more, every workgroup
+// runs one item and nothing is claimed.
+// a value every lane holds alike, in scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+struct ItemOrder {
+  int ntile;                 // row blocks of the longest request
+  int64_t per_tile, nitems;  // items per row block (groups x requests), all items
+  int64_t nfixed;            // items dealt out in fixed rounds
+  unsigned long long last_claim;  // value of the launch's last claim
+};
+
+__device__ __forceinline__ ItemOrder item_order(const PrefillArgs& a, int G) {
+  ItemOrder o;
+  o.ntile = (a.max_q_len + kRows - 1) / kRows;
+  o.per_tile = (int64_t)a.num_kv_heads * a.num_seqs;
+  o.nitems = o.per_tile * o.ntile;
+  const int64_t rounds = (o.nitems + G - 1) / G;
+  o.nfixed = o.nitems <= G ? o.nitems : (rounds - (rounds + 2) / 3) * G;
+  // every workgroup claims until a claim fails: nitems - nfixed claims that
+  // succeed and one per workgroup that does not
+  o.last_claim = (unsigned long long)(o.nitems - o.nfixed + G - 1);
+  return o;
+}
+
 // One work item: the kRows query rows of row block `tile` of request rl.b,
-// for KV group g.  Every wave of the workgroup runs it (waves without rows
-// still stage pages and meet the barriers); items with no rows return at
-// once.  `item` is the item's slot in the item order (it only labels the
-// stamps).  carry: in, the ids of this item's first three pairs if valid; out,
-// those of the next item (next_ok: it belongs to the same request and walks
-// [next_pf, next_pl]).
+// for KV group g, at slot `item` of the item order.  Every wave of the
+// workgroup runs it (waves without rows still stage pages and meet the
+// barriers); items with no rows return at once.  Returns the slot of the
+// workgroup's next item: next_fixed, or when `claim` the one claimed during
+// this item.  Wave 0's lane 0 takes the claim (early, so that it has returned
+// by the time pair 0 has been staged) and writes it to sm_claim[par] before
+// a barrier; every wave reads it after that barrier.  par alternates between
+// a workgroup's items: a wave may still read one item's claim while wave 0
+// writes the next one's.  carry: in, the ids of this item's first three pairs
+// if valid; out, those of the next item when it belongs to the same request.
 template <bool WINDOWED, bool KV8>
-__device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int g,
-                                             const ReqLens& rl, int64_t item,
-                                             unsigned char (&sm)[2][kBufBytes],
-                                             float (&sm_sink)[kGroup], IdCarry& carry,
-                                             bool next_ok, int next_pf, int next_pl) {
+__device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const ItemOrder& o,
+                                                int tile, int g, const ReqLens& rl, int64_t item,
+                                                unsigned char (&sm)[2][kBufBytes],
+                                                float (&sm_sink)[kGroup], int64_t (&sm_claim)[2],
+                                                int par, IdCarry& carry, bool claim,
+                                                int64_t next_fixed) {
   const int b = rl.b;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, gq = lane >> 4;
   const int hkv = a.num_kv_heads, hq = hkv * kGroup;
   PF_STAMP(0);
-  PF_STAMP_VALUE(6, __smid());
+  PF_STAMP_VALUE(6, ((unsigned long long)blockIdx.x << 16) | __smid());
 
   const int q0 = rl.q0, q_len = rl.q_len, seq_len = rl.seq_len;
   const bool carried = carry.valid;
   carry.valid = false;
   const int wg_row0 = tile * kRows;
-  if (q_len <= 0 || wg_row0 >= q_len) return;  // no rows in this workgroup
-  // rows outside q / out: a request whose cu_q_lens range leaves
-  // [0, total_q) is not touched at all (no row of it can be located safely)
-  if (q0 < 0 || (int64_t)q0 + q_len > a.total_q) return;
+  // the claim's value as wave 0 publishes it; the last claim of the launch
+  // leaves the counter at zero for the next one
+  auto publish = [&](unsigned long long c) {
+    sm_claim[par] = (int64_t)c;
+    if (c == o.last_claim) atomicExch(a.claims, 0ull);
+  };
+  // no rows in this workgroup, or rows outside q / out: a request whose
+  // cu_q_lens range leaves [0, total_q) is not touched at all (no row of it
+  // can be located safely)
+  if (q_len <= 0 || wg_row0 >= q_len || q0 < 0 || (int64_t)q0 + q_len > a.total_q) {
+    if (!claim) return next_fixed;
+    if (tid == 0) publish(atomicAdd(a.claims, 1ull));
+    __syncthreads();
+    return o.nfixed + uniform64(sm_claim[par]);
+  }
   const bool req_bad = q_len > a.max_q_len || seq_len > a.max_seq_len || q_len > seq_len;
   const int base = seq_len - q_len;  // position of row 0
 
@@ -437,6 +489,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
   u32x4 kr0, vr0, kr1, vr1;
   int ia0, ib0, ia1, ib1, ia2, ib2;
   float sink_l2 = 0.f;
+  unsigned long long cval = 0;
   if (npairs > 0) {
     const float sink = a.sinks[g * kGroup + (lane & 7)];
     if (carried) {  // requested by the previous item, after its last pair
@@ -456,9 +509,13 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
 #pragma unroll
       for (int c = 0; c < 4; ++c) qop[mt][c] = *(const bf16x8*)(qp + c * 32);
     }
+    // after the ids (the wait for them does not wait for the claim), before
+    // pair 0's pages (the wait for them does)
+    if (claim && tid == 0) cval = atomicAdd(a.claims, 1ull);
     fetch(0, ia0, ib0, kr0, vr0);  // waits for the ids, hence for the sinks
     sink_l2 = sink * kLog2e;
     stage_pair<KV8>(sm[0], tid, kr0, vr0);
+    if (claim && tid == 0) publish(cval);
     // Q and the sinks were issued before pair 0, so they are in; pinning
     // them here keeps the compiler from waiting for them inside the loop,
     // where it could not tell them from the page loads in flight
@@ -471,12 +528,20 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
     fetch(2, ia2, ib2, kr0, vr0);
     load_ids(3, ia1, ib1);
     load_ids(4, ia0, ib0);
+  } else if (claim && tid == 0) {
+    publish(atomicAdd(a.claims, 1ull));
   }
   __syncthreads();
   PF_STAMP(3);
   // every wave has left the previous item's epilogue (the last reader of
   // sm_sink) by the barrier above; the loop's first barrier publishes this
   if (npairs > 0 && tid < kGroup) sm_sink[tid] = sink_l2;
+  // the next item, and its page range if it belongs to this request
+  const int64_t next = claim ? o.nfixed + uniform64(sm_claim[par]) : next_fixed;
+  bool next_ok = false;
+  int next_pf = 0, next_pl = 0;
+  if (next < o.nitems && (int)(next % o.per_tile) / hkv == b)
+    next_ok = item_pages<WINDOWED>(a, o.ntile - 1 - (int)(next / o.per_tile), rl, next_pf, next_pl);
   for (int i = 0; i < npairs; i += 2) {
     compute(i);
     if (i + 1 < npairs) stage_pair<KV8>(sm[1], tid, kr1, vr1);
@@ -503,7 +568,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
     }
     carry.valid = true;
   }
-  if (!active) return;
+  if (!active) return next;
 
   bad = __any(bad);
   // epilogue: acc rows gq*4+i are query vectors; their m and l live in lane gq*4+i
@@ -531,36 +596,33 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, int tile, int
     }
   }
   PF_STAMP(5);
+  return next;
 }
 
 // Persistent grid: at most kPrefillWorkgroups workgroups (one per CU), each
-// looping over items.  Items are ordered longest key range first (row blocks
-// from the last down, then KV group, then request) and dealt out in rounds of
-// gridDim.x, every other round in reverse, so each workgroup's total is
-// balanced (for one causal request, exactly up to the last partial round).
-// Handing items to workgroups here rather than launching one workgroup per
-// item leaves no dispatch gaps: MI355X deals workgroups to its 8 XCDs in
-// turn, so with items of unequal length a CU that frees up waits until the
-// XCD whose turn it is has a free CU too.
+// looping over items in the order of ItemOrder: fixed rounds first, balanced
+// by the longest-first zig-zag deal, then claimed items, which even out the
+// CUs' differing speeds.  Handing items to workgroups here rather than
+// launching one workgroup per item leaves no dispatch gaps: MI355X deals
+// workgroups to its 8 XCDs in turn, so with items of unequal length a CU that
+// frees up waits until the XCD whose turn it is has a free CU too.
 template <bool WINDOWED, bool KV8>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sm[2][kBufBytes];
   __shared__ float sm_sink[kGroup];  // log2-scaled sinks of the current item's heads
-  const int ntile = (a.max_q_len + kRows - 1) / kRows;
-  const int64_t per_tile = (int64_t)a.num_kv_heads * a.num_seqs;
-  const int64_t nitems = per_tile * ntile;
+  __shared__ int64_t sm_claim[2];    // claimed item offsets, alternating between items
   const int G = gridDim.x;
+  const ItemOrder o = item_order(a, G);
   auto slot_of = [&](int64_t r) {
     return r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
   };
   ReqLens rl = {-1, 0, 0, 0};
   IdCarry carry;
   carry.valid = false;
-  for (int64_t r = 0;; ++r) {
-    const int64_t slot = slot_of(r);
-    if (slot >= nitems) break;
-    const int tile = ntile - 1 - (int)(slot / per_tile);
-    const int rest = (int)(slot % per_tile);
+  int64_t slot = slot_of(0);
+  for (int64_t r = 0; slot < o.nitems; ++r) {
+    const int tile = o.ntile - 1 - (int)(slot / o.per_tile);
+    const int rest = (int)(slot % o.per_tile);
     const int b = rest / a.num_kv_heads;
     if (b != rl.b) {
       rl.b = b;
@@ -568,18 +630,11 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
       rl.q_len = a.cu_q_lens[b + 1] - rl.q0;
       rl.seq_len = a.seq_lens[b];
     }
-    // the next item, if it belongs to the same request: its page range
-    const int64_t nslot = slot_of(r + 1);
-    bool next_ok = false;
-    int next_pf = 0, next_pl = 0;
-    if (nslot < nitems) {
-      const int nrest = (int)(nslot % per_tile);
-      if (nrest / a.num_kv_heads == b)
-        next_ok = item_pages<WINDOWED>(a, ntile - 1 - (int)(nslot / per_tile), rl, next_pf,
-                                       next_pl);
-    }
-    prefill_item<WINDOWED, KV8>(a, tile, rest % a.num_kv_heads, rl, slot, sm, sm_sink, carry,
-                                next_ok, next_pf, next_pl);
+    // the next item is claimed from its last fixed one on
+    const bool claim = o.nfixed < o.nitems && (r + 1) * G >= o.nfixed;
+    slot = prefill_item<WINDOWED, KV8>(a, o, tile, rest % a.num_kv_heads, rl, slot, sm, sm_sink,
+                                       sm_claim, (int)(r & 1), carry, claim,
+                                       claim ? o.nitems : slot_of(r + 1));
   }
 }
 
@@ -597,10 +652,21 @@ extern "C" int flint_stamps_prefill(void* dst, size_t bytes) {
 }
 #endif
 
+static int64_t prefill_items(int32_t num_seqs, int32_t num_kv_heads, int32_t max_q_len) {
+  return (int64_t)((max_q_len + kRows - 1) / kRows) * num_kv_heads * num_seqs;
+}
+
+size_t prefill_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t max_q_len) {
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_q_len <= 0) return 0;
+  return prefill_items(num_seqs, num_kv_heads, max_q_len) > kPrefillWorkgroups
+             ? sizeof(unsigned long long)
+             : 0;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
-  const int64_t items =
-      (int64_t)((a.max_q_len + kRows - 1) / kRows) * a.num_kv_heads * a.num_seqs;
+  const int64_t items = prefill_items(a.num_seqs, a.num_kv_heads, a.max_q_len);
+  if (items > kPrefillWorkgroups && !a.claims) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(items < kPrefillWorkgroups ? items : kPrefillWorkgroups));
   if (a.kv_fp8) {
     if (a.window > 0)

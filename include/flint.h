@@ -23,7 +23,8 @@
  * Conventions for every call
  *   - Pointers are DEVICE pointers unless stated otherwise, owned by the
  *     caller.  The library never allocates or frees memory and keeps no state
- *     between calls; scratch space comes from the caller's workspace.
+ *     between calls; scratch space comes from the caller's workspace (the
+ *     prefill's work-item counter in it is zero before and after a call).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     All work is enqueued on it; no call synchronises or reads device memory
  *     back, so every call can be captured into a HIP graph.
@@ -314,6 +315,13 @@ flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32
  * whose rows cu_q_lens[b] .. cu_q_lens[b+1]-1 do not lie inside
  * [0, total_q) is skipped: none of q or out is touched for it.
  * An fp8 cache is widened to bf16 (exactly) as its pages are staged.
+ * Workspace: flint_attn_prefill_workspace_size bytes (0 when the work items,
+ * ceil(max_q_len / 32) x num_kv_heads x num_seqs, number at most 256;
+ * otherwise 8: one work-item counter), 8-byte aligned.  It must hold zeros
+ * when the call runs, and every call leaves it zero again, so one zero-fill
+ * when it is allocated serves every later call; calls that overlap in time
+ * must not share it.  A call that fails its host-side checks does not touch
+ * it.  Too small or NULL: FLINT_ERR_WORKSPACE_TOO_SMALL.
  */
 size_t flint_attn_prefill_workspace_size(const flint_attn_layer* L, int32_t num_seqs,
                                          int32_t max_q_len, int32_t max_seq_len);

@@ -203,6 +203,33 @@ def test_prefill_rejects_bad_arguments():
     assert lib.flint_attn_prefill(*empty) == 0
 
 
+def test_prefill_workspace_is_one_counter_past_one_item_per_workgroup():
+    # work items: ceil(max_q_len / 32) row blocks x KV heads x requests; the
+    # persistent grid has 256 workgroups, and past 256 items the later ones
+    # are claimed from an 8-byte counter in the workspace
+    L = fl.full_layer()
+    size = fl.flint_attn_prefill_workspace_size
+    assert size(L, 1, 64 * 32, 4096) == 0          # 64 x 4 x 1 = 256 items
+    assert size(L, 1, 64 * 32 + 1, 4096) == 8      # 65 row blocks: 260
+    assert size(L, 64, 32, 4096) == 0 and size(L, 65, 32, 4096) == 8
+    assert size(L, 1, 32768, 32768) == 8 and size(L, 0, 32768, 32768) == 0
+    L1 = fl.full_layer(num_q_heads=8, num_kv_heads=1)
+    assert size(L1, 1, 256 * 32, 8192) == 0 and size(L1, 1, 256 * 32 + 1, 8192) == 8
+    lib = fl.lib()
+    # 128 row blocks x 4 heads = 512 items: a workspace is required, checked
+    # before anything is launched
+    base = [C.byref(L), 1, P, P + 0x10000, 4096, 4096, Q, Q + 0x10000, 256, P + 0x20000, 256,
+            P + 0x30000, 4096, P + 0x40000, P + 0x50000, None, 0, None]
+    assert lib.flint_attn_prefill(*base) == WS_SMALL
+    assert "need 8" in lib.flint_last_error().decode()
+    small = list(base)
+    small[15], small[16] = P + 0x60000, 4
+    assert lib.flint_attn_prefill(*small) == WS_SMALL
+    misaligned = list(base)
+    misaligned[15], misaligned[16] = P + 0x60004, 8
+    assert lib.flint_attn_prefill(*misaligned) == INVALID
+
+
 def test_decode_plan_covers_every_page():
     L = fl.full_layer()
     for B, ctx, pps in ((1, 100000, 0), (1, 4096, 0), (64, 131072, 0), (3, 17, 0), (1, 100000, 7)):

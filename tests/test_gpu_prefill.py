@@ -67,7 +67,7 @@ class PrefillCase:
         return oracle.attn_prefill(self.L, full_q, self.cu, kc, vc, self.bt, self.seq_lens,
                                    self.sinks, rows=None if rows is None else idx)
 
-    def run_gpu(self, bt=None, seq_lens=None):
+    def run_gpu(self, bt=None, seq_lens=None, workspace=None):
         import torch
         import full_gqa_decode_amd as fl
         kd, vd = empty_caches(self.L, self.num_blocks, device=True)
@@ -81,7 +81,7 @@ class PrefillCase:
         bt = self.bt if bt is None else bt
         sl = self.seq_lens if seq_lens is None else seq_lens
         fl.flint_attn_prefill(self.FL, qc, up(self.cu), self.max_q, kd, vd, up(bt), up(sl),
-                              int(self.seq_lens.max()), up(self.sinks), out)
+                              int(self.seq_lens.max()), up(self.sinks), out, workspace)
         torch.cuda.synchronize()
         return out.cpu().numpy(), kd, vd, qb
 
@@ -227,6 +227,38 @@ def test_prefill_many_requests_more_items_than_workgroups(window):
     assert_parity(got[good], want[good])
 
 
+def _sample(n, stride=7):
+    rows = np.concatenate([np.arange(min(n, 64)), np.arange(3, n, stride), np.arange(n - 64, n)])
+    return np.unique(rows[(rows >= 0) & (rows < n)])
+
+
+@pytest.mark.parametrize("window,hkv,reqs", [
+    (513, 1, [(257 * 32, 257 * 32)]),                             # 257 items: one claimed
+    (0, 4, [(65 * 32 + 5, 65 * 32)]),                             # 260 items
+    (513, 2, [(3000, 1500), (40, 40), (900, 0), (2100, 2000)]),   # 504, many without rows
+])
+def test_prefill_claimed_items_share_one_workspace_across_calls(window, hkv, reqs):
+    # Past 256 work items the persistent grid claims the later ones from a
+    # counter in the workspace, which must be zero when a call starts and
+    # which every call leaves zero: two calls in a row on one workspace give
+    # the same, correct output and leave it zero.
+    import torch
+    import full_gqa_decode_amd as fl
+    case = PrefillCase(15, reqs, window=window, hkv=hkv)
+    need = fl.flint_attn_prefill_workspace_size(case.FL, len(reqs), case.max_q,
+                                                int(case.seq_lens.max()))
+    assert need == 8
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    first, _, _, _ = case.run_gpu(workspace=ws)
+    assert not ws.any().item()
+    second, _, _, _ = case.run_gpu(workspace=ws)
+    assert not ws.any().item()
+    assert np.array_equal(first, second)
+    rows = _sample(len(case.chunk_rows))
+    want = case.expected(rows=rows)
+    assert_parity(first[rows], want[rows])
+
+
 def test_prefill_graph_replays_match_eager():
     import torch
     import full_gqa_decode_amd as fl
@@ -250,6 +282,38 @@ def test_prefill_graph_replays_match_eager():
         # eager work between replays
         fl.flint_attn_prefill(case.FL, qc, cu, case.max_q, kd, vd, bt, sl,
                               int(case.seq_lens.max()), sk, torch.empty_like(out))
+        torch.cuda.synchronize()
+
+
+def test_prefill_graph_with_claimed_items_replays_match_eager():
+    # 7 row blocks x 4 heads x 24 requests = 672 items, the later ones claimed:
+    # each replay finds the counter the previous launch left at zero
+    import torch
+    import full_gqa_decode_amd as fl
+    reqs = _many_requests()
+    case = PrefillCase(16, reqs, window=513)
+    eager, kd, vd, qb = case.run_gpu()
+    qc = qb[torch.from_numpy(case.chunk_rows).to(dev())].contiguous()
+    cu, bt, sl, sk = up(case.cu), up(case.bt), up(case.seq_lens), up(case.sinks)
+    ws = torch.zeros(8, dtype=torch.uint8, device=dev())
+    out = torch.empty((len(case.chunk_rows), 32, 128), dtype=torch.float32, device=dev())
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fl.flint_attn_prefill(case.FL, qc, cu, case.max_q, kd, vd, bt, sl,
+                                  int(case.seq_lens.max()), sk, out, ws)
+    torch.cuda.synchronize()
+    assert not ws.any().item()  # captured, not run
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager)
+        assert not ws.any().item()
+        fl.flint_attn_prefill(case.FL, qc, cu, case.max_q, kd, vd, bt, sl,
+                              int(case.seq_lens.max()), sk, torch.empty_like(out), ws)
         torch.cuda.synchronize()
 
 
