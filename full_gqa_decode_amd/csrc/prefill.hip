@@ -42,6 +42,7 @@ constexpr int kTiles = 2;                    // 16-vector MFMA tiles per wave
 // value MFMAs with the softmax (see compute() below)
 constexpr int kSchedValu = 0x002, kSchedMfma = 0x008;
 constexpr int kSoftmaxValuFirst = 40, kValuPerMfma = 2;
+constexpr int kFastValuFirst = 20, kFastValuPerMfma = 3;
 constexpr int kWaveRows = kTiles * 2;        // query rows per wave
 constexpr int kPWaves = 8;                   // waves per workgroup
 constexpr int kPThreads = kPWaves * 64;
@@ -59,7 +60,14 @@ constexpr int kPrefillWorkgroups = 256;      // persistent grid: one workgroup p
 constexpr int kKStride = kHeadDim * 2;
 constexpr int kVStride = 2 * kPage * 2;
 constexpr int kKBytes = 2 * kPage * kKStride;
+// V is staged as fp16, the value MFMA's operand.
 constexpr int kBufBytes = kKBytes + kHeadDim * kVStride;
+// P enters the value MFMA as fp16(p * kPScale): p < 2^8 (the lazy max), so
+// p * 2^7 < 2^15 stays inside fp16's range and small p stay normal down to
+// 2^-21; the output is scaled back by 1/kPScale.
+constexpr float kPScale = 128.f, kPScaleLog2 = 7.f;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 static_assert(kPThreads == 2 * 256, "staging: one K and one V 16-byte chunk per thread");
 
 __device__ __forceinline__ int k_slot(int r, int ch) { return r * kKStride + ((ch ^ (r & 15)) << 4); }
@@ -99,22 +107,49 @@ __device__ __forceinline__ void fetch_pair(const PrefillArgs& a, int pga, int pg
   }
 }
 
-template <bool KV8>
+// Two fp8 codes (byte pair HI of w) or two bf16 values (a word) as fp16,
+// exactly (every E4M3 value is an fp16 number; a bf16 value is one when its
+// magnitude is at most 65504, and a larger one becomes +-inf).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const float lo = __builtin_bit_cast(float, w << 16);
+  const float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+}
+
+// Stages this thread's chunk of a pair: K as bf16 (fp8 codes widened
+// exactly); V as fp16 (F16) or bf16.
+template <bool KV8, bool F16>
 __device__ __forceinline__ void stage_pair(unsigned char* buf, int tid, u32x4 kr, u32x4 vr) {
   const int sel = tid >> 8, c = tid & 255;
-  if constexpr (KV8) {  // codes -> bf16 (exact), same elements in the same order
+  u32x4 vh;
+  if constexpr (KV8) {  // codes -> bf16 / fp16 (exact), same elements in the same order
     const u32x2 k0 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(kr[0]));
     const u32x2 k1 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(kr[1]));
-    const u32x2 v0 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(vr[0]));
-    const u32x2 v1 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(vr[1]));
     kr = u32x4{k0[0], k0[1], k1[0], k1[1]};
-    vr = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    if constexpr (F16) {
+      vh = u32x4{fp8x2_to_f16x2<false>(vr[0]), fp8x2_to_f16x2<true>(vr[0]),
+                 fp8x2_to_f16x2<false>(vr[1]), fp8x2_to_f16x2<true>(vr[1])};
+    } else {
+      const u32x2 v0 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(vr[0]));
+      const u32x2 v1 = __builtin_bit_cast(u32x2, fp8x4_to_bf16x4(vr[1]));
+      vh = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    }
+  } else if constexpr (F16) {
+    vh = u32x4{bf16x2_to_f16x2(vr[0]), bf16x2_to_f16x2(vr[1]), bf16x2_to_f16x2(vr[2]),
+               bf16x2_to_f16x2(vr[3])};
+  } else {
+    vh = vr;
   }
   *(u32x4*)(buf + k_slot(sel * kPage + (c >> 4), c & 15)) = kr;
   // V chunk: dim c>>1, keys h*8..h*8+7 = key groups 2h and 2h+1 of page sel
   const int d = c >> 1, h = c & 1;
-  *(u32x2*)(buf + v_slot(d, 2 * h) + sel * 8) = u32x2{vr[0], vr[1]};
-  *(u32x2*)(buf + v_slot(d, 2 * h + 1) + sel * 8) = u32x2{vr[2], vr[3]};
+  *(u32x2*)(buf + v_slot(d, 2 * h) + sel * 8) = u32x2{vh[0], vh[1]};
+  *(u32x2*)(buf + v_slot(d, 2 * h + 1) + sel * 8) = u32x2{vh[2], vh[3]};
 }
 
 __device__ __forceinline__ void read_pair(const unsigned char* buf, int n, int gq, PairRegs& r) {
@@ -207,6 +242,17 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// The workspace: the claim counter (8 bytes), the count of flagged items (4
+// bytes, then 4 of padding) and one flag per item: set when a bf16 cache's
+// page pairs of the item hold a V value beyond fp16's range, cleared by the
+// fix-up launch once it has recomputed the item.
+__device__ __forceinline__ unsigned* fix_count(const PrefillArgs& a) {
+  return (unsigned*)(a.claims + 1);
+}
+__device__ __forceinline__ unsigned* fix_flags(const PrefillArgs& a) {
+  return (unsigned*)(a.claims + 2);
+}
+
 struct ItemOrder {
   int ntile;                 // row blocks of the longest request
   int64_t per_tile, nitems;  // items per row block (groups x requests), all items
@@ -238,7 +284,7 @@ __device__ __forceinline__ ItemOrder item_order(const PrefillArgs& a, int G) {
 // a workgroup's items: a wave may still read one item's claim while wave 0
 // writes the next one's.  carry: in, the ids of this item's first three pairs
 // if valid; out, those of the next item when it belongs to the same request.
-template <bool WINDOWED, bool KV8>
+template <bool WINDOWED, bool KV8, bool F16>
 __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const ItemOrder& o,
                                                 int tile, int g, const ReqLens& rl, int64_t item,
                                                 unsigned char (&sm)[2][kBufBytes],
@@ -398,18 +444,19 @@ __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const Item
           }
         }
       }
-      // exponent arguments x = s * qscale - m_run (log2 units).  Lazy
-      // rescale: the reference max moves only when some x exceeds 8, so
-      // p = 2^x < 2^8 and the accumulators are rescaled a few times per row
-      // rather than every pair.  The exact row max is taken only then.
+      // exponent arguments x = s * qscale - m_run (log2 units), carried as
+      // x + 7 so that 2^(x+7) = kPScale * p.  Lazy rescale: the reference max
+      // moves only when some x exceeds 8, so p = 2^x < 2^8 and the
+      // accumulators are rescaled a few times per row rather than every
+      // pair.  The exact row max is taken only then.
       float xv[kTiles][8];
       bool grow = false;
 #pragma unroll
       for (int mt = 0; mt < kTiles; ++mt)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          xv[mt][j] = fmaf(sv[mt][j], a.qscale, -m_run[mt]);
-          grow |= xv[mt][j] > 8.f;
+          xv[mt][j] = fmaf(sv[mt][j], a.qscale, kPScaleLog2 - m_run[mt]);
+          grow |= xv[mt][j] > 8.f + kPScaleLog2;
         }
       if (__any(grow)) {
 #pragma unroll
@@ -431,46 +478,82 @@ __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const Item
             for (int i2 = 0; i2 < 4; ++i2) acc[mt][nb][i2] *= al[i2];
           m_run[mt] = m_new;
 #pragma unroll
-          for (int j = 0; j < 8; ++j) xv[mt][j] = fmaf(sv[mt][j], a.qscale, -m_new);
+          for (int j = 0; j < 8; ++j) xv[mt][j] = fmaf(sv[mt][j], a.qscale, kPScaleLog2 - m_new);
         }
       }
+      // p (scaled by kPScale) into the value product.  Common path: fp16 P
+      // against the fp16 copy of V, one MFMA per 16 dims: fp16 carries p to
+      // 2^-12 relative.  A pair with a V value beyond fp16's range (bf16
+      // cache only) takes bf16 V, with P split into bf16(p) and its bf16
+      // remainder (two MFMAs).
+      if constexpr (F16) {
 #pragma unroll
-      for (int mt = 0; mt < kTiles; ++mt) {
-        float pv[8];
+        for (int mt = 0; mt < kTiles; ++mt) {
+          float pv[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(xv[mt][j]);
-        l_part[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-        bf16x8 ph, pl;
+          for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(xv[mt][j]);
+          l_part[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+          f16x8 ph;
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const f32x2 pp = {pv[j], pv[j + 1]};
-          const bf16x2 h = __builtin_convertvector(pp, bf16x2);
-          const bf16x2 l = __builtin_convertvector(pp - __builtin_convertvector(h, f32x2), bf16x2);
-          ph[j] = h[0];
-          ph[j + 1] = h[1];
-          pl[j] = l[0];
-          pl[j + 1] = l[1];
+          for (int j = 0; j < 8; j += 2) {
+            const f32x2 pp = {pv[j], pv[j + 1]};
+            const f16x2 h = __builtin_convertvector(pp, f16x2);
+            ph[j] = h[0];
+            ph[j + 1] = h[1];
+          }
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+            acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                ph, __builtin_bit_cast(f16x8, pr.v[nb]), acc[mt][nb], 0, 0, 0);
         }
+        // tile 0's exponentials and conversions, then its 8 value MFMAs each
+        // followed by vector instructions of tile 1's softmax, then tile 1's
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, kFastValuFirst, 0);
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          const bf16x8 vv = __builtin_bit_cast(bf16x8, pr.v[nb]);
-          acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, acc[mt][nb], 0, 0, 0);
-          acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, acc[mt][nb], 0, 0, 0);
+        for (int k = 0; k < 8; ++k) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedValu, kFastValuPerMfma, 0);
         }
-      }
-      // Issue order of the block above: tile 0's exponentials and splits
-      // first, then tile 0's 16 value MFMAs each followed by two vector
-      // instructions of tile 1's softmax, then tile 1's value MFMAs.  Left to
-      // itself the scheduler puts both tiles' softmax ahead of every value
-      // MFMA, so a wave's vector work never runs under its own MFMAs
-      // (measured: the 32K full layer 11.5 -> 11.1-11.2 ms).
-      __builtin_amdgcn_sched_group_barrier(kSchedValu, kSoftmaxValuFirst, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 8, 0);
+      } else {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+        for (int mt = 0; mt < kTiles; ++mt) {
+          float pv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv[j] = exp2_fast(xv[mt][j]);
+          l_part[mt] += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+          bf16x8 ph, pl;
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            const f32x2 pp = {pv[j], pv[j + 1]};
+            const bf16x2 h = __builtin_convertvector(pp, bf16x2);
+            const bf16x2 l = __builtin_convertvector(pp - __builtin_convertvector(h, f32x2), bf16x2);
+            ph[j] = h[0];
+            ph[j + 1] = h[1];
+            pl[j] = l[0];
+            pl[j + 1] = l[1];
+          }
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const bf16x8 vv = __builtin_bit_cast(bf16x8, pr.v[nb]);
+            acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vv, acc[mt][nb], 0, 0, 0);
+            acc[mt][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vv, acc[mt][nb], 0, 0, 0);
+          }
+        }
+        // Issue order of the block above: tile 0's exponentials and splits
+        // first, then tile 0's 16 value MFMAs each followed by two vector
+        // instructions of tile 1's softmax, then tile 1's value MFMAs.  Left to
+        // itself the scheduler puts both tiles' softmax ahead of every value
+        // MFMA, so a wave's vector work never runs under its own MFMAs
+        // (measured: the 32K full layer 11.5 -> 11.1-11.2 ms).
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, kSoftmaxValuFirst, 0);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedValu, kValuPerMfma, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
     }
   };
   // In flight at the top of iteration i: pair i in LDS buffer i&1, the page
@@ -514,7 +597,7 @@ __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const Item
     if (claim && tid == 0) cval = atomicAdd(a.claims, 1ull);
     fetch(0, ia0, ib0, kr0, vr0);  // waits for the ids, hence for the sinks
     sink_l2 = sink * kLog2e;
-    stage_pair<KV8>(sm[0], tid, kr0, vr0);
+    stage_pair<KV8, F16>(sm[0], tid, kr0, vr0);
     if (claim && tid == 0) publish(cval);
     // Q and the sinks were issued before pair 0, so they are in; pinning
     // them here keeps the compiler from waiting for them inside the loop,
@@ -544,13 +627,13 @@ __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const Item
     next_ok = item_pages<WINDOWED>(a, o.ntile - 1 - (int)(next / o.per_tile), rl, next_pf, next_pl);
   for (int i = 0; i < npairs; i += 2) {
     compute(i);
-    if (i + 1 < npairs) stage_pair<KV8>(sm[1], tid, kr1, vr1);
+    if (i + 1 < npairs) stage_pair<KV8, F16>(sm[1], tid, kr1, vr1);
     fetch(i + 3, ia1, ib1, kr1, vr1);
     load_ids(i + 5, ia1, ib1);
     __syncthreads();
     if (i + 1 >= npairs) break;
     compute(i + 1);
-    if (i + 2 < npairs) stage_pair<KV8>(sm[0], tid, kr0, vr0);
+    if (i + 2 < npairs) stage_pair<KV8, F16>(sm[0], tid, kr0, vr0);
     fetch(i + 4, ia0, ib0, kr0, vr0);
     load_ids(i + 6, ia0, ib0);
     __syncthreads();
@@ -572,6 +655,7 @@ __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const Item
 
   bad = __any(bad);
   // epilogue: acc rows gq*4+i are query vectors; their m and l live in lane gq*4+i
+  bool nonfinite = false;
 #pragma unroll
   for (int mt = 0; mt < kTiles; ++mt) {
     float l_c = l_part[mt] + __shfl_xor(l_part[mt], 16);
@@ -580,7 +664,7 @@ __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const Item
     for (int i = 0; i < 4; ++i) {
       const int v = gq * 4 + i;  // query vector of acc row
       const float m = __shfl(m_run[mt], v);
-      const float l = __shfl(l_c, v);
+      const float l = __shfl(l_c, v) * (1.f / kPScale);  // l_part sums kPScale * p
       const int r = row0 + 2 * mt + (v >> 3);
       if (r >= q_len) continue;
       const int h = g * kGroup + (v & 7);
@@ -588,12 +672,23 @@ __device__ __forceinline__ int64_t prefill_item(const PrefillArgs& a, const Item
       const float M2 = fmaxf(m, sink);
       const float so = exp2_fast(m - M2);
       const float inv = 1.f / (l * so + exp2_fast(sink - M2));
-      const float vs = KV8 ? a.v_scale : 1.f;
+      const float vs = (KV8 ? a.v_scale : 1.f) * (1.f / kPScale);  // acc holds kPScale * P.V
       float* dst = a.out + ((int64_t)(q0 + r) * hq + h) * kHeadDim + n;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        dst[nb * 16] = bad ? __builtin_nanf("") : acc[mt][nb][i] * so * inv * vs;
+      for (int nb = 0; nb < 8; ++nb) {
+        const float x = acc[mt][nb][i] * so * inv * vs;
+        nonfinite |= !__builtin_isfinite(x);
+        dst[nb * 16] = bad ? __builtin_nanf("") : x;
+      }
     }
+  }
+  // A bf16 V value beyond fp16's range was staged as +-inf, and every row of
+  // a wave whose MFMAs took it reads inf or NaN (0 * inf for the rows that
+  // do not see that key): the item is flagged, and the fix-up launch
+  // recomputes it with bf16 V.  (Non-finite inputs flag it too; the
+  // recomputation then gives the same non-finite rows.)
+  if (F16 && !KV8 && !bad && __any(nonfinite) && lane == 0) {
+    if (atomicCAS(&fix_flags(a)[item], 0u, 1u) == 0u) atomicAdd(fix_count(a), 1u);
   }
   PF_STAMP(5);
   return next;
@@ -632,9 +727,47 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
     // the next item is claimed from its last fixed one on
     const bool claim = o.nfixed < o.nitems && (r + 1) * G >= o.nfixed;
-    slot = prefill_item<WINDOWED, KV8>(a, o, tile, rest % a.num_kv_heads, rl, slot, sm, sm_sink,
-                                       sm_claim, (int)(r & 1), carry, claim,
-                                       claim ? o.nitems : slot_of(r + 1));
+    slot = prefill_item<WINDOWED, KV8, true>(a, o, tile, rest % a.num_kv_heads, rl, slot, sm,
+                                             sm_sink, sm_claim, (int)(r & 1), carry, claim,
+                                             claim ? o.nitems : slot_of(r + 1));
+  }
+}
+
+// Fix-up launch after a bf16-cache prefill: recomputes, with bf16 V and P
+// split into bf16(p) and its bf16 remainder, every item the main launch
+// flagged (a V value beyond fp16's range in its pages), and clears the flags.
+// With no item flagged every workgroup returns after one load.
+template <bool WINDOWED>
+__global__ __launch_bounds__(kPThreads, 1) void prefill_fix_kernel(PrefillArgs a) {
+  if (__hip_atomic_load(fix_count(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) return;
+  __shared__ __attribute__((aligned(16))) unsigned char sm[2][kBufBytes];
+  __shared__ float sm_sink[kGroup];
+  __shared__ int64_t sm_claim[2];
+  const int G = gridDim.x;
+  ItemOrder o = item_order(a, G);
+  o.nfixed = o.nitems;  // every item in fixed rounds: nothing is claimed
+  unsigned* flags = fix_flags(a);
+  for (int64_t r = 0;; ++r) {
+    const int64_t slot = r * G + ((r & 1) ? G - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (slot >= o.nitems) break;
+    if (__hip_atomic_load(&flags[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) continue;
+    const int tile = o.ntile - 1 - (int)(slot / o.per_tile);
+    const int rest = (int)(slot % o.per_tile);
+    const int b = rest / a.num_kv_heads;
+    ReqLens rl;
+    rl.b = b;
+    rl.q0 = a.cu_q_lens[b];
+    rl.q_len = a.cu_q_lens[b + 1] - rl.q0;
+    rl.seq_len = a.seq_lens[b];
+    IdCarry carry;
+    carry.valid = false;
+    prefill_item<WINDOWED, false, false>(a, o, tile, rest % a.num_kv_heads, rl, slot, sm, sm_sink,
+                                         sm_claim, (int)(r & 1), carry, false, o.nitems);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      flags[slot] = 0u;
+      atomicSub(fix_count(a), 1u);
+    }
   }
 }
 
@@ -656,27 +789,31 @@ static int64_t prefill_items(int32_t num_seqs, int32_t num_kv_heads, int32_t max
   return (int64_t)((max_q_len + kRows - 1) / kRows) * num_kv_heads * num_seqs;
 }
 
+// The claim counter, the flagged-item count and one flag per item (see
+// fix_flags); the caller zero-fills it once and every call leaves it zero.
 size_t prefill_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t max_q_len) {
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_q_len <= 0) return 0;
-  return prefill_items(num_seqs, num_kv_heads, max_q_len) > kPrefillWorkgroups
-             ? sizeof(unsigned long long)
-             : 0;
+  return 16 + 4 * (size_t)prefill_items(num_seqs, num_kv_heads, max_q_len);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0 || a.max_q_len == 0) return hipSuccess;
+  if (!a.claims) return hipErrorInvalidValue;
   const int64_t items = prefill_items(a.num_seqs, a.num_kv_heads, a.max_q_len);
-  if (items > kPrefillWorkgroups && !a.claims) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(items < kPrefillWorkgroups ? items : kPrefillWorkgroups));
   if (a.kv_fp8) {
     if (a.window > 0)
       hipLaunchKernelGGL((prefill_kernel<true, true>), grid, dim3(kPThreads), 0, st, a);
     else
       hipLaunchKernelGGL((prefill_kernel<false, true>), grid, dim3(kPThreads), 0, st, a);
-  } else if (a.window > 0) {
+    return hipGetLastError();
+  }
+  if (a.window > 0) {
     hipLaunchKernelGGL((prefill_kernel<true, false>), grid, dim3(kPThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_fix_kernel<true>), grid, dim3(kPThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL((prefill_kernel<false, false>), grid, dim3(kPThreads), 0, st, a);
+    hipLaunchKernelGGL((prefill_fix_kernel<false>), grid, dim3(kPThreads), 0, st, a);
   }
   return hipGetLastError();
 }

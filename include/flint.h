@@ -314,10 +314,19 @@ flint_status flint_attn_merge(const flint_attn_layer* L, int32_t num_seqs, int32
  * pages include an id outside [0, num_blocks), are set to NaN.  A request
  * whose rows cu_q_lens[b] .. cu_q_lens[b+1]-1 do not lie inside
  * [0, total_q) is skipped: none of q or out is touched for it.
- * An fp8 cache is widened to bf16 (exactly) as its pages are staged.
- * Workspace: flint_attn_prefill_workspace_size bytes (0 when the work items,
- * ceil(max_q_len / 32) x num_kv_heads x num_seqs, number at most 256;
- * otherwise 8: one work-item counter), 8-byte aligned.  It must hold zeros
+ * An fp8 cache is widened as its pages are staged: K to bf16, V to fp16
+ * (both exactly).  The value product P.V takes P in fp16 (relative rounding
+ * at most 2^-11, so an output moves by at most 2^-11 of the largest |V| it
+ * averages) against V in fp16; a bf16 cache's V converts to fp16 exactly up
+ * to |V| = 65504.  A larger value becomes +-inf there, which makes the rows
+ * of the work item (32 rows of one KV head) that take it non-finite: such an
+ * item is flagged in the workspace and recomputed by a second launch of the
+ * same call with bf16 V and P carried as bf16(p) plus its bf16 remainder
+ * (as is an item whose inputs are not finite; its result is the same).
+ * Workspace: flint_attn_prefill_workspace_size bytes, 16 + 4 per work item
+ * (items: ceil(max_q_len / 32) x num_kv_heads x num_seqs): a work-item
+ * counter, a count of flagged items and one flag per item; 8-byte aligned.
+ * It must hold zeros
  * when the call runs, and every call leaves it zero again, so one zero-fill
  * when it is allocated serves every later call; calls that overlap in time
  * must not share it.  A call that fails its host-side checks does not touch

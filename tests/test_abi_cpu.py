@@ -203,30 +203,31 @@ def test_prefill_rejects_bad_arguments():
     assert lib.flint_attn_prefill(*empty) == 0
 
 
-def test_prefill_workspace_is_one_counter_past_one_item_per_workgroup():
+def test_prefill_workspace_is_a_counter_and_one_flag_per_item():
     # work items: ceil(max_q_len / 32) row blocks x KV heads x requests; the
-    # persistent grid has 256 workgroups, and past 256 items the later ones
-    # are claimed from an 8-byte counter in the workspace
+    # workspace holds the claim counter (8 bytes), the count of items flagged
+    # for the bf16 fix-up launch (4 + 4 bytes) and one 4-byte flag per item
     L = fl.full_layer()
     size = fl.flint_attn_prefill_workspace_size
-    assert size(L, 1, 64 * 32, 4096) == 0          # 64 x 4 x 1 = 256 items
-    assert size(L, 1, 64 * 32 + 1, 4096) == 8      # 65 row blocks: 260
-    assert size(L, 64, 32, 4096) == 0 and size(L, 65, 32, 4096) == 8
-    assert size(L, 1, 32768, 32768) == 8 and size(L, 0, 32768, 32768) == 0
+    assert size(L, 1, 64 * 32, 4096) == 16 + 4 * 256       # 64 x 4 x 1 items
+    assert size(L, 1, 64 * 32 + 1, 4096) == 16 + 4 * 260   # 65 row blocks
+    assert size(L, 64, 32, 4096) == 16 + 4 * 256 and size(L, 65, 32, 4096) == 16 + 4 * 260
+    assert size(L, 1, 32768, 32768) == 16 + 4 * 4096 and size(L, 0, 32768, 32768) == 0
+    assert size(L, 1, 0, 4096) == 0
     L1 = fl.full_layer(num_q_heads=8, num_kv_heads=1)
-    assert size(L1, 1, 256 * 32, 8192) == 0 and size(L1, 1, 256 * 32 + 1, 8192) == 8
+    assert size(L1, 1, 256 * 32, 8192) == 16 + 4 * 256
     lib = fl.lib()
-    # 128 row blocks x 4 heads = 512 items: a workspace is required, checked
-    # before anything is launched
+    # 128 row blocks x 4 heads = 512 items: 2064 bytes, checked before
+    # anything is launched
     base = [C.byref(L), 1, P, P + 0x10000, 4096, 4096, Q, Q + 0x10000, 256, P + 0x20000, 256,
             P + 0x30000, 4096, P + 0x40000, P + 0x50000, None, 0, None]
     assert lib.flint_attn_prefill(*base) == WS_SMALL
-    assert "need 8" in lib.flint_last_error().decode()
+    assert "need 2064" in lib.flint_last_error().decode()
     small = list(base)
-    small[15], small[16] = P + 0x60000, 4
+    small[15], small[16] = P + 0x60000, 2060
     assert lib.flint_attn_prefill(*small) == WS_SMALL
     misaligned = list(base)
-    misaligned[15], misaligned[16] = P + 0x60004, 8
+    misaligned[15], misaligned[16] = P + 0x60004, 2064
     assert lib.flint_attn_prefill(*misaligned) == INVALID
 
 

@@ -5,7 +5,17 @@ import pytest
 
 import oracle
 import synth
-from flint_cases import TOL, assert_parity, check_err, dev, empty_caches, layers, max_err, up
+import flint_cases as fc
+from flint_cases import GUARD, PREFILL_GUARD, TOL, dev, empty_caches, layers, max_err, up
+
+
+def assert_parity(got, ref, what=""):
+    """The contract and the prefill guard (fp16 P in the value product)."""
+    return fc.assert_parity(got, ref, what, guard=PREFILL_GUARD)
+
+
+def check_err(err, ref, what=""):
+    return fc.check_err(err, ref, what, guard=PREFILL_GUARD)
 
 pytestmark = pytest.mark.gpu
 
@@ -247,7 +257,8 @@ def test_prefill_claimed_items_share_one_workspace_across_calls(window, hkv, req
     case = PrefillCase(15, reqs, window=window, hkv=hkv)
     need = fl.flint_attn_prefill_workspace_size(case.FL, len(reqs), case.max_q,
                                                 int(case.seq_lens.max()))
-    assert need == 8
+    items = -(-case.max_q // 32) * hkv * len(reqs)
+    assert need == 16 + 4 * items
     ws = torch.zeros(need, dtype=torch.uint8, device=dev())
     first, _, _, _ = case.run_gpu(workspace=ws)
     assert not ws.any().item()
@@ -267,12 +278,14 @@ def test_prefill_graph_replays_match_eager():
     qc = qb[torch.from_numpy(case.chunk_rows).to(dev())].contiguous()
     cu, bt, sl, sk = up(case.cu), up(case.bt), up(case.seq_lens), up(case.sinks)
     out = torch.empty((len(case.chunk_rows), 32, 128), dtype=torch.float32, device=dev())
+    ws = torch.zeros(fl.flint_attn_prefill_workspace_size(case.FL, 2, case.max_q, 700),
+                     dtype=torch.uint8, device=dev())
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             fl.flint_attn_prefill(case.FL, qc, cu, case.max_q, kd, vd, bt, sl,
-                                  int(case.seq_lens.max()), sk, out)
+                                  int(case.seq_lens.max()), sk, out, ws)
     for _ in range(3):
         out.fill_(float("nan"))
         torch.cuda.synchronize()
@@ -295,7 +308,9 @@ def test_prefill_graph_with_claimed_items_replays_match_eager():
     eager, kd, vd, qb = case.run_gpu()
     qc = qb[torch.from_numpy(case.chunk_rows).to(dev())].contiguous()
     cu, bt, sl, sk = up(case.cu), up(case.bt), up(case.seq_lens), up(case.sinks)
-    ws = torch.zeros(8, dtype=torch.uint8, device=dev())
+    ws = torch.zeros(fl.flint_attn_prefill_workspace_size(case.FL, len(reqs), case.max_q,
+                                                          int(case.seq_lens.max())),
+                     dtype=torch.uint8, device=dev())
     out = torch.empty((len(case.chunk_rows), 32, 128), dtype=torch.float32, device=dev())
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
@@ -347,3 +362,41 @@ def test_last_fp8_prefill_row_matches_fp8_decode():
     torch.cuda.synchronize()
     # prefill's q is bf16, decode's fp32: they agree to the bf16 rounding of q
     assert np.abs(got[-1] - out.cpu().numpy()[0]).max() <= TOL
+
+
+@pytest.mark.parametrize("window", [0, 513])
+def test_prefill_values_beyond_fp16_range_are_recomputed_in_bf16(window):
+    # V values past fp16's range (65504) in a bf16 cache: the work items whose
+    # page pairs hold them are flagged and recomputed by the fix-up launch
+    # with bf16 V; every other item keeps the fp16 value product.  The
+    # workspace's flags and counts are back at zero after each call, and a
+    # second call on the same workspace gives the same result.
+    import torch
+    import full_gqa_decode_amd as fl
+    case = PrefillCase(23, [(700, 700), (300, 100)], window=window)
+    case.v_in[600:611] *= 3.0e4          # request 0, positions 600..610: |V| up to ~1.3e5
+    assert np.abs(case.v_in[600:611]).max() > 65504
+    want = case.expected()
+    ws = torch.zeros(fl.flint_attn_prefill_workspace_size(case.FL, 2, case.max_q, 700),
+                     dtype=torch.uint8, device=dev())
+    first = None
+    for _ in range(2):
+        got, _, _, _ = case.run_gpu(workspace=ws)
+        assert int(ws.count_nonzero()) == 0
+        if first is None:
+            first = got
+        assert np.array_equal(got, first)
+    assert np.isfinite(got).all()
+    # rows that see none of the large values: the contract and the guard
+    far = np.r_[0:576, 700:800]
+    assert_parity(got[far], want[far])
+    # rows that average values of ~1e5: the bar relative to each row's scale
+    # (a fixed 4e-3 presumes outputs of order one)
+    for r in range(576, 700):
+        err = max_err(got[r], want[r])
+        assert err <= GUARD * max(1.0, float(np.abs(want[r]).max())), (r, err)
+    # the same chunk without the large values takes no fix-up (nothing flagged)
+    plain = PrefillCase(23, [(700, 700), (300, 100)], window=window)
+    got2, _, _, _ = plain.run_gpu(workspace=ws)
+    assert int(ws.count_nonzero()) == 0
+    assert_parity(got2, plain.expected())
