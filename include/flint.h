@@ -86,7 +86,7 @@
 extern "C" {
 #endif
 
-#define FLINT_ABI_VERSION 3
+#define FLINT_ABI_VERSION 4
 
 typedef enum {
   FLINT_OK = 0,

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = fl.lib()
-    assert lib.flint_abi_version() == 3
+    assert lib.flint_abi_version() == 4
     # 12 four-byte fields, in the header's order
     assert C.sizeof(fl.FlintAttnLayer) == 48
     assert [f[0] for f in fl.FlintAttnLayer._fields_][-3:] == ["kv_dtype", "k_scale", "v_scale"]
