@@ -16,6 +16,7 @@ starts.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import math
 import os
@@ -75,6 +76,20 @@ def measured_traffic(key="traffic_bytes_per_launch"):
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def marker(name):
+    """A roctx range (torch.cuda.nvtx maps to roctx on ROCm) around a phase of
+    the bench, so that `rocprofv3 --marker-trace` ties each kernel to its leg
+    and, in the eager step, to its layer.  Host-side only: graph replays carry
+    none, and the timed loop gets one range around all of its steps."""
+    import torch
+    torch.cuda.nvtx.range_push(name)
+    try:
+        yield
+    finally:
+        torch.cuda.nvtx.range_pop()
 
 
 def build_inputs(dev):
@@ -198,8 +213,9 @@ def main():
                                   workspace=ws)
 
     def step():
-        for L in layers:
-            layer_step(L)
+        for idx, L in enumerate(layers):
+            with marker(f"layer {idx} ({'full' if L['full'] else 'sliding'})"):
+                layer_step(L)
 
     def step_unfused():
         for L in layers:
@@ -235,7 +251,7 @@ def main():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    with torch.cuda.stream(stream):
+    with torch.cuda.stream(stream), marker(f"timed: {args.steps} steps of the 49-layer graph"):
         ev[0].record(stream)
         for i in range(args.steps):
             g.replay()
@@ -368,15 +384,19 @@ def main():
     }
 
     if not args.no_fp8:
-        result["fp8"] = bench_fp8(fl, dev, layers, ws, ones, seq_lens, capture, time_graph,
-                                  args.steps, stream, eps)
+        with marker("fp8 cache leg"):
+            result["fp8"] = bench_fp8(fl, dev, layers, ws, ones, seq_lens, capture, time_graph,
+                                      args.steps, stream, eps)
 
     if not args.no_moe:
-        result["moe"] = bench_moe(fl, dev, capture, stream)
+        with marker("MoE leg"):
+            result["moe"] = bench_moe(fl, dev, capture, stream)
 
     if not args.no_configs:
-        result["configs"] = bench_configs(fl, dev)
-        result["ceilings"] = bench_ceilings(dev)
+        with marker("other workloads"):
+            result["configs"] = bench_configs(fl, dev)
+        with marker("machine ceilings"):
+            result["ceilings"] = bench_ceilings(dev)
         walk = result["ceilings"]["page_walk"]["us_per_launch"]
         result["roofline"]["loads_alone_us"] = walk
         result["roofline"]["frac_of_loads_alone"] = round(walk / us_k2, 4)
@@ -1014,6 +1034,11 @@ PREFILL_TIMED_MS = 20.0
 
 
 def prefill_leg(fl, dev, window, fp8=False):
+    with marker(f"prefill leg: 32768 tokens, window {window}{', fp8 cache' if fp8 else ''}"):
+        return _prefill_leg(fl, dev, window, fp8)
+
+
+def _prefill_leg(fl, dev, window, fp8=False):
     import torch
     T = 32768
     eps = float(np.float32(1e-6))
