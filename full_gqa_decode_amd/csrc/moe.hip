@@ -249,22 +249,33 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_gate_up_kernel(MoeArgs a) 
 // One wave per (output row r, token t), every slot's row loaded up front.
 // NS = top_k + num_shared, a template argument so that the slot loop has no
 // branch: at a branch's join the compiler waits for the loads issued inside
-// it, which would cost one memory round trip per slot.
+// it, which would cost one memory round trip per slot.  The token's h (NS x
+// 2 KiB) is staged once per workgroup in LDS: read by every wave from memory
+// it would be twice the bytes of the wave's own rows (NS x 1 KiB), all
+// through the CU's one load path.
 template <int NS>
 __global__ __launch_bounds__(kMoeWaves * 64) void moe_down_kernel(MoeArgs a) {
   static_assert(kMoeMaxInter == 512, "one 16-byte lane load per row");
+  constexpr int kThreads = kMoeWaves * 64;
+  constexpr int kChunks = NS * kMoeMaxInter / 4;  // 16-byte chunks of h
+  constexpr int kPasses = (kChunks + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) float sm_h[NS * kMoeMaxInter];
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * kMoeWaves + (threadIdx.x >> 6);
   const int t = blockIdx.y;
   const int H = a.hidden, I = a.inter;
-  if (r >= H) return;
+  const int r_w = blockIdx.x * kMoeWaves + (threadIdx.x >> 6);
+  const int r = min(r_w, H - 1);  // every wave meets the barrier; past H none stores
   // the token's expert ids and weights in one vector load (lane k holds slot
   // k's, the index clamped), so one wait precedes every row address
   const int kl = t * a.top_k + min(lane, a.top_k - 1);
   const int id_l = a.topk_ids[kl];
   const float wt_l = a.topk_weights[kl];
+  // h: unconditional loads (index clamped), so no wait lands on a branch
+  const f32x4* hg = (const f32x4*)(a.h + (int64_t)t * NS * I);
+  f32x4 hs[kPasses];
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) hs[i] = hg[min((int)threadIdx.x + i * kThreads, kChunks - 1)];
   u32x4 wv[NS];
-  f32x4 h0[NS], h1[NS];
   float wk[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
@@ -273,15 +284,22 @@ __global__ __launch_bounds__(kMoeWaves * 64) void moe_down_kernel(MoeArgs a) {
     const int e = routed ? __builtin_amdgcn_readlane(id_l, kr) : a.num_experts + (k - a.top_k);
     wk[k] = routed ? readlane_f32(wt_l, kr) : 1.f;
     const uint16_t* wd = a.w_down + ((int64_t)e * H + r) * I + lane * 8;
-    const float* hp = a.h + ((int64_t)t * NS + k) * I + lane * 8;
     wv[k] = __builtin_nontemporal_load((const u32x4*)wd);
-    h0[k] = *(const f32x4*)hp;
-    h1[k] = *(const f32x4*)(hp + 4);
   }
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) {
+    const int c = threadIdx.x + i * kThreads;
+    if (c < kChunks) ((f32x4*)sm_h)[c] = hs[i];
+  }
+  __syncthreads();
   float y = 0.f;
 #pragma unroll
-  for (int k = 0; k < NS; ++k) y = fmaf(wk[k], wave_sum_f32(dot8(wv[k], h0[k], h1[k], 0.f)), y);
-  if (lane == 0) a.out[(int64_t)t * H + r] = y;
+  for (int k = 0; k < NS; ++k) {
+    const f32x4 h0 = *(const f32x4*)&sm_h[k * kMoeMaxInter + lane * 8];
+    const f32x4 h1 = *(const f32x4*)&sm_h[k * kMoeMaxInter + lane * 8 + 4];
+    y = fmaf(wk[k], wave_sum_f32(dot8(wv[k], h0, h1, 0.f)), y);
+  }
+  if (lane == 0 && r_w < H) a.out[(int64_t)t * H + r] = y;
 }
 
 template <int CH>
